@@ -1,0 +1,190 @@
+"""CPU oracle for row-wise softmax with the online normalizer (double precision).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package; the product path
+(``online_normalizer_amd``) never does and fails loudly without its HIP library.
+
+The arithmetic lives in ``oracle.c`` (plain C, IEEE double, no fast-math); this
+module only loads it and marshals numpy arrays.  What each function computes,
+with the passages it follows:
+
+* ``softmax`` -- safe softmax in three passes (max, sum of e^{x-m}, divide):
+  "OnlineSoftmax: Online normalizer calculation for softmax", section 2
+  (safe softmax), and "CUDA算子优化(3)：Softmax", section "Softmax的cpu实现".
+* ``stats`` -- the per-row state (m, d) by the same plain definition.
+* ``online_state`` -- the element-by-element recurrence of section 3.1 of the
+  paper summary, starting from the identity (-inf, 0) ("第 7 课：Online Softmax
+  与可结合状态", section 3).
+* ``combine`` -- the binary operator of section 3.3 of the paper summary.
+* ``topk`` -- brute-force sort of the whole row under (value desc, index asc),
+  probabilities e^{u-m}/d over the whole row (section 4 of the paper summary).
+
+Rows are independent, so the wrappers may split a batch of rows over host
+threads (each thread runs the same sequential C code on its own rows).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(*args, **kwargs) -> str:
+    """Compile ``oracle.c`` (see ``oracle/build.py``)."""
+    from .build import build as _build
+    return _build(*args, **kwargs)
+
+__all__ = ["Oracle", "load", "build", "DEFAULT_LIB"]
+
+_c_double_p = ctypes.POINTER(ctypes.c_double)
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class Oracle:
+    """Handle on one compiled copy of ``oracle.c``."""
+
+    def __init__(self, path: str = DEFAULT_LIB):
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"oracle library {path} is missing; run __graft_entry__.build() "
+                "or python -m oracle.build")
+        self.path = path
+        lib = ctypes.CDLL(path)
+        i64 = ctypes.c_int64
+        vp = ctypes.c_void_p
+        for name in ("oracle_softmax_f32", "oracle_softmax_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, i64, i64, vp]
+            fn.restype = ctypes.c_int
+        for name in ("oracle_stats_f32", "oracle_stats_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, i64, i64, vp, vp]
+            fn.restype = ctypes.c_int
+        lib.oracle_online_state.argtypes = [vp, i64, _c_double_p, _c_double_p]
+        lib.oracle_online_state.restype = None
+        lib.oracle_combine.argtypes = [ctypes.c_double] * 4 + [_c_double_p, _c_double_p]
+        lib.oracle_combine.restype = None
+        lib.oracle_topk_f32.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
+        lib.oracle_topk_f32.restype = ctypes.c_int
+        self.lib = lib
+
+    # -- helpers -----------------------------------------------------------
+    @staticmethod
+    def _split(rows: int, threads: int):
+        threads = max(1, min(threads, rows))
+        step = -(-rows // threads)
+        return [(r0, min(rows, r0 + step)) for r0 in range(0, rows, step)]
+
+    def _run_rows(self, fn, rows: int, threads: int):
+        spans = self._split(rows, threads)
+        if len(spans) == 1:
+            rc = fn(*spans[0])
+            if rc != 0:
+                raise RuntimeError(f"oracle call failed with status {rc}")
+            return
+        with ThreadPoolExecutor(max_workers=len(spans)) as pool:
+            for rc in pool.map(lambda s: fn(*s), spans):
+                if rc != 0:
+                    raise RuntimeError(f"oracle call failed with status {rc}")
+
+    # -- softmax -----------------------------------------------------------
+    def softmax(self, x: np.ndarray, threads: int = 1) -> np.ndarray:
+        """Row-wise softmax in double.  ``x``: 2-D float32, or uint16 bf16 bits."""
+        x = np.ascontiguousarray(x)
+        if x.ndim != 2:
+            raise ValueError("x must be 2-D [rows, cols]")
+        rows, cols = x.shape
+        y = np.empty((rows, cols), dtype=np.float64)
+        if rows == 0 or cols == 0:
+            return y
+        if x.dtype == np.float32:
+            fn, esz = self.lib.oracle_softmax_f32, 4
+        elif x.dtype == np.uint16:
+            fn, esz = self.lib.oracle_softmax_bf16, 2
+        else:
+            raise TypeError("x must be float32 or uint16 (bf16 bit patterns)")
+        xb, yb = x.ctypes.data, y.ctypes.data
+
+        def part(r0, r1):
+            return fn(ctypes.c_void_p(xb + r0 * cols * esz), r1 - r0, cols,
+                      ctypes.c_void_p(yb + r0 * cols * 8))
+
+        self._run_rows(part, rows, threads)
+        return y
+
+    def stats(self, x: np.ndarray, threads: int = 1):
+        """Per-row (m, d) in double by the plain definition."""
+        x = np.ascontiguousarray(x)
+        rows, cols = x.shape
+        m = np.empty(rows, dtype=np.float64)
+        d = np.empty(rows, dtype=np.float64)
+        if rows == 0:
+            return m, d
+        if x.dtype == np.float32:
+            fn, esz = self.lib.oracle_stats_f32, 4
+        elif x.dtype == np.uint16:
+            fn, esz = self.lib.oracle_stats_bf16, 2
+        else:
+            raise TypeError("x must be float32 or uint16 (bf16 bit patterns)")
+        xb, mb, db = x.ctypes.data, m.ctypes.data, d.ctypes.data
+
+        def part(r0, r1):
+            return fn(ctypes.c_void_p(xb + r0 * cols * esz), r1 - r0, cols,
+                      ctypes.c_void_p(mb + r0 * 8), ctypes.c_void_p(db + r0 * 8))
+
+        self._run_rows(part, rows, threads)
+        return m, d
+
+    # -- the recurrence and the operator -------------------------------------
+    def online_state(self, x) -> tuple[float, float]:
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float64).reshape(-1))
+        m = ctypes.c_double()
+        d = ctypes.c_double()
+        self.lib.oracle_online_state(_ptr(x), x.size, ctypes.byref(m), ctypes.byref(d))
+        return m.value, d.value
+
+    def combine(self, a, b) -> tuple[float, float]:
+        m = ctypes.c_double()
+        d = ctypes.c_double()
+        self.lib.oracle_combine(float(a[0]), float(a[1]), float(b[0]), float(b[1]),
+                                ctypes.byref(m), ctypes.byref(d))
+        return m.value, d.value
+
+    # -- fused-softmax top-K, by brute force ----------------------------------
+    def topk(self, x: np.ndarray, K: int, threads: int = 1):
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        rows, cols = x.shape
+        probs = np.empty((rows, K), dtype=np.float64)
+        idx = np.empty((rows, K), dtype=np.int32)
+        if rows == 0:
+            return probs, idx
+        xb, pb, ib = x.ctypes.data, probs.ctypes.data, idx.ctypes.data
+        fn = self.lib.oracle_topk_f32
+
+        def part(r0, r1):
+            return fn(ctypes.c_void_p(xb + r0 * cols * 4), r1 - r0, cols, K,
+                      ctypes.c_void_p(pb + r0 * K * 8), ctypes.c_void_p(ib + r0 * K * 4))
+
+        self._run_rows(part, rows, threads)
+        return probs, idx
+
+
+_DEFAULT: Oracle | None = None
+
+
+def load(path: str = DEFAULT_LIB) -> Oracle:
+    """The oracle built from ``oracle/oracle.c`` (cached)."""
+    global _DEFAULT
+    if path != DEFAULT_LIB:
+        return Oracle(path)
+    if _DEFAULT is None:
+        _DEFAULT = Oracle(path)
+    return _DEFAULT
