@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of row-wise softmax with the online normalizer on one MI355X.
+
+Workload (the benchmark's headline configuration): 4096 rows x 32000 columns of
+fp32 LM-logit rows, 2*N(0,1) with 0.1% of entries at +-80 and 0.01% at -inf
+(seeded synthetic, ``workloads.config(2)``), fp32 output.  A step is one
+``os_softmax_forward`` over the whole batch: the fold into (m, d), the merge,
+and the normalising pass.
+
+Printed: one JSON line.  ``value`` is the effective HBM bandwidth, algorithmic
+bytes (one read of the input + one write of the output) per second of wall
+time over the timed steps; ``rows_per_s`` the same in rows.  ``roofline``
+prices the dominant kernel against the 8 TB/s HBM peak using its average
+duration from HIP events recorded on the launch stream; ``traffic`` is the
+HBM bytes per launch from rocprofv3 counters (``profiles/``), or null when the
+kernels changed since the counters were taken.  ``cpu_baseline`` is the CPU
+oracle timed on this host.  Comparison legs on the same input: the three-pass
+safe-softmax baseline, the streaming two-pass kernel, and a plain copy.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["online_normalizer_amd/csrc/os_kernels.hpp", "online_normalizer_amd/csrc/os_device.hpp",
+                  "online_normalizer_amd/csrc/os_abi.hip"]
+COUNTERS_FILE = "profiles/counters_softmax_fwd_4096x32000_f32.txt"
+WORKLOAD = 2
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(launch_bytes_alg: float):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    path = os.path.join(ROOT, COUNTERS_FILE)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernels changed since the counters were taken"
+    try:
+        fetch = float(vals["fetch_kib_per_dispatch"]) * 1024 * float(vals["fetch_scale"])
+        write = float(vals["write_kib_per_dispatch"]) * 1024 * float(vals["write_scale"])
+    except (KeyError, ValueError):
+        return None, "counter summary incomplete"
+    return fetch + write, None
+
+
+def time_launches(fn, steps: int, warmup: int, stream):
+    """Run fn() warmup+steps times back to back; HIP events around each timed launch."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        starts[k].record(stream)
+        fn()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
+    return wall, per
+
+
+def cpu_baseline(x, bytes_per_row: float):
+    import oracle
+    orc = oracle.load()
+    cores = len(os.sched_getaffinity(0))
+    rows = x.shape[0]
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    orc.softmax(x, threads=cores)
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return {
+        "value": round(rows * bytes_per_row / wall / 1e9, 3),
+        "unit": "GB/s",
+        "rows_per_s": round(rows / wall, 1),
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"all {rows} rows x {x.shape[1]} cols of the workload, 3-pass safe softmax in double, "
+                  f"{cpu:.1f} s of CPU time over {wall:.2f} s wall",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true", help="skip the comparison legs")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              "(rows are independent: each GPU would run the same kernel on its own share of rows)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import online_normalizer_amd as ons
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    x_host = workloads.config(WORKLOAD)
+    rows, cols = x_host.shape
+    x = torch.from_numpy(x_host).to(dev)
+    y = torch.empty_like(x)
+    bytes_alg = rows * cols * (4 + 4)  # one read of the input, one write of the output
+
+    wall, per = time_launches(lambda: ons.os_softmax_forward(x, out=y), args.steps, args.warmup, stream)
+    avg = sum(per) / len(per)
+    value = bytes_alg * args.steps / wall / 1e9
+    achieved = bytes_alg / avg / 1e9
+    traffic, traffic_note = load_traffic(bytes_alg)
+    lanes, vecs = ons.os_forward_plan(cols)
+
+    out = {
+        "metric": "achieved HBM GB/s and rows/s for 2-pass online softmax; % of MI355X HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"LM-logit row softmax, {rows} rows x {cols} cols fp32 -> fp32, "
+                               "2*N(0,1) with 0.1% +-80 and 0.01% -inf (seed 1002)",
+                   "rows": rows, "cols": cols, "kernel": f"register-resident, {lanes} lanes x {vecs} "
+                                                         "16-byte vectors per row"},
+        "rows_per_s": round(rows * args.steps / wall, 1),
+        "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel_us": round(avg * 1e6, 2),
+            "algorithmic_bytes": bytes_alg,
+        },
+    }
+    if traffic_note:
+        out["roofline"]["traffic_note"] = traffic_note
+
+    if not args.no_compare:
+        legs = {}
+        _, per3 = time_launches(lambda: ons.safe_softmax_forward(x, out=y), 20, 3, stream)
+        a3 = sum(per3) / len(per3)
+        legs["safe_3pass"] = {"kernel_us": round(a3 * 1e6, 2), "effective_GBs": round(bytes_alg / a3 / 1e9, 2)}
+        _, per2 = time_launches(lambda: ons.os_softmax_forward_tuned(x, 0, 0, 0, out=y), 20, 3, stream)
+        a2 = sum(per2) / len(per2)
+        legs["online_stream_2pass"] = {"kernel_us": round(a2 * 1e6, 2),
+                                       "effective_GBs": round(bytes_alg / a2 / 1e9, 2)}
+        _, perc = time_launches(lambda: ons.os_device_copy(x, y), 20, 3, stream)
+        ac = sum(perc) / len(perc)
+        legs["copy"] = {"kernel_us": round(ac * 1e6, 2), "GBs": round(bytes_alg / ac / 1e9, 2)}
+        # the headline kernel with L2 / Infinity Cache flushed before each launch
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        times = []
+        for _ in range(10):
+            scratch.zero_()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            ons.os_softmax_forward(x, out=y)
+            e.record(stream)
+            torch.cuda.synchronize()
+            times.append(s.elapsed_time(e) * 1e-3)
+        del scratch
+        af = sorted(times)[len(times) // 2]
+        legs["online_flushed"] = {"kernel_us": round(af * 1e6, 2), "effective_GBs": round(bytes_alg / af / 1e9, 2)}
+        legs["speedup_vs_safe_3pass"] = round(a3 / avg, 3)
+        legs["pct_of_copy"] = round(100.0 * ac / avg, 2)
+        out["compare"] = legs
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x_host, cols * 8)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,167 @@
+/*
+ * online_softmax.h -- C ABI of the MI355X (gfx950) row-wise softmax library
+ * built on the online normalizer.
+ *
+ * The method (each entry point below cites the passage it implements):
+ *   - "OnlineSoftmax: Online normalizer calculation for softmax" (paper
+ *     summary), section 3.1: one pass folds a row into (m, d), m the running
+ *     maximum and d = sum_j e^{x_j - m}, by
+ *         m_j = max(m_{j-1}, x_j),  d_j = d_{j-1} e^{m_{j-1} - m_j} + e^{x_j - m_j};
+ *     section 3.3: partial states merge with the associative, commutative
+ *         (m1,d1) (+) (m2,d2) = (max, d1 e^{m1-max} + d2 e^{m2-max});
+ *     a second pass writes y_i = e^{x_i - m} / d.
+ *   - "第 7 课：Online Softmax 与可结合状态", section 3: the identity state
+ *     is (-inf, 0).
+ *   - The paper summary, section 4 "Softmax and top-k fusion": one pass keeps
+ *     the K largest logits next to (m, d); only K probabilities are written.
+ *   - The paper summary, section 2, and "5.2 Hiện thực và tối ưu CUDA Online
+ *     Softmax", section 1.1: safe softmax in three passes (max, sum, divide),
+ *     the baseline.
+ *
+ * Conventions shared by every entry point
+ *   Layout     row-major, contiguous, row stride == cols elements.
+ *   Pointers   device pointers (HIP device memory of the current device) unless
+ *              stated; the caller allocates and owns every buffer.  The library
+ *              allocates no device memory.
+ *   Stream     `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *              Calls are asynchronous on that stream and never synchronise;
+ *              results are valid once the stream reaches the call.
+ *   dtype      OS_F32: float in, float out.  OS_BF16: bfloat16 in and out
+ *              (raw 16-bit patterns), fp32 arithmetic inside, output rounded to
+ *              nearest-even.
+ *   Aliasing   `in == out` (exact alias) is allowed for the forward and safe
+ *              entry points; any other overlap is undefined.
+ *   Sizes      0 <= cols <= OS_MAX_COLS; rows * cols * element size must fit in
+ *              int64.
+ *   Empty      rows == 0, or cols == 0 for the forward/safe entry points, is a
+ *              no-op returning OS_OK (pointers may then be NULL).
+ *   Special    a row containing NaN or +inf gives NaN for the whole row; -inf
+ *   values     entries get probability 0; a row with no entry above -inf has
+ *              state (-inf, 0) and softmax NaN (0/0).
+ *   Errors     a negative status; nothing is launched on an error found while
+ *              checking arguments, which happens before any HIP call.
+ *              os_last_error() describes the last failure on the calling thread.
+ *              Pointers must be aligned to their element size; 16-byte
+ *              alignment of the row starts selects 128-bit accesses, anything
+ *              else a slower per-element path (not an error).
+ */
+#ifndef ONLINE_SOFTMAX_H
+#define ONLINE_SOFTMAX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define OS_OK 0
+#define OS_EINVAL (-1)       /* bad argument (null pointer, size, dtype, K, misalignment) */
+#define OS_EUNSUPPORTED (-2) /* a requested kernel shape is not built into the library */
+#define OS_ELAUNCH (-3)      /* the HIP runtime rejected a launch or a device query */
+
+/* element types */
+#define OS_F32 0
+#define OS_BF16 1
+
+/* largest K accepted by os_softmax_topk */
+#define OS_TOPK_KMAX 32
+
+/* largest row length (columns) accepted by every entry point: 2^30 */
+#define OS_MAX_COLS (1LL << 30)
+
+/*
+ * y = softmax(x) row by row with the online normalizer (paper summary,
+ * sections 3.1 and 3.3; the normalising pass as in "5.2 Hiện thực và tối ưu
+ * CUDA Online Softmax", section 2.2).
+ *   in, out   [rows, cols] of `dtype`.
+ *   The kernel is chosen from `cols` and `dtype`: rows short enough to stay in
+ *   registers are read from HBM once (several rows per wavefront, one
+ *   wavefront per row, or one workgroup per row); longer rows are streamed in
+ *   two passes (fold, then normalise), reading the row twice.
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                       void *stream);
+
+/*
+ * Same computation as os_softmax_forward with an explicit kernel shape, for
+ * tests and tuning.
+ *   lanes_per_row   lanes that share one row: 4, 8, 16, 32, 64, 128, 256, 512
+ *                   or 1024 (register-resident kernels), or 0 for the
+ *                   streaming two-pass kernel.
+ *   vecs_per_lane   16-byte vectors held per lane (2, 4, 8 or 16; only the
+ *                   combinations built into the library are accepted).  The
+ *                   shape must hold the row: lanes_per_row * vecs_per_lane *
+ *                   (16 / element size) >= cols.  Ignored when lanes_per_row == 0.
+ *   grid_blocks     workgroups to launch (grid-stride over rows); 0 = automatic.
+ *   Returns OS_OK, OS_EINVAL (shape too small or grid_blocks < 0),
+ *   OS_EUNSUPPORTED (shape not built), or OS_ELAUNCH.
+ */
+int os_softmax_forward_tuned(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                             int lanes_per_row, int vecs_per_lane, int grid_blocks, void *stream);
+
+/*
+ * The shape os_softmax_forward uses for (cols, dtype).  Host only: no HIP call.
+ *   *lanes_per_row, *vecs_per_lane receive the shape (0, 0 for streaming).
+ *   Returns OS_OK or OS_EINVAL.
+ */
+int os_forward_plan(int64_t cols, int dtype, int *lanes_per_row, int *vecs_per_lane);
+
+/*
+ * Per-row normaliser state (m, d) from the fold and the (+) merge alone, no
+ * output pass (paper summary, sections 3.1-3.3).
+ *   in      [rows, cols] of `dtype`.
+ *   m, d    [rows] float each.  A row with no entry above -inf (or cols == 0)
+ *           gets the identity (-inf, 0).
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_softmax_stats(const void *in, float *m, float *d, int64_t rows, int64_t cols, int dtype,
+                     void *stream);
+
+/*
+ * Fused softmax + top-K in one read of the input (paper summary, section 4):
+ * the K largest logits of each row and their probabilities over the WHOLE row,
+ * v = e^{u - m} / d (not renormalised over the K).  The full softmax is never
+ * written.
+ *   in      [rows, cols] float.
+ *   probs   [rows, K] float, best first.
+ *   idx     [rows, K] int32 column indices, best first.  Order: larger logit
+ *           first; equal logits (including -0.0 == +0.0) by lower index first.
+ *   K       1 <= K <= min(cols, OS_TOPK_KMAX).
+ *   Rows containing NaN give NaN probabilities and unspecified indices.
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_softmax_topk(const float *in, float *probs, int32_t *idx, int64_t rows, int64_t cols, int K,
+                    void *stream);
+
+/*
+ * Baseline: safe softmax in three streaming passes over the input (maximum,
+ * sum of e^{x-m}, normalise and store), as in the paper summary, section 2,
+ * and "5.2 Hiện thực và tối ưu CUDA Online Softmax", section 1.1.  It reads
+ * every row three times; same arguments and results as os_softmax_forward.
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int safe_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                         void *stream);
+
+/*
+ * Plain device copy of `bytes` bytes with 128-bit accesses: the reference
+ * read+write kernel used to calibrate traffic counters and as a bandwidth
+ * ceiling.  src and dst must be 16-byte aligned, bytes a multiple of 16,
+ * no overlap.  Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_device_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+/* Message for the last failing call on this thread ("" if none).  The pointer
+ * stays valid until the next call on the same thread. */
+const char *os_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int os_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONLINE_SOFTMAX_H */

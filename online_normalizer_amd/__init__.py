@@ -1,0 +1,211 @@
+"""MI355X (gfx950) row-wise softmax with the online normalizer.
+
+Thin Python binding over the C ABI of ``libonline_softmax.so`` (declared in
+``include/online_softmax.h``).  The functions here only marshal arguments:
+they take torch tensors that live on the GPU, pass their device pointers,
+sizes and the current HIP stream to the library, and raise on a non-zero
+status.  Every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory and streams.
+
+Entry points (same names as the C ABI):
+  os_softmax_forward(x, out=None)              y = softmax(x) over the last dim
+  os_softmax_forward_tuned(x, lanes_per_row, vecs_per_lane, grid_blocks=0, out=None)
+  os_softmax_stats(x) -> (m, d)                per-row normaliser state
+  os_softmax_topk(x, K) -> (probs, idx)        fused softmax + top-K
+  safe_softmax_forward(x, out=None)            three-pass baseline
+  os_device_copy(src, dst)                     plain copy (bandwidth reference)
+  os_forward_plan(cols, dtype) -> (lanes_per_row, vecs_per_lane)
+  os_last_error(), os_version()
+
+There is no fallback: if the library is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loaded first: its HIP runtime is the one the library binds to
+
+__all__ = [
+    "OS_F32", "OS_BF16", "OS_TOPK_KMAX", "OnlineSoftmaxError", "LIB_PATH", "lib",
+    "os_softmax_forward", "os_softmax_forward_tuned", "os_softmax_stats", "os_softmax_topk",
+    "safe_softmax_forward", "os_device_copy", "os_forward_plan", "os_last_error", "os_version",
+]
+
+OS_OK, OS_EINVAL, OS_EUNSUPPORTED, OS_ELAUNCH = 0, -1, -2, -3
+OS_F32, OS_BF16 = 0, 1
+OS_TOPK_KMAX = 32
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libonline_softmax.so")
+
+
+class OnlineSoftmaxError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def _hip_runtimes_mapped() -> set[str]:
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                path = line.rsplit(" ", 1)[-1].strip()
+                if "libamdhip64.so" in os.path.basename(path):
+                    found.add(os.path.realpath(path))
+    except OSError:
+        pass
+    return found
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+            "(or python -m online_normalizer_amd.build); there is no fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are loaded in this process: {sorted(runtimes)}")
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "os_softmax_forward": [vp, vp, i64, i64, i32, vp],
+        "os_softmax_forward_tuned": [vp, vp, i64, i64, i32, i32, i32, i32, vp],
+        "os_forward_plan": [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
+        "os_softmax_stats": [vp, vp, vp, i64, i64, i32, vp],
+        "os_softmax_topk": [vp, vp, vp, i64, i64, i32, vp],
+        "safe_softmax_forward": [vp, vp, i64, i64, i32, vp],
+        "os_device_copy": [vp, vp, i64, vp],
+        "os_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = i32
+    L.os_last_error.argtypes = []
+    L.os_last_error.restype = ctypes.c_char_p
+    return L
+
+
+_LIB: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raw ctypes handle)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+lib()
+
+
+def os_last_error() -> str:
+    return lib().os_last_error().decode()
+
+
+def os_version() -> int:
+    return lib().os_version()
+
+
+def _check(fn: str, status: int):
+    if status != OS_OK:
+        raise OnlineSoftmaxError(fn, status, os_last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return OS_F32
+    if t.dtype == torch.bfloat16:
+        return OS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _rows_cols(x: torch.Tensor):
+    if x.dim() == 0:
+        raise ValueError("softmax needs at least one dimension")
+    if not x.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not x.is_contiguous():
+        raise ValueError("tensors must be contiguous (row stride == cols)")
+    cols = x.shape[-1]
+    rows = math.prod(x.shape[:-1])
+    return rows, cols
+
+
+def _stream(x: torch.Tensor) -> int:
+    return torch.cuda.current_stream(x.device).cuda_stream
+
+
+def _out_like(x, out):
+    if out is None:
+        return torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor with the input's shape, dtype and device")
+    return out
+
+
+def os_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    rows, cols = _rows_cols(x)
+    out = _out_like(x, out)
+    _check("os_softmax_forward",
+           lib().os_softmax_forward(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), _stream(x)))
+    return out
+
+
+def os_softmax_forward_tuned(x: torch.Tensor, lanes_per_row: int, vecs_per_lane: int,
+                             grid_blocks: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    rows, cols = _rows_cols(x)
+    out = _out_like(x, out)
+    _check("os_softmax_forward_tuned",
+           lib().os_softmax_forward_tuned(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x),
+                                          lanes_per_row, vecs_per_lane, grid_blocks, _stream(x)))
+    return out
+
+
+def os_forward_plan(cols: int, dtype: torch.dtype = torch.float32) -> tuple[int, int]:
+    code = OS_BF16 if dtype == torch.bfloat16 else OS_F32
+    a, b = ctypes.c_int(), ctypes.c_int()
+    _check("os_forward_plan", lib().os_forward_plan(cols, code, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def os_softmax_stats(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    rows, cols = _rows_cols(x)
+    shape = x.shape[:-1]
+    m = torch.empty(shape, dtype=torch.float32, device=x.device)
+    d = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check("os_softmax_stats",
+           lib().os_softmax_stats(x.data_ptr(), m.data_ptr(), d.data_ptr(), rows, cols, _dtype_code(x),
+                                  _stream(x)))
+    return m, d
+
+
+def os_softmax_topk(x: torch.Tensor, K: int) -> tuple[torch.Tensor, torch.Tensor]:
+    rows, cols = _rows_cols(x)
+    if x.dtype != torch.float32:
+        raise TypeError("os_softmax_topk takes float32 input")
+    shape = (*x.shape[:-1], K)
+    probs = torch.empty(shape, dtype=torch.float32, device=x.device)
+    idx = torch.empty(shape, dtype=torch.int32, device=x.device)
+    _check("os_softmax_topk",
+           lib().os_softmax_topk(x.data_ptr(), probs.data_ptr(), idx.data_ptr(), rows, cols, K, _stream(x)))
+    return probs, idx
+
+
+def safe_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    rows, cols = _rows_cols(x)
+    out = _out_like(x, out)
+    _check("safe_softmax_forward",
+           lib().safe_softmax_forward(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), _stream(x)))
+    return out
+
+
+def os_device_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _check("os_device_copy", lib().os_device_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(src)))
+    return dst

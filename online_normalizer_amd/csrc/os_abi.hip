@@ -1,0 +1,346 @@
+// os_abi.hip -- the C ABI declared in include/online_softmax.h: argument
+// checks (all before any HIP call), kernel selection, and launches on the
+// caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/online_softmax.h"
+#include "os_kernels.hpp"
+
+using namespace onorm;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+thread_local char g_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_error[0] = '\0';
+    return OS_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elt_size(int dtype) { return dtype == OS_BF16 ? 2 : 4; }
+
+// Common checks of a [rows, cols] problem.  Returns OS_OK, an error, or 1 for
+// "empty: nothing to do".
+int check_problem(const char* fn, const void* in, const void* out, bool need_out, int64_t rows,
+                  int64_t cols, int dtype) {
+    if (dtype != OS_F32 && dtype != OS_BF16) return fail(OS_EINVAL, "%s: unknown dtype %d", fn, dtype);
+    if (rows < 0 || cols < 0)
+        return fail(OS_EINVAL, "%s: rows (%lld) and cols (%lld) must be >= 0", fn, (long long)rows,
+                    (long long)cols);
+    if (cols > OS_MAX_COLS) return fail(OS_EINVAL, "%s: cols %lld exceeds OS_MAX_COLS", fn, (long long)cols);
+    if (rows == 0 || cols == 0) return 1;
+    if (rows > INT64_MAX / cols / 4)
+        return fail(OS_EINVAL, "%s: rows * cols overflows the addressable range", fn);
+    if (in == nullptr) return fail(OS_EINVAL, "%s: input pointer is NULL", fn);
+    if (need_out && out == nullptr) return fail(OS_EINVAL, "%s: output pointer is NULL", fn);
+    const uintptr_t es = static_cast<uintptr_t>(elt_size(dtype));
+    if (!aligned(in, es) || (out != nullptr && !aligned(out, es)))
+        return fail(OS_EINVAL, "%s: pointers must be aligned to the element size (%d bytes)", fn,
+                    (int)es);
+    return OS_OK;
+}
+
+// 16-byte vector path: every row start aligned (base aligned, row bytes a multiple of 16).
+bool vector_ok(const void* in, const void* out, int64_t cols, int dtype) {
+    return aligned(in, 16) && (out == nullptr || aligned(out, 16)) && ((cols * elt_size(dtype)) % 16) == 0;
+}
+
+// ---------------------------------------------------------------------------
+// Device properties (compute units per device), cached per device ordinal.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int compute_units(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(OS_ELAUNCH, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(OS_ELAUNCH, "device ordinal %d out of range", dev);
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return fail(OS_ELAUNCH, "hipDeviceGetAttribute(MultiprocessorCount) failed");
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    *cus = n;
+    return OS_OK;
+}
+
+int launched(const char* fn) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(OS_ELAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident shapes built into the library.
+// ---------------------------------------------------------------------------
+typedef void (*RowKernel)(const void*, void*, float*, float*, int64_t, int);
+
+struct ResidentShape {
+    int lpr, vpl;
+    RowKernel fn[2][2];  // [bf16][aligned]
+};
+
+#define ONORM_RESIDENT(L, V)                                                         \
+    {                                                                                \
+        L, V, {                                                                      \
+            {k_resident<false, L, V, false>, k_resident<false, L, V, true>},         \
+            {k_resident<true, L, V, false>, k_resident<true, L, V, true>},           \
+        }                                                                            \
+    }
+// fp32 only: 16 vectors of bf16 are 128 fp32 values per lane, more than a
+// 1024-thread workgroup's 128-VGPR budget, so bf16 rows this long stream.
+#define ONORM_RESIDENT_F32(L, V)                                                     \
+    {                                                                                \
+        L, V, {                                                                      \
+            {k_resident<false, L, V, false>, k_resident<false, L, V, true>},         \
+            {nullptr, nullptr},                                                      \
+        }                                                                            \
+    }
+
+const ResidentShape kResident[] = {
+    ONORM_RESIDENT(4, 2),    ONORM_RESIDENT(4, 4),    ONORM_RESIDENT(8, 2),
+    ONORM_RESIDENT(8, 4),    ONORM_RESIDENT(16, 2),   ONORM_RESIDENT(16, 4),
+    ONORM_RESIDENT(32, 4),   ONORM_RESIDENT(64, 2),   ONORM_RESIDENT(64, 4),
+    ONORM_RESIDENT(64, 8),   ONORM_RESIDENT(128, 8),  ONORM_RESIDENT(256, 8),
+    ONORM_RESIDENT(512, 8),  ONORM_RESIDENT(1024, 8), ONORM_RESIDENT_F32(1024, 16),
+};
+constexpr int kNumResident = sizeof(kResident) / sizeof(kResident[0]);
+
+// Automatic choice, smallest capacity first (lanes_per_row, vecs_per_lane).
+const int kAutoPlan[][2] = {{4, 2},   {4, 4},   {8, 4},   {16, 4},  {32, 4},   {64, 4},
+                            {64, 8},  {128, 8}, {256, 8}, {512, 8}, {1024, 8}, {1024, 16}};
+constexpr int kNumAuto = sizeof(kAutoPlan) / sizeof(kAutoPlan[0]);
+
+const ResidentShape* find_shape(int lpr, int vpl, int dtype) {
+    const int bf = dtype == OS_BF16 ? 1 : 0;
+    for (int i = 0; i < kNumResident; ++i)
+        if (kResident[i].lpr == lpr && kResident[i].vpl == vpl && kResident[i].fn[bf][0] != nullptr)
+            return &kResident[i];
+    return nullptr;
+}
+
+int64_t vectors_needed(int64_t cols, int dtype) {
+    const int64_t vec = 16 / elt_size(dtype);
+    return (cols + vec - 1) / vec;
+}
+
+void auto_plan(int64_t cols, int dtype, int* lpr, int* vpl) {
+    const int64_t need = vectors_needed(cols, dtype);
+    for (int i = 0; i < kNumAuto; ++i) {
+        if (static_cast<int64_t>(kAutoPlan[i][0]) * kAutoPlan[i][1] >= need &&
+            find_shape(kAutoPlan[i][0], kAutoPlan[i][1], dtype) != nullptr) {
+            *lpr = kAutoPlan[i][0];
+            *vpl = kAutoPlan[i][1];
+            return;
+        }
+    }
+    *lpr = 0;
+    *vpl = 0;
+}
+
+// Streaming kernels: 16 waves per row, 4 vectors per lane per step.
+constexpr int kStreamW = 16;
+constexpr int kStreamU = 4;
+
+RowKernel stream_kernel(int dtype, bool al) {
+    if (dtype == OS_BF16)
+        return al ? k_stream<true, kStreamW, kStreamU, true> : k_stream<true, kStreamW, kStreamU, false>;
+    return al ? k_stream<false, kStreamW, kStreamU, true> : k_stream<false, kStreamW, kStreamU, false>;
+}
+
+// Workgroups for a grid-stride launch over `groups` row groups.
+int grid_for(int64_t groups, int block, int cus, int requested) {
+    if (requested > 0) return static_cast<int>(groups < requested ? groups : requested);
+    // Enough workgroups for every CU to hold several at once; beyond that the
+    // kernels stride over the remaining rows.
+    const int64_t per_cu = block >= 1024 ? 2 : (block >= 512 ? 4 : 16);
+    int64_t cap = static_cast<int64_t>(cus) * per_cu * 8;
+    if (cap > INT32_MAX) cap = INT32_MAX;
+    return static_cast<int>(groups < cap ? groups : cap);
+}
+
+int run_rows(const char* fn, const void* in, void* out, float* st_m, float* st_d, int64_t rows,
+             int64_t cols, int dtype, int lpr, int vpl, int grid_req, void* stream) {
+    // Shape checks first: no HIP call happens before every argument is known good.
+    const ResidentShape* shape = nullptr;
+    if (lpr != 0) {
+        shape = find_shape(lpr, vpl, dtype);
+        if (shape == nullptr)
+            return fail(OS_EUNSUPPORTED, "%s: no kernel built for lanes_per_row=%d vecs_per_lane=%d", fn, lpr,
+                        vpl);
+        if (static_cast<int64_t>(lpr) * vpl < vectors_needed(cols, dtype))
+            return fail(OS_EINVAL, "%s: lanes_per_row=%d x vecs_per_lane=%d cannot hold %lld columns", fn, lpr,
+                        vpl, (long long)cols);
+    }
+    int cus = 0;
+    int rc = compute_units(&cus);
+    if (rc != OS_OK) return rc;
+    const bool al = vector_ok(in, out, cols, dtype);
+    const int bf = dtype == OS_BF16 ? 1 : 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (shape == nullptr) {
+        const int block = kStreamW * 64;
+        const int grid = grid_for(rows, block, cus, grid_req);
+        hipLaunchKernelGGL(stream_kernel(dtype, al), dim3(grid), dim3(block), 0, st, in, out, st_m, st_d,
+                           rows, static_cast<int>(cols));
+        return launched(fn);
+    }
+    const int block = lpr <= 64 ? 256 : lpr;
+    const int rpb = block / lpr;
+    const int64_t groups = (rows + rpb - 1) / rpb;
+    const int grid = grid_for(groups, block, cus, grid_req);
+    hipLaunchKernelGGL(shape->fn[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, st_m, st_d, rows,
+                       static_cast<int>(cols));
+    return launched(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int os_version(void) { return kVersion; }
+
+const char* os_last_error(void) { return g_error; }
+
+int os_forward_plan(int64_t cols, int dtype, int* lanes_per_row, int* vecs_per_lane) {
+    if (dtype != OS_F32 && dtype != OS_BF16) return fail(OS_EINVAL, "os_forward_plan: unknown dtype %d", dtype);
+    if (cols < 0 || cols > OS_MAX_COLS) return fail(OS_EINVAL, "os_forward_plan: cols %lld out of range", (long long)cols);
+    if (lanes_per_row == nullptr || vecs_per_lane == nullptr)
+        return fail(OS_EINVAL, "os_forward_plan: NULL output pointer");
+    auto_plan(cols, dtype, lanes_per_row, vecs_per_lane);
+    return ok();
+}
+
+int os_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
+    const char* fn = "os_softmax_forward";
+    int rc = check_problem(fn, in, out, true, rows, cols, dtype);
+    if (rc == 1) return ok();
+    if (rc != OS_OK) return rc;
+    int lpr = 0, vpl = 0;
+    auto_plan(cols, dtype, &lpr, &vpl);
+    return run_rows(fn, in, out, nullptr, nullptr, rows, cols, dtype, lpr, vpl, 0, stream);
+}
+
+int os_softmax_forward_tuned(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int lanes_per_row,
+                             int vecs_per_lane, int grid_blocks, void* stream) {
+    const char* fn = "os_softmax_forward_tuned";
+    int rc = check_problem(fn, in, out, true, rows, cols, dtype);
+    if (rc != OS_OK && rc != 1) return rc;
+    if (lanes_per_row < 0 || grid_blocks < 0)
+        return fail(OS_EINVAL, "%s: lanes_per_row and grid_blocks must be >= 0", fn);
+    if (lanes_per_row != 0 && find_shape(lanes_per_row, vecs_per_lane, dtype) == nullptr)
+        return fail(OS_EUNSUPPORTED, "%s: no kernel built for lanes_per_row=%d vecs_per_lane=%d", fn, lanes_per_row,
+                    vecs_per_lane);
+    if (rc == 1) return ok();
+    return run_rows(fn, in, out, nullptr, nullptr, rows, cols, dtype, lanes_per_row, vecs_per_lane, grid_blocks,
+                    stream);
+}
+
+int os_softmax_stats(const void* in, float* m, float* d, int64_t rows, int64_t cols, int dtype, void* stream) {
+    const char* fn = "os_softmax_stats";
+    int rc = check_problem(fn, in, nullptr, false, rows, cols, dtype);
+    if (rc != OS_OK && rc != 1) return rc;
+    if (rows == 0) return ok();
+    if (m == nullptr || d == nullptr) return fail(OS_EINVAL, "%s: m and d must not be NULL", fn);
+    if (!aligned(m, 4) || !aligned(d, 4)) return fail(OS_EINVAL, "%s: m and d must be 4-byte aligned", fn);
+    // cols == 0: every row is empty and gets the identity state; the input is never read.
+    int lpr = 0, vpl = 0;
+    auto_plan(cols, dtype, &lpr, &vpl);
+    return run_rows(fn, cols == 0 ? nullptr : in, nullptr, m, d, rows, cols, dtype, lpr, vpl, 0, stream);
+}
+
+int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
+    const char* fn = "safe_softmax_forward";
+    int rc = check_problem(fn, in, out, true, rows, cols, dtype);
+    if (rc == 1) return ok();
+    if (rc != OS_OK) return rc;
+    int cus = 0;
+    rc = compute_units(&cus);
+    if (rc != OS_OK) return rc;
+    const bool al = vector_ok(in, out, cols, dtype);
+    const int block = kStreamW * 64;
+    const int grid = grid_for(rows, block, cus, 0);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    void (*k)(const void*, void*, int64_t, int);
+    if (dtype == OS_BF16)
+        k = al ? k_safe3<true, kStreamW, kStreamU, true> : k_safe3<true, kStreamW, kStreamU, false>;
+    else
+        k = al ? k_safe3<false, kStreamW, kStreamU, true> : k_safe3<false, kStreamW, kStreamU, false>;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, st, in, out, rows, static_cast<int>(cols));
+    return launched(fn);
+}
+
+int os_softmax_topk(const float* in, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K, void* stream) {
+    const char* fn = "os_softmax_topk";
+    if (rows < 0 || cols < 0) return fail(OS_EINVAL, "%s: rows and cols must be >= 0", fn);
+    if (cols > OS_MAX_COLS) return fail(OS_EINVAL, "%s: cols %lld exceeds OS_MAX_COLS", fn, (long long)cols);
+    if (K < 1 || K > OS_TOPK_KMAX) return fail(OS_EINVAL, "%s: K=%d outside [1, %d]", fn, K, OS_TOPK_KMAX);
+    if (rows == 0) return ok();
+    if (static_cast<int64_t>(K) > cols)
+        return fail(OS_EINVAL, "%s: K=%d exceeds cols=%lld", fn, K, (long long)cols);
+    if (rows > INT64_MAX / cols / 4) return fail(OS_EINVAL, "%s: rows * cols overflows", fn);
+    if (in == nullptr || probs == nullptr || idx == nullptr) return fail(OS_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(in, 4) || !aligned(probs, 4) || !aligned(idx, 4))
+        return fail(OS_EINVAL, "%s: pointers must be 4-byte aligned", fn);
+    int cus = 0;
+    int rc = compute_units(&cus);
+    if (rc != OS_OK) return rc;
+    const bool al = aligned(in, 16) && (cols % 4) == 0;
+    constexpr int W = 16, U = 4;
+    const int grid = grid_for(rows, W * 64, cus, 0);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (al)
+        hipLaunchKernelGGL((k_topk<W, U, true>), dim3(grid), dim3(W * 64), 0, st, in, probs, idx, rows,
+                           static_cast<int>(cols), K);
+    else
+        hipLaunchKernelGGL((k_topk<W, U, false>), dim3(grid), dim3(W * 64), 0, st, in, probs, idx, rows,
+                           static_cast<int>(cols), K);
+    return launched(fn);
+}
+
+int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    const char* fn = "os_device_copy";
+    if (bytes < 0 || bytes % 16 != 0) return fail(OS_EINVAL, "%s: bytes must be a non-negative multiple of 16", fn);
+    if (bytes == 0) return ok();
+    if (src == nullptr || dst == nullptr) return fail(OS_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(OS_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    const char* s = static_cast<const char*>(src);
+    const char* d = static_cast<const char*>(dst);
+    if (s < d + bytes && d < s + bytes) return fail(OS_EINVAL, "%s: source and destination overlap", fn);
+    int cus = 0;
+    int rc = compute_units(&cus);
+    if (rc != OS_OK) return rc;
+    const int64_t n16 = bytes / 16;
+    int64_t want = (n16 + 255) / 256;
+    const int64_t cap = static_cast<int64_t>(cus) * 16;
+    const int grid = static_cast<int>(want < cap ? want : cap);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_copy, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+    return launched(fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+// os_device.hpp -- device building blocks for the gfx950 (CDNA4, wave64)
+// softmax kernels: the normaliser state and its merge, cross-lane reductions
+// on DPP and the gfx950 permlane swaps, 128-bit loads and stores, and bf16
+// packing.
+//
+// The state (m, d) and the merge follow "OnlineSoftmax: Online normalizer
+// calculation for softmax" (paper summary), sections 3.1 and 3.3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace onorm {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.44269504088896340736f;
+// Start value of every running maximum: -FLT_MAX rather than -inf, so that
+// differences of two maxima are never inf - inf (a NaN).  On every state a
+// kernel can build, (kFloor, 0) behaves exactly as the identity (-inf, 0):
+// max(m, kFloor) = m for any m >= kFloor, and its d = 0 adds nothing.  A
+// -inf input still contributes e^{-inf - m} = 0.
+constexpr float kFloor = -3.40282346638528859812e+38f;
+
+// e^t as 2^(t * log2 e) on the hardware base-2 exponential (v_exp_f32).
+// Callers form t = x - m first, so the rounding of the product stays
+// relative to the small difference, not to |x|.
+__device__ __forceinline__ float exp_e(float t) { return __builtin_amdgcn_exp2f(t * kLog2e); }
+
+__device__ __forceinline__ float rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// ---------------------------------------------------------------------------
+// The normaliser state and the merge (+).
+// ---------------------------------------------------------------------------
+struct State {
+    float m;  // running maximum
+    float d;  // sum of e^{x - m} over the elements folded so far
+};
+
+// (m1,d1) (+) (m2,d2) = (max, d_big + d_small * e^{m_small - m_big}).
+// This is the paper summary's two-exponential form with the factor
+// e^{m_big - max} = 1 dropped, so one exponential per merge.  It is exactly
+// symmetric in its operands (same bits either way round), which keeps every
+// lane of a butterfly reduction bit-identical.
+__device__ __forceinline__ State oplus(State a, State b) {
+    const float hi = fmaxf(a.m, b.m);
+    const float s = exp_e(-fabsf(a.m - b.m));
+    const float d = (a.m >= b.m) ? fmaf(b.d, s, a.d) : fmaf(a.d, s, b.d);
+    return {hi, d};
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane data movement.
+// ---------------------------------------------------------------------------
+enum : int {
+    kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141, // row_half_mirror: lane i <-> 7-i within 8
+    kDppMirror = 0x140,     // row_mirror: lane i <-> 15-i within 16
+    kDppWaveShr1 = 0x138,   // wave_shr:1, lane i reads lane i-1
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+// v_permlane16_swap: returns {own row's copy, partner row's copy} so that
+// every lane of row pair (0,1) or (2,3) sees the values of both rows at its
+// position within the row.
+__device__ __forceinline__ f32x2 swap_rows16(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// v_permlane32_swap: the same between the two 32-lane halves.
+__device__ __forceinline__ f32x2 swap_rows32(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Merge of the states of an aligned group of LANES lanes (1..64); every lane
+// of the group ends with the same bits.
+template <int LANES>
+__device__ __forceinline__ State group_oplus(State s) {
+    if constexpr (LANES >= 2) s = oplus(s, State{dpp<kDppXor1>(s.m), dpp<kDppXor1>(s.d)});
+    if constexpr (LANES >= 4) s = oplus(s, State{dpp<kDppXor2>(s.m), dpp<kDppXor2>(s.d)});
+    if constexpr (LANES >= 8) s = oplus(s, State{dpp<kDppHalfMirror>(s.m), dpp<kDppHalfMirror>(s.d)});
+    if constexpr (LANES >= 16) s = oplus(s, State{dpp<kDppMirror>(s.m), dpp<kDppMirror>(s.d)});
+    if constexpr (LANES >= 32) {
+        const f32x2 m = swap_rows16(s.m), d = swap_rows16(s.d);
+        s = oplus(State{m[0], d[0]}, State{m[1], d[1]});
+    }
+    if constexpr (LANES >= 64) {
+        const f32x2 m = swap_rows32(s.m), d = swap_rows32(s.d);
+        s = oplus(State{m[0], d[0]}, State{m[1], d[1]});
+    }
+    return s;
+}
+
+// Plain maximum / sum over the whole wave (for the three-pass baseline and
+// the top-K threshold); every lane ends with the same bits.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    f32x2 t = swap_rows16(v);
+    v = fmaxf(t[0], t[1]);
+    t = swap_rows32(v);
+    return fmaxf(t[0], t[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = v + dpp<kDppXor1>(v);
+    v = v + dpp<kDppXor2>(v);
+    v = v + dpp<kDppHalfMirror>(v);
+    v = v + dpp<kDppMirror>(v);
+    f32x2 t = swap_rows16(v);
+    v = t[0] + t[1];
+    t = swap_rows32(v);
+    return t[0] + t[1];
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// ---------------------------------------------------------------------------
+// Element access.  A 16-byte vector holds 4 fp32 or 8 bf16 values.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+struct Elt;
+
+template <>
+struct Elt<false> {
+    static constexpr int kVec = 4;
+    static constexpr int kSize = 4;
+    __device__ static __forceinline__ void unpack(u32x4 r, float* v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
+    }
+    __device__ static __forceinline__ u32x4 pack(const float* v) {
+        return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                     __float_as_uint(v[3])};
+    }
+    __device__ static __forceinline__ float load1(const void* row, int e) {
+        return static_cast<const float*>(row)[e];
+    }
+    __device__ static __forceinline__ void store1(void* row, int e, float v) {
+        static_cast<float*>(row)[e] = v;
+    }
+};
+
+// bf16 -> fp32 is exact (the bf16 bits are the top half of the fp32 word);
+// fp32 -> bf16 rounds to nearest-even in hardware (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 f = {lo, hi};
+    const bf16x2 b = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+template <>
+struct Elt<true> {
+    static constexpr int kVec = 8;
+    static constexpr int kSize = 2;
+    __device__ static __forceinline__ void unpack(u32x4 r, float* v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(r[i] << 16);
+            v[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
+        }
+    }
+    __device__ static __forceinline__ u32x4 pack(const float* v) {
+        return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])};
+    }
+    __device__ static __forceinline__ float load1(const void* row, int e) {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[e]) << 16);
+    }
+    __device__ static __forceinline__ void store1(void* row, int e, float v) {
+        static_cast<uint16_t*>(row)[e] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    }
+};
+
+// 128-bit global loads and stores.  STREAM = true marks data touched once
+// (non-temporal hint); a pass whose data is read again later uses plain
+// loads so that the re-read can hit in L2 / Infinity Cache.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    else
+        return *static_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+}
+
+}  // namespace onorm

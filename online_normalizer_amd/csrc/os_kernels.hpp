@@ -1,0 +1,519 @@
+// os_kernels.hpp -- gfx950 kernels for row-wise softmax with the online
+// normalizer ("OnlineSoftmax: Online normalizer calculation for softmax",
+// paper summary, sections 3.1-3.3 and 4), the three-pass safe-softmax
+// baseline (same page, section 2), and a plain copy used as a bandwidth
+// reference.
+//
+// Row layout: row-major, stride == cols.  Lanes address a row in 16-byte
+// vectors: vector slot vi covers elements [vi*VEC, vi*VEC + VEC).  ALIGNED
+// kernels move whole vectors with 128-bit accesses (row starts 16-byte
+// aligned, cols a multiple of VEC); the others move the same slots element by
+// element with bounds checks.  Missing elements read as -inf, which adds
+// e^{-inf} = 0 to any state.
+#pragma once
+
+#include "os_device.hpp"
+
+namespace onorm {
+
+constexpr int kTopKMax = 32;
+
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ int vec_count(int cols) {
+    constexpr int VEC = Elt<BF16>::kVec;
+    return ALIGNED ? cols / VEC : (cols + VEC - 1) / VEC;
+}
+
+// Load vector slot vi of a row into v[VEC] (-inf where out of range).
+template <bool BF16, bool ALIGNED, bool STREAM>
+__device__ __forceinline__ void load_slot(const char* row, int vi, int nvec, int cols, bool live,
+                                          float* v) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    if constexpr (ALIGNED) {
+        if (live && vi < nvec) {
+            E::unpack(load16<STREAM>(row + static_cast<int64_t>(vi) * 16), v);
+        } else {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) v[k] = -INFINITY;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const int e = vi * VEC + k;
+            v[k] = (live && e < cols) ? E::load1(row, e) : -INFINITY;
+        }
+    }
+}
+
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ void store_slot(char* row, int vi, int nvec, int cols, const float* v) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    if constexpr (ALIGNED) {
+        if (vi < nvec) store16(row + static_cast<int64_t>(vi) * 16, E::pack(v));
+    } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const int e = vi * VEC + k;
+            if (e < cols) E::store1(row, e, v[k]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident forward: the row is read from HBM once.
+//
+// LPR lanes share a row and each holds VPL vectors of it in VGPRs.  LPR <= 64:
+// 256-thread workgroups carry 256/LPR rows, the merge stays inside the
+// wavefront (DPP / permlane).  LPR = 64*W: one row per W-wave workgroup, and
+// the W wave states meet once in LDS (one barrier per row; the LDS slots
+// alternate between rows so the next row's writes never race this row's
+// reads).
+//
+// Pass 1 per lane (the tile form of the recurrence, with the lane's slice as
+// one tile): m_l = max of the slice, e_k = e^{x_k - m_l}, d_l = sum e_k; the
+// e_k stay in registers.  The lane states merge with (+).  Pass 2 writes
+// y_k = e_k * (e^{m_l - m} / d): one exponential per element in all.
+// Writes y when out != nullptr and (m, d) when st_m != nullptr.
+// ---------------------------------------------------------------------------
+template <bool BF16, int LPR, int VPL, bool ALIGNED>
+__global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
+    k_resident(const void* in, void* out, float* st_m, float* st_d, int64_t rows, int cols) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    constexpr int BLOCK = LPR <= 64 ? 256 : LPR;
+    constexpr int RPB = BLOCK / LPR;
+    constexpr int W = LPR > 64 ? LPR / 64 : 1;
+    constexpr int GROUP = LPR < 64 ? LPR : 64;
+    __shared__ State lds[2][W];
+
+    const int tid = threadIdx.x;
+    const int j = tid % LPR;
+    const int g = tid / LPR;
+    const int nvec = vec_count<BF16, ALIGNED>(cols);
+    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
+    int par = 0;
+
+    for (int64_t rb = blockIdx.x; rb * RPB < rows; rb += gridDim.x) {
+        const int64_t row = rb * RPB + g;
+        const bool live = row < rows;
+        const char* rin = static_cast<const char*>(in) + (live ? row : 0) * row_bytes;
+
+        float x[VPL][VEC];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) load_slot<BF16, ALIGNED, true>(rin, v * LPR + j, nvec, cols, live, x[v]);
+
+        float ml = kFloor;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) ml = fmaxf(ml, x[v][k]);
+        float dl = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                x[v][k] = exp_e(x[v][k] - ml);
+                dl += x[v][k];
+            }
+
+        State s = group_oplus<GROUP>(State{ml, dl});
+        if constexpr (W > 1) {
+            if ((tid & (kWave - 1)) == 0) lds[par][tid / kWave] = s;
+            __syncthreads();
+            s = lds[par][0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) s = oplus(s, lds[par][w]);
+            par ^= 1;
+        }
+
+        if (live) {
+            if (st_m != nullptr && j == 0) {
+                st_m[row] = (s.d == 0.0f) ? -INFINITY : s.m;
+                st_d[row] = s.d;
+            }
+            if (out != nullptr) {
+                const float scale = exp_e(ml - s.m) * rcp(s.d);
+                char* rout = static_cast<char*>(out) + row * row_bytes;
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) x[v][k] *= scale;
+                    store_slot<BF16, ALIGNED>(rout, v * LPR + j, nvec, cols, x[v]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming two-pass forward for rows too long for registers: one W-wave
+// workgroup per row.  Pass 1 folds U vectors per lane at a time:
+// m' = max(m, max(tile)), d = d e^{m - m'} + sum e^{x - m'} (the tile form of
+// the recurrence); the lane states merge with (+) across the wave and then
+// through LDS.  Pass 2 re-reads the row (plain loads in pass 1 leave it in
+// L2 / Infinity Cache where it fits) and writes y = e^{x - m} / d.
+// ---------------------------------------------------------------------------
+template <bool BF16, int W, int U, bool ALIGNED>
+__global__ void __launch_bounds__(W * 64)
+    k_stream(const void* in, void* out, float* st_m, float* st_d, int64_t rows, int cols) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    constexpr int BLOCK = W * 64;
+    __shared__ State lds[2][W];
+
+    const int tid = threadIdx.x;
+    const int nvec = vec_count<BF16, ALIGNED>(cols);
+    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
+    int par = 0;
+
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const char* rin = static_cast<const char*>(in) + row * row_bytes;
+        float ml = kFloor, dl = 0.0f;
+        for (int base = 0; base < nvec; base += BLOCK * U) {
+            float x[U][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, false>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+            float mc = kFloor;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) mc = fmaxf(mc, x[u][k]);
+            const float mn = fmaxf(ml, mc);
+            float acc = dl * exp_e(ml - mn);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc += exp_e(x[u][k] - mn);
+            dl = acc;
+            ml = mn;
+        }
+        State s = group_oplus<64>(State{ml, dl});
+        if constexpr (W > 1) {
+            if ((tid & (kWave - 1)) == 0) lds[par][tid / kWave] = s;
+            __syncthreads();
+            s = lds[par][0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) s = oplus(s, lds[par][w]);
+            par ^= 1;
+        }
+        if (st_m != nullptr && tid == 0) {
+            st_m[row] = (s.d == 0.0f) ? -INFINITY : s.m;
+            st_d[row] = s.d;
+        }
+        if (out != nullptr) {
+            const float inv_d = rcp(s.d);
+            char* rout = static_cast<char*>(out) + row * row_bytes;
+            for (int base = 0; base < nvec; base += BLOCK * U) {
+                float x[U][VEC];
+#pragma unroll
+                for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, true>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - s.m) * inv_d;
+                    store_slot<BF16, ALIGNED>(rout, base + u * BLOCK + tid, nvec, cols, x[u]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Baseline: safe softmax in three streaming passes over global memory
+// (maximum; sum of e^{x - m}; normalise and store), same geometry and loads
+// as k_stream so that the two differ only in the passes.
+// ---------------------------------------------------------------------------
+template <bool BF16, int W, int U, bool ALIGNED>
+__global__ void __launch_bounds__(W * 64)
+    k_safe3(const void* in, void* out, int64_t rows, int cols) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    constexpr int BLOCK = W * 64;
+    __shared__ float lds_m[2][W];
+    __shared__ float lds_d[2][W];
+
+    const int tid = threadIdx.x;
+    const int nvec = vec_count<BF16, ALIGNED>(cols);
+    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
+    int par = 0;
+
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const char* rin = static_cast<const char*>(in) + row * row_bytes;
+        // pass 1: maximum
+        float m = kFloor;
+        for (int base = 0; base < nvec; base += BLOCK * U) {
+            float x[U][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, false>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[u][k]);
+        }
+        m = wave_max(m);
+        if constexpr (W > 1) {
+            if ((tid & (kWave - 1)) == 0) lds_m[par][tid / kWave] = m;
+            __syncthreads();
+            m = lds_m[par][0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) m = fmaxf(m, lds_m[par][w]);
+        }
+        // pass 2: sum of e^{x - m}
+        float d = 0.0f;
+        for (int base = 0; base < nvec; base += BLOCK * U) {
+            float x[U][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, false>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) d += exp_e(x[u][k] - m);
+        }
+        d = wave_sum(d);
+        if constexpr (W > 1) {
+            if ((tid & (kWave - 1)) == 0) lds_d[par][tid / kWave] = d;
+            __syncthreads();
+            d = lds_d[par][0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) d += lds_d[par][w];
+            par ^= 1;
+        }
+        // pass 3: normalise and store
+        const float inv_d = rcp(d);
+        char* rout = static_cast<char*>(out) + row * row_bytes;
+        for (int base = 0; base < nvec; base += BLOCK * U) {
+            float x[U][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, true>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - m) * inv_d;
+                store_slot<BF16, ALIGNED>(rout, base + u * BLOCK + tid, nvec, cols, x[u]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused softmax + top-K (paper summary, section 4), one read of the input.
+//
+// One W-wave workgroup per row.  Every lane folds (m, d) over its slots as in
+// k_stream.  Candidates: each wave keeps ONE sorted list of the best K
+// (value, index) pairs it has seen, spread over lanes 0..K-1 (lane k holds
+// rank k) under the total order (value desc, index asc).  Most elements are
+// rejected by a compare with a wave-uniform threshold T, a lower bound on the
+// row's K-th largest value:
+//   - first tile: the K-th largest of the 64 lane maxima (K lanes each hold
+//     an element at least that large);
+//   - then: the K-th entry of the wave's own list, and the largest K-th entry
+//     published by any wave of the workgroup (an LDS atomic max).
+// Survivors (x >= T, so ties at T are kept) are inserted one at a time:
+// position p = number of entries ahead of the new pair, entries from p on
+// shift down one lane (DPP wave_shr:1).  Every true top-K element survives
+// every filter and stays in its wave's list, so the final K-way selection
+// over the W sorted lists (16-lane argmax rounds, lowest index on ties) is
+// exact.  Output: probs = e^{u - m} / d over the whole row, and indices.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int ordered_bits(float f) {
+    const int i = __float_as_int(f);
+    return i >= 0 ? i : (i ^ 0x7FFFFFFF);
+}
+__device__ __forceinline__ float from_ordered_bits(int i) {
+    return __int_as_float(i >= 0 ? i : (i ^ 0x7FFFFFFF));
+}
+
+// (a_v, a_i) ranks ahead of (b_v, b_i)
+__device__ __forceinline__ bool ahead_of(float av, int ai, float bv, int bi) {
+    return (av > bv) || (av == bv && ai < bi);
+}
+
+// Insert the wave-uniform pair (v, i) into the lane-distributed sorted list.
+__device__ __forceinline__ void list_insert(float& L, int& I, float v, int i, int K, int lane,
+                                            uint64_t kmask) {
+    const bool ahead = ahead_of(L, I, v, i);
+    const int p = __popcll(__ballot(ahead) & kmask);
+    if (p < K) {
+        const float Ls = dpp<kDppWaveShr1>(L);
+        const int Is = dpp<kDppWaveShr1>(I);
+        if (lane > p) {
+            L = Ls;
+            I = Is;
+        } else if (lane == p) {
+            L = v;
+            I = i;
+        }
+    }
+}
+
+// K-th largest of one value per lane (lanes with equal values count
+// separately); -inf when fewer than K lanes hold a value above -inf.
+__device__ __forceinline__ float kth_largest_lane_value(float v, int K) {
+    float t = -INFINITY;
+    int need = K;
+    for (int r = 0; r < K; ++r) {
+        const float top = wave_max(v);
+        if (top == -INFINITY) break;
+        need -= __popcll(__ballot(v == top));
+        t = top;
+        if (need <= 0) break;
+        v = (v == top) ? -INFINITY : v;
+    }
+    return need > 0 ? -INFINITY : t;
+}
+
+template <int W, int U, bool ALIGNED>
+__global__ void __launch_bounds__(W * 64)
+    k_topk(const float* in, float* probs, int* idx, int64_t rows, int cols, int K) {
+    static_assert(W <= 16, "the final selection runs inside one 16-lane DPP row");
+    constexpr int BLOCK = W * 64;
+    constexpr int VEC = 4;
+    __shared__ float s_val[W][kTopKMax];
+    __shared__ int s_idx[W][kTopKMax];
+    __shared__ State s_md[W];
+    __shared__ int s_thr;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const uint64_t kmask = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
+    const int nvec = vec_count<false, ALIGNED>(cols);
+
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const char* rin = reinterpret_cast<const char*>(in + row * static_cast<int64_t>(cols));
+        if (tid == 0) s_thr = ordered_bits(-INFINITY);
+        __syncthreads();
+
+        float ml = kFloor, dl = 0.0f;
+        float L = -INFINITY;
+        int I = 0x7FFFFFFF;
+        float T = -INFINITY;
+        bool first = true;
+        for (int base = 0; base < nvec; base += BLOCK * U) {
+            float x[U][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_slot<false, ALIGNED, true>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) mx = fmaxf(mx, x[u][k]);
+            // (m, d) fold over the tile
+            const float mn = fmaxf(ml, mx);
+            float acc = dl * exp_e(ml - mn);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc += exp_e(x[u][k] - mn);
+            dl = acc;
+            ml = mn;
+            // candidates
+            if (first) {
+                T = kth_largest_lane_value(mx, K);
+                first = false;
+            }
+            T = fmaxf(T, from_ordered_bits(__hip_atomic_load(&s_thr, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_WORKGROUP)));
+            if (__ballot(mx >= T) != 0) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int slot = base + u * BLOCK + tid;
+                    const int wave_slot0 = base + u * BLOCK + w * kWave;
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) {
+                        const bool hit = (slot * VEC + k < cols) && (x[u][k] >= T);
+                        uint64_t mask = __ballot(hit);
+                        while (mask != 0) {
+                            const int l = __builtin_ctzll(mask);
+                            mask &= mask - 1;
+                            const float v = readlane(x[u][k], l);
+                            const int i = (wave_slot0 + l) * VEC + k;
+                            list_insert(L, I, v, i, K, lane, kmask);
+                        }
+                    }
+                }
+                const float kth = readlane(L, K - 1);
+                if (kth > T) {
+                    T = kth;
+                    if (lane == 0)
+                        __hip_atomic_fetch_max(&s_thr, ordered_bits(kth), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+            }
+        }
+
+        const State s = group_oplus<64>(State{ml, dl});
+        if (lane < K) {
+            s_val[w][lane] = L;
+            s_idx[w][lane] = I;
+        }
+        if (lane == 0) s_md[w] = s;
+        __syncthreads();
+
+        if (w == 0) {
+            State t = s_md[0];
+#pragma unroll
+            for (int ww = 1; ww < W; ++ww) t = oplus(t, s_md[ww]);
+            const float inv_d = rcp(t.d);
+            int pos = 0;
+            float hv = (lane < W) ? s_val[lane][0] : -INFINITY;
+            int hi = (lane < W) ? s_idx[lane][0] : 0x7FFFFFFF;
+            float out_v = -INFINITY;
+            int out_i = 0;
+            for (int k = 0; k < K; ++k) {
+                float bv = hv;
+                int bi = hi;
+                {
+                    float ov = dpp<kDppXor1>(bv);
+                    int oi = dpp<kDppXor1>(bi);
+                    if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+                    ov = dpp<kDppXor2>(bv);
+                    oi = dpp<kDppXor2>(bi);
+                    if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+                    ov = dpp<kDppHalfMirror>(bv);
+                    oi = dpp<kDppHalfMirror>(bi);
+                    if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+                    ov = dpp<kDppMirror>(bv);
+                    oi = dpp<kDppMirror>(bi);
+                    if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+                }
+                bv = readlane(bv, 0);
+                bi = readlane(bi, 0);
+                if (lane == k) {
+                    out_v = bv;
+                    out_i = bi;
+                }
+                if (lane < W && hi == bi) {
+                    ++pos;
+                    hv = (pos < K) ? s_val[lane][pos] : -INFINITY;
+                    hi = (pos < K) ? s_idx[lane][pos] : 0x7FFFFFFF;
+                }
+            }
+            if (lane < K) {
+                probs[row * K + lane] = exp_e(out_v - t.m) * inv_d;
+                idx[row * K + lane] = out_i;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Plain 128-bit copy (bandwidth reference and counter calibration).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_copy(const u32x4* src, u32x4* dst, int64_t n16) {
+    constexpr int U = 4;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = load16<true>(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) store16(dst + i + u * stride, v[u]);
+    }
+    for (; i < n16; i += stride) store16(dst + i, load16<true>(src + i));
+}
+
+}  // namespace onorm

@@ -1,0 +1,161 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments before making any HIP call (so these
+tests need no GPU; nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "online_softmax.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import online_normalizer_amd as ons
+    return ons.lib()
+
+
+@pytest.fixture(scope="module")
+def ons():
+    import online_normalizer_amd
+    return online_normalizer_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:os|safe)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["os_softmax_forward", "os_softmax_topk", "safe_softmax_forward", "os_softmax_stats",
+              "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} not exported"
+
+
+def test_exported_symbols_are_c_linkage():
+    from online_normalizer_amd import LIB_PATH
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms
+
+
+def test_version(ons):
+    assert ons.os_version() == 100
+
+
+EINVAL, EUNSUP = -1, -2
+F32, BF16 = 0, 1
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, 4, 4, F32), EINVAL),        # null input
+    ((FAKE, None, 4, 4, F32), EINVAL),        # null output
+    ((FAKE, FAKE, -1, 4, F32), EINVAL),       # negative rows
+    ((FAKE, FAKE, 4, -1, F32), EINVAL),       # negative cols
+    ((FAKE, FAKE, 4, 4, 7), EINVAL),          # unknown dtype
+    ((FAKE, FAKE, 4, (1 << 30) + 1, F32), EINVAL),  # cols beyond OS_MAX_COLS
+    ((FAKE, FAKE, 1 << 62, 1 << 20, F32), EINVAL),  # rows*cols overflow
+    ((FAKE + 2, FAKE, 4, 4, F32), EINVAL),    # fp32 pointer not 4-byte aligned
+    ((FAKE + 1, FAKE, 4, 4, BF16), EINVAL),   # bf16 pointer not 2-byte aligned
+    ((None, None, 0, 4, F32), 0),             # empty: no-op
+    ((None, None, 4, 0, BF16), 0),            # empty rows: no-op
+])
+def test_forward_and_safe_validation(L, ons, args, code):
+    for fn in (L.os_softmax_forward, L.safe_softmax_forward):
+        rc = fn(*args, None)
+        assert rc == code, (fn.__name__, ons.os_last_error())
+        if code != 0:
+            assert ons.os_last_error()
+        else:
+            assert ons.os_last_error() == ""
+
+
+def test_tuned_validation(L, ons):
+    rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 1024, F32, 48, 4, 0, None)
+    assert rc == EUNSUP and "lanes_per_row=48" in ons.os_last_error()
+    rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 1024, BF16, 1024, 16, 0, None)
+    assert rc == EUNSUP  # that shape exists for fp32 only
+    rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 1025, F32, 64, 4, 0, None)
+    assert rc == EINVAL and "cannot hold" in ons.os_last_error()
+    rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 64, F32, 64, 4, -1, None)
+    assert rc == EINVAL
+    rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 64, F32, -4, 4, 0, None)
+    assert rc == EINVAL
+
+
+def test_stats_validation(L):
+    assert L.os_softmax_stats(FAKE, None, FAKE, 4, 4, F32, None) == EINVAL
+    assert L.os_softmax_stats(FAKE, FAKE + 1, FAKE, 4, 4, F32, None) == EINVAL
+    assert L.os_softmax_stats(None, FAKE, FAKE, 4, 4, F32, None) == EINVAL
+    assert L.os_softmax_stats(None, None, None, 0, 4, F32, None) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, FAKE, 4, 100, 0), EINVAL),     # K < 1
+    ((FAKE, FAKE, FAKE, 4, 100, 33), EINVAL),    # K > KMAX
+    ((FAKE, FAKE, FAKE, 4, 5, 6), EINVAL),       # K > cols
+    ((None, FAKE, FAKE, 4, 100, 8), EINVAL),
+    ((FAKE, None, FAKE, 4, 100, 8), EINVAL),
+    ((FAKE, FAKE, None, 4, 100, 8), EINVAL),
+    ((FAKE + 2, FAKE, FAKE, 4, 100, 8), EINVAL),
+    ((FAKE, FAKE, FAKE, -3, 100, 8), EINVAL),
+    ((FAKE, FAKE, FAKE, 4, (1 << 30) + 1, 8), EINVAL),  # cols beyond OS_MAX_COLS
+    ((None, None, None, 0, 100, 8), 0),
+])
+def test_topk_validation(L, args, code):
+    assert L.os_softmax_topk(*args, None) == code
+
+
+def test_copy_validation(L):
+    assert L.os_device_copy(FAKE, FAKE + 4096, 20, None) == EINVAL      # not a multiple of 16
+    assert L.os_device_copy(FAKE + 4, FAKE + 4096, 32, None) == EINVAL  # misaligned
+    assert L.os_device_copy(FAKE, FAKE + 16, 64, None) == EINVAL        # overlap
+    assert L.os_device_copy(None, None, 0, None) == 0
+
+
+def test_forward_plan(ons):
+    import torch
+    assert ons.os_forward_plan(1) == (4, 2)
+    assert ons.os_forward_plan(128) == (8, 4)
+    assert ons.os_forward_plan(1024) == (64, 4)
+    assert ons.os_forward_plan(2048, torch.bfloat16) == (64, 4)
+    assert ons.os_forward_plan(32000) == (1024, 8)
+    assert ons.os_forward_plan(65536) == (1024, 16)
+    assert ons.os_forward_plan(65537) == (0, 0)
+    assert ons.os_forward_plan(65536, torch.bfloat16) == (1024, 8)
+    assert ons.os_forward_plan(65537, torch.bfloat16) == (0, 0)
+    with pytest.raises(ons.OnlineSoftmaxError):
+        ons.os_forward_plan(-5)
+
+
+def test_binding_rejects_host_tensors(ons):
+    import torch
+    with pytest.raises(ValueError):
+        ons.os_softmax_forward(torch.zeros(4, 4))
+
+
+def test_single_hip_runtime(ons):
+    assert len(ons._hip_runtimes_mapped()) <= 1
+
+
+def test_error_message_is_thread_local(L, ons):
+    import threading
+    assert L.os_softmax_forward(None, FAKE, 4, 4, F32, None) == EINVAL
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(ons.os_last_error()))
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert "NULL" in ons.os_last_error()

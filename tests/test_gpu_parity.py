@@ -1,0 +1,335 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle
+on the same seeded inputs.
+
+Bars: fp32 max |err| <= 2e-6 and per-row |sum - 1| <= 1e-5; bf16 max relative
+error <= 8e-3; top-K indices bit-exact under (value desc, index asc), top-K
+probabilities within 2e-6.  NaN must appear exactly where the oracle has NaN.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import (TOPK_PROB_ABS, assert_fp32_parity, assert_parity, say, to_device, to_host)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ons():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_normalizer_amd
+    return online_normalizer_amd
+
+
+@pytest.fixture(scope="module")
+def orc(oracle_lib):
+    return oracle_lib
+
+
+def bf16_bits(x32: np.ndarray) -> np.ndarray:
+    return workloads.f32_to_bf16_bits(x32)
+
+
+def run_forward(ons, x: np.ndarray, **kw):
+    xd = to_device(x)
+    if "lanes" in kw:
+        y = ons.os_softmax_forward_tuned(xd, kw["lanes"], kw.get("vecs", 0), kw.get("grid", 0))
+    elif kw.get("safe"):
+        y = ons.safe_softmax_forward(xd)
+    else:
+        y = ons.os_softmax_forward(xd)
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+# -- the pages' worked examples --------------------------------------------------
+
+def test_two_shard_example(ons, orc):
+    say("two-shard row [1,2,3]")
+    x = workloads.two_shard_row()
+    y = run_forward(ons, x)
+    assert_fp32_parity(y, orc.softmax(x), "two-shard")
+    m, d = ons.os_softmax_stats(to_device(x))
+    torch.cuda.synchronize()
+    assert float(m[0]) == 3.0
+    assert abs(float(d[0]) - (1.0 + math.exp(-1.0) + math.exp(-2.0))) <= 2e-7
+    # each shard's state on the GPU, merged by the oracle's operator
+    ma, da = ons.os_softmax_stats(to_device(np.array([[1.0, 2.0]], dtype=np.float32)))
+    mb, db = ons.os_softmax_stats(to_device(np.array([[3.0]], dtype=np.float32)))
+    torch.cuda.synchronize()
+    assert float(ma[0]) == 2.0 and abs(float(da[0]) - 1.367879) <= 1e-6
+    assert float(mb[0]) == 3.0 and float(db[0]) == 1.0
+    mab, dab = orc.combine((float(ma[0]), float(da[0])), (float(mb[0]), float(db[0])))
+    assert mab == 3.0 and abs(dab - 1.503214) <= 1e-6
+
+
+def test_lesson_mock_vector(ons, orc):
+    say("mock vector")
+    x = workloads.mock_row()
+    assert_fp32_parity(run_forward(ons, x), orc.softmax(x), "mock")
+
+
+def test_config1(ons, orc):
+    say("config 1: 64x1024 fp32")
+    x = workloads.config(1)
+    assert_fp32_parity(run_forward(ons, x), orc.softmax(x), "config1")
+
+
+# -- every kernel shape, ragged and unaligned tails ---------------------------------
+
+SHAPES = [(4, 2), (4, 4), (8, 2), (8, 4), (16, 2), (16, 4), (32, 4), (64, 2), (64, 4), (64, 8),
+          (128, 8), (256, 8), (512, 8), (1024, 8), (1024, 16)]
+
+
+@pytest.mark.parametrize("lanes,vecs", SHAPES, ids=[f"{a}x{b}" for a, b in SHAPES])
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_every_resident_shape(ons, orc, lanes, vecs, bf16):
+    if bf16 and (lanes, vecs) == (1024, 16):
+        pytest.skip("fp32-only shape")
+    vec = 8 if bf16 else 4
+    cap = lanes * vecs * vec
+    for cols in sorted({cap, cap - 1, cap - vec, max(1, cap // 2 + 3), max(1, cap // 3)}):
+        rows = 37
+        say(f"resident {lanes}x{vecs} bf16={bf16} rows={rows} cols={cols}")
+        x32 = workloads.normal(rows, cols, seed=cols * 7 + lanes, scale=2.0)
+        x = bf16_bits(x32) if bf16 else x32
+        y = run_forward(ons, x, lanes=lanes, vecs=vecs)
+        assert_parity(y, orc.softmax(x), bf16, f"{lanes}x{vecs} cols={cols}")
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_auto_dispatch_edge_columns(ons, orc, bf16):
+    cols_list = [1, 2, 3, 5, 7, 8, 9, 31, 32, 33, 63, 64, 65, 127, 128, 129, 257, 1000, 1023, 1024, 1025,
+                 2047, 2048, 2049, 4097, 8191, 8193, 16385, 32000, 32768, 32769, 65536, 65537, 100003]
+    for cols in cols_list:
+        rows = 19 if cols < 20000 else 5
+        say(f"auto bf16={bf16} rows={rows} cols={cols}")
+        x32 = workloads.normal(rows, cols, seed=1000 + cols, scale=3.0)
+        x = bf16_bits(x32) if bf16 else x32
+        assert_parity(run_forward(ons, x), orc.softmax(x), bf16, f"auto cols={cols}")
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_streaming_two_pass(ons, orc, bf16):
+    for rows, cols in [(3, 1), (5, 100), (7, 4096), (9, 32000), (3, 200001), (2, 1 << 20)]:
+        say(f"stream bf16={bf16} rows={rows} cols={cols}")
+        x32 = workloads.normal(rows, cols, seed=cols + 5, scale=2.0)
+        x = bf16_bits(x32) if bf16 else x32
+        assert_parity(run_forward(ons, x, lanes=0), orc.softmax(x), bf16, f"stream cols={cols}")
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_safe_three_pass(ons, orc, bf16):
+    for rows, cols in [(3, 1), (11, 33), (7, 4096), (9, 32000), (3, 200001)]:
+        say(f"safe3 bf16={bf16} rows={rows} cols={cols}")
+        x32 = workloads.normal(rows, cols, seed=cols + 9, scale=2.0)
+        x = bf16_bits(x32) if bf16 else x32
+        assert_parity(run_forward(ons, x, safe=True), orc.softmax(x), bf16, f"safe cols={cols}")
+
+
+def test_grid_stride_with_few_blocks(ons, orc):
+    """Few workgroups striding over many rows (LDS slot reuse across rows)."""
+    for lanes, vecs, cols in [(1024, 8, 30000), (256, 8, 7000), (8, 4, 128), (64, 4, 1024)]:
+        say(f"grid-stride {lanes}x{vecs} cols={cols}")
+        x = workloads.normal(301, cols, seed=cols + 1, scale=2.0)
+        y = run_forward(ons, x, lanes=lanes, vecs=vecs, grid=3)
+        assert_fp32_parity(y, orc.softmax(x), f"grid=3 {lanes}x{vecs}")
+    say("grid-stride stream")
+    x = workloads.normal(33, 70000, seed=3, scale=2.0)
+    assert_fp32_parity(run_forward(ons, x, lanes=0, grid=2), orc.softmax(x), "stream grid=2")
+
+
+def test_misaligned_base_and_in_place(ons, orc):
+    x = workloads.normal(23, 1024, seed=77, scale=2.0)
+    ref = orc.softmax(x)
+    say("misaligned base pointer")
+    flat = torch.zeros(x.size + 1, dtype=torch.float32, device="cuda")
+    flat[1:] = torch.from_numpy(x.reshape(-1)).cuda()
+    xin = flat[1:].view(23, 1024)
+    out_flat = torch.zeros(x.size + 3, dtype=torch.float32, device="cuda")
+    yout = out_flat[3:].view(23, 1024)
+    ons.os_softmax_forward(xin, out=yout)
+    torch.cuda.synchronize()
+    assert_fp32_parity(to_host(yout), ref, "misaligned")
+    say("in place")
+    xd = to_device(x)
+    ons.os_softmax_forward(xd, out=xd)
+    torch.cuda.synchronize()
+    assert_fp32_parity(to_host(xd), ref, "in-place")
+    xd = to_device(x)
+    ons.safe_softmax_forward(xd, out=xd)
+    torch.cuda.synchronize()
+    assert_fp32_parity(to_host(xd), ref, "in-place safe")
+
+
+@pytest.mark.parametrize("cols", [6, 128, 1024, 32000, 70000])
+def test_special_values(ons, orc, cols):
+    """-inf entries give 0; rows with +inf, NaN, or only -inf give NaN rows."""
+    x = workloads.normal(8, cols, seed=cols, scale=2.0)
+    x[0, ::3] = -np.inf
+    x[1, :] = -np.inf
+    x[2, cols // 2] = np.inf
+    x[3, cols - 1] = np.nan
+    x[4, 0] = 80.0
+    x[4, cols - 1] = 80.0
+    x[5, :] = -np.inf
+    x[5, cols - 1] = -3.0e38
+    x[6, :] = 0.0
+    ref = orc.softmax(x)
+    for kw in ({}, {"safe": True}, {"lanes": 0}):
+        say(f"special values cols={cols} {kw}")
+        assert_fp32_parity(run_forward(ons, x, **kw), ref, f"special {kw}")
+    say(f"special values stats cols={cols}")
+    m, d = ons.os_softmax_stats(to_device(x))
+    torch.cuda.synchronize()
+    m, d = to_host(m), to_host(d)
+    assert m[1] == -np.inf and d[1] == 0.0  # identity state of an all -inf row
+    assert m[5] == np.float32(-3.0e38) and d[5] == 1.0
+
+
+def test_shift_invariance_is_bitwise(ons):
+    """Exact shifts (grid values, +64) give bitwise identical outputs on every path."""
+    for cols, kw in [(128, {}), (1024, {}), (32000, {}), (5000, {"lanes": 0}), (300, {"safe": True}),
+                     (1000, {"lanes": 64, "vecs": 4})]:
+        say(f"shift invariance cols={cols} {kw}")
+        x = workloads.grid_values(17, cols, seed=cols)
+        y0 = run_forward(ons, x, **kw)
+        y1 = run_forward(ons, x + np.float32(64.0), **kw)
+        assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+
+
+def test_deterministic(ons):
+    x = to_device(workloads.config(2, 0, 512))
+    say("determinism")
+    a = ons.os_softmax_forward(x)
+    b = ons.os_softmax_forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_stats_invariants(ons, orc):
+    """1 <= d <= N (up to fp32 rounding), m is the exact row maximum, d matches the oracle."""
+    for n in (1, 2, 4):
+        x = workloads.config(n, 0, 256)
+        say(f"stats config {n}")
+        m, d = ons.os_softmax_stats(to_device(x))
+        torch.cuda.synchronize()
+        m, d = to_host(m).astype(np.float64), to_host(d).astype(np.float64)
+        mo, do = orc.stats(x)
+        N = x.shape[1]
+        assert np.array_equal(m, mo)
+        assert np.all(d >= 1.0) and np.all(d <= N * (1 + N * 2.0 ** -24))
+        assert np.max(np.abs(d - do) / do) <= 1e-5
+    xb = workloads.config(3, 0, 256)
+    m, d = ons.os_softmax_stats(to_device(xb))
+    torch.cuda.synchronize()
+    mo, do = orc.stats(xb)
+    assert np.array_equal(to_host(m).astype(np.float64), mo)
+    assert np.max(np.abs(to_host(d) - do) / do) <= 1e-5
+
+
+# -- fused softmax + top-K ---------------------------------------------------------
+
+def check_topk(ons, orc, x: np.ndarray, K: int, what: str):
+    say(f"topk {what} rows={x.shape[0]} cols={x.shape[1]} K={K}")
+    xd = to_device(np.ascontiguousarray(x))
+    p, i = ons.os_softmax_topk(xd, K)
+    torch.cuda.synchronize()
+    pr, ir = orc.topk(x, K, threads=8)
+    i = to_host(i)
+    bad = np.argwhere(i != ir)
+    assert bad.size == 0, f"{what}: first index mismatch at {bad[:3].tolist()}: {i[bad[0][0]]} vs {ir[bad[0][0]]}"
+    p = to_host(p).astype(np.float64)
+    finite = ~np.isnan(pr)
+    assert np.array_equal(np.isnan(p), np.isnan(pr))
+    assert np.max(np.abs(p[finite] - pr[finite]), initial=0.0) <= TOPK_PROB_ABS, what
+
+
+@pytest.mark.parametrize("K", [1, 2, 8, 17, 32])
+def test_topk_small_and_ragged(ons, orc, K):
+    rng = np.random.Generator(np.random.PCG64(K))
+    for cols in [K, K + 1, K + 3, 63, 100, 1023, 4096, 4099, 65537]:
+        if cols < K:
+            continue
+        x = workloads.normal(13, cols, seed=cols * 31 + K, scale=3.0)
+        check_topk(ons, orc, x, K, f"normal K={K}")
+        xi = rng.integers(-3, 4, size=(13, cols)).astype(np.float32)  # heavy ties
+        check_topk(ons, orc, xi, K, f"ties K={K}")
+
+
+def test_topk_special_rows(ons, orc):
+    cols = 5000
+    x = workloads.normal(8, cols, seed=5, scale=3.0)
+    x[0, :] = 1.25                      # all equal: lowest indices win
+    x[1, ::2] = -np.inf                 # half -inf
+    x[2, :] = -np.inf
+    x[2, [7, 4000, 4999]] = [1.0, 1.0, -2.0]  # fewer finite entries than K: -inf fill by index
+    x[3, 10] = -0.0
+    x[3, 11] = 0.0
+    x[3, :10] = -5.0
+    x[4, [0, 4999, 2500]] = 50.0        # triple tie at the top
+    x[5, 4090:4100] = 40.0              # ties straddling ranks 8 and 9
+    check_topk(ons, orc, x, 8, "special rows")
+    check_topk(ons, orc, x[:, 1:4999], 8, "unaligned cols")
+
+
+def test_topk_matches_forward(ons):
+    """The fused probabilities equal the full softmax at the selected indices."""
+    x = workloads.config(5, 0, 16)
+    xd = to_device(x)
+    say("topk vs forward")
+    p, i = ons.os_softmax_topk(xd, 8)
+    y = ons.os_softmax_forward(xd)
+    torch.cuda.synchronize()
+    yi = torch.gather(y, 1, i.long())
+    assert float((yi - p).abs().max()) <= 2e-6
+
+
+# -- full-size configurations, in the launch configuration the benchmark times -------
+
+def test_config2_full(ons, orc):
+    say("config 2 full: 4096x32000 fp32")
+    x = workloads.config(2)
+    y = run_forward(ons, x)
+    ref = orc.softmax(x, threads=16)
+    assert_fp32_parity(y, ref, "config2")
+
+
+def test_config3_full(ons, orc):
+    say("config 3 full: 524288x2048 bf16")
+    x = workloads.config(3)
+    xd = to_device(x)
+    y = ons.os_softmax_forward(xd)
+    torch.cuda.synchronize()
+    # every row: its bf16 outputs sum to 1 within the rounding of 2048 outputs
+    s = y.float().sum(dim=1)
+    assert float((s - 1).abs().max()) <= 2.0 ** -8 + 1e-5  # |sum of rounding errors| <= u_bf16 * sum(y)
+    rng = np.random.Generator(np.random.PCG64(3))
+    rows = np.unique(np.concatenate([[0, 1, x.shape[0] - 1], rng.choice(x.shape[0], 4096, replace=False)]))
+    yr = to_host(y[torch.from_numpy(rows).cuda()])
+    assert_parity(yr, orc.softmax(x[rows], threads=16), True, "config3 sampled rows")
+
+
+def test_config4_full(ons, orc):
+    say("config 4 full: 8388608x128 fp32")
+    x = workloads.config(4)
+    xd = to_device(x)
+    y = ons.os_softmax_forward(xd)
+    torch.cuda.synchronize()
+    for r0 in range(0, x.shape[0], 1 << 21):  # every row sums to 1
+        s = y[r0:r0 + (1 << 21)].double().sum(dim=1)
+        assert float((s - 1).abs().max()) <= 1e-5
+    rng = np.random.Generator(np.random.PCG64(4))
+    rows = np.unique(np.concatenate([[0, 1, x.shape[0] - 1], rng.choice(x.shape[0], 65536, replace=False)]))
+    yr = to_host(y[torch.from_numpy(rows).cuda()])
+    assert_fp32_parity(yr, orc.softmax(x[rows], threads=16), "config4 sampled rows")
+
+
+def test_config5_topk_full(ons, orc):
+    x = workloads.config(5)
+    check_topk(ons, orc, x, workloads.TOPK_K, "config5")
