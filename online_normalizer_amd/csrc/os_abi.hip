@@ -330,13 +330,10 @@ int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     const char* s = static_cast<const char*>(src);
     const char* d = static_cast<const char*>(dst);
     if (s < d + bytes && d < s + bytes) return fail(OS_EINVAL, "%s: source and destination overlap", fn);
-    int cus = 0;
-    int rc = compute_units(&cus);
-    if (rc != OS_OK) return rc;
     const int64_t n16 = bytes / 16;
-    int64_t want = (n16 + 255) / 256;
-    const int64_t cap = static_cast<int64_t>(cus) * 16;
-    const int grid = static_cast<int>(want < cap ? want : cap);
+    const int64_t tiles = (n16 + 256 * kCopyVecs - 1) / (256 * kCopyVecs);
+    if (tiles > INT32_MAX) return fail(OS_EINVAL, "%s: copy too large", fn);
+    const int grid = static_cast<int>(tiles);
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_copy, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);

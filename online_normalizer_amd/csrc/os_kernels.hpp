@@ -502,18 +502,23 @@ __global__ void __launch_bounds__(W * 64)
 // ---------------------------------------------------------------------------
 // Plain 128-bit copy (bandwidth reference and counter calibration).
 // ---------------------------------------------------------------------------
+// Each thread moves kCopyVecs 16-byte vectors, all loads issued before the
+// stores, one 256-thread workgroup per tile of 256 * kCopyVecs vectors.
+constexpr int kCopyVecs = 8;
+
 __global__ void __launch_bounds__(256) k_copy(const u32x4* src, u32x4* dst, int64_t n16) {
-    constexpr int U = 4;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
-    int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    for (; i + (U - 1) * stride < n16; i += U * stride) {
-        u32x4 v[U];
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * (256 * kCopyVecs) + threadIdx.x;
+    u32x4 v[kCopyVecs];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = load16<true>(src + i + u * stride);
-#pragma unroll
-        for (int u = 0; u < U; ++u) store16(dst + i + u * stride, v[u]);
+    for (int u = 0; u < kCopyVecs; ++u) {
+        const int64_t i = base + u * 256;
+        if (i < n16) v[u] = load16<true>(src + i);
     }
-    for (; i < n16; i += stride) store16(dst + i, load16<true>(src + i));
+#pragma unroll
+    for (int u = 0; u < kCopyVecs; ++u) {
+        const int64_t i = base + u * 256;
+        if (i < n16) store16(dst + i, v[u]);
+    }
 }
 
 }  // namespace onorm

@@ -50,3 +50,10 @@ def test_shapes_of_every_config():
     for n, (rows, cols) in workloads.SHAPES.items():
         x = workloads.config(n, 0, 2)
         assert x.shape == (2, cols)
+
+
+def test_row_range_is_clamped_to_the_workload():
+    x = workloads.config(1, 0, 256)
+    assert x.shape == (64, 1024)
+    assert np.array_equal(x, workloads.config(1))
+    assert workloads.config(5, 250, 400).shape == (6, 128256)

@@ -174,6 +174,8 @@ def config(n: int, row_start: int = 0, row_stop: int | None = None) -> np.ndarra
     """Rows [row_start, row_stop) of workload ``n`` (fp32, or uint16 bf16 bits)."""
     rows, cols = SHAPES[n]
     seed = SEED_BASE + n
+    row_stop = rows if row_stop is None else min(row_stop, rows)
+    row_start = min(row_start, row_stop)
     if n == 1:
         fill, dt = (lambda g, k: g.standard_normal((k, cols), dtype=np.float32)), np.float32
     elif n == 2:
@@ -183,7 +185,7 @@ def config(n: int, row_start: int = 0, row_stop: int | None = None) -> np.ndarra
     elif n == 4:
         fill, dt = (lambda g, k: g.uniform(-10.0, 10.0, (k, cols)).astype(np.float32)), np.float32
     elif n == 5:
-        if row_start != 0 or (row_stop not in (None, rows)):
+        if row_start != 0 or row_stop != rows:
             full = config(5)
             return np.ascontiguousarray(full[row_start:row_stop])
         fill, dt = (lambda g, k: g.standard_normal((k, cols), dtype=np.float32) * np.float32(3.0)), np.float32
