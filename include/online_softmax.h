@@ -67,8 +67,8 @@ extern "C" {
 /* largest K accepted by os_softmax_topk */
 #define OS_TOPK_KMAX 32
 
-/* largest row length (columns) accepted by every entry point: 2^30 */
-#define OS_MAX_COLS (1LL << 30)
+/* largest row length (columns) accepted by every entry point: 2^28 */
+#define OS_MAX_COLS (1LL << 28)
 
 /*
  * y = softmax(x) row by row with the online normalizer (paper summary,

@@ -8,7 +8,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <atomic>
 
 #include "../../include/online_softmax.h"
 #include "os_kernels.hpp"
@@ -64,26 +63,6 @@ bool vector_ok(const void* in, const void* out, int64_t cols, int dtype) {
     return aligned(in, 16) && (out == nullptr || aligned(out, 16)) && ((cols * elt_size(dtype)) % 16) == 0;
 }
 
-// ---------------------------------------------------------------------------
-// Device properties (compute units per device), cached per device ordinal.
-// ---------------------------------------------------------------------------
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_cus[kMaxDevices];
-
-int compute_units(int* cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(OS_ELAUNCH, "hipGetDevice failed");
-    if (dev < 0 || dev >= kMaxDevices) return fail(OS_ELAUNCH, "device ordinal %d out of range", dev);
-    int n = g_cus[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            return fail(OS_ELAUNCH, "hipDeviceGetAttribute(MultiprocessorCount) failed");
-        g_cus[dev].store(n, std::memory_order_relaxed);
-    }
-    *cus = n;
-    return OS_OK;
-}
-
 int launched(const char* fn) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(OS_ELAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -118,18 +97,30 @@ struct ResidentShape {
     }
 
 const ResidentShape kResident[] = {
-    ONORM_RESIDENT(4, 2),    ONORM_RESIDENT(4, 4),    ONORM_RESIDENT(8, 2),
-    ONORM_RESIDENT(8, 4),    ONORM_RESIDENT(16, 2),   ONORM_RESIDENT(16, 4),
-    ONORM_RESIDENT(32, 4),   ONORM_RESIDENT(64, 2),   ONORM_RESIDENT(64, 4),
-    ONORM_RESIDENT(64, 8),   ONORM_RESIDENT(128, 8),  ONORM_RESIDENT(256, 8),
-    ONORM_RESIDENT(512, 8),  ONORM_RESIDENT(1024, 8), ONORM_RESIDENT_F32(1024, 16),
+    ONORM_RESIDENT(4, 1),     ONORM_RESIDENT(4, 2),     ONORM_RESIDENT(4, 4),
+    ONORM_RESIDENT(8, 1),     ONORM_RESIDENT(8, 2),     ONORM_RESIDENT(8, 4),
+    ONORM_RESIDENT(16, 1),    ONORM_RESIDENT(16, 2),    ONORM_RESIDENT(16, 4),
+    ONORM_RESIDENT(32, 1),    ONORM_RESIDENT(32, 2),    ONORM_RESIDENT(32, 4),
+    ONORM_RESIDENT(64, 1),    ONORM_RESIDENT(64, 2),    ONORM_RESIDENT(64, 4),    ONORM_RESIDENT(64, 8),
+    ONORM_RESIDENT(128, 1),   ONORM_RESIDENT(128, 2),   ONORM_RESIDENT(128, 4),   ONORM_RESIDENT(128, 8),
+    ONORM_RESIDENT(256, 1),   ONORM_RESIDENT(256, 2),   ONORM_RESIDENT(256, 4),   ONORM_RESIDENT(256, 8),
+    ONORM_RESIDENT(512, 1),   ONORM_RESIDENT(512, 2),   ONORM_RESIDENT(512, 4),   ONORM_RESIDENT(512, 8),
+    ONORM_RESIDENT(1024, 1),  ONORM_RESIDENT(1024, 2),  ONORM_RESIDENT(1024, 4),  ONORM_RESIDENT(1024, 8),
+    ONORM_RESIDENT_F32(1024, 16),
 };
 constexpr int kNumResident = sizeof(kResident) / sizeof(kResident[0]);
 
-// Automatic choice, smallest capacity first (lanes_per_row, vecs_per_lane).
-const int kAutoPlan[][2] = {{4, 2},   {4, 4},   {8, 4},   {16, 4},  {32, 4},   {64, 4},
-                            {64, 8},  {128, 8}, {256, 8}, {512, 8}, {1024, 8}, {1024, 16}};
-constexpr int kNumAuto = sizeof(kAutoPlan) / sizeof(kAutoPlan[0]);
+// Automatic choice, by the row's 16-byte vector count (next power of two),
+// from a sweep of every built shape on MI355X at ~0.5 GiB per launch: one
+// vector per lane up to 128 vectors (several rows per wavefront up to 64),
+// then two vectors per lane on up to 1024 lanes, then 1024 lanes with 4, 8
+// or 16 vectors.  Entry i covers rows of up to 4 << i vectors.
+const int kAutoF32[][2] = {{4, 1},   {8, 1},   {16, 1},    {32, 1},    {64, 1},    {128, 1},   {128, 2},
+                           {256, 2}, {512, 2}, {1024, 2},  {1024, 4},  {1024, 8},  {1024, 16}};
+const int kAutoBF16[][2] = {{4, 1},   {8, 1},   {16, 1},    {32, 1},    {64, 1},    {64, 2},    {128, 2},
+                            {256, 2}, {512, 2}, {1024, 2},  {1024, 4},  {1024, 8}};
+constexpr int kNumAutoF32 = sizeof(kAutoF32) / sizeof(kAutoF32[0]);
+constexpr int kNumAutoBF16 = sizeof(kAutoBF16) / sizeof(kAutoBF16[0]);
 
 const ResidentShape* find_shape(int lpr, int vpl, int dtype) {
     const int bf = dtype == OS_BF16 ? 1 : 0;
@@ -146,11 +137,12 @@ int64_t vectors_needed(int64_t cols, int dtype) {
 
 void auto_plan(int64_t cols, int dtype, int* lpr, int* vpl) {
     const int64_t need = vectors_needed(cols, dtype);
-    for (int i = 0; i < kNumAuto; ++i) {
-        if (static_cast<int64_t>(kAutoPlan[i][0]) * kAutoPlan[i][1] >= need &&
-            find_shape(kAutoPlan[i][0], kAutoPlan[i][1], dtype) != nullptr) {
-            *lpr = kAutoPlan[i][0];
-            *vpl = kAutoPlan[i][1];
+    const int(*table)[2] = dtype == OS_BF16 ? kAutoBF16 : kAutoF32;
+    const int n = dtype == OS_BF16 ? kNumAutoBF16 : kNumAutoF32;
+    for (int i = 0; i < n; ++i) {
+        if (static_cast<int64_t>(table[i][0]) * table[i][1] >= need) {
+            *lpr = table[i][0];
+            *vpl = table[i][1];
             return;
         }
     }
@@ -158,25 +150,50 @@ void auto_plan(int64_t cols, int dtype, int* lpr, int* vpl) {
     *vpl = 0;
 }
 
-// Streaming kernels: 16 waves per row, 4 vectors per lane per step.
-constexpr int kStreamW = 16;
+// Streaming kernels: 4 vectors per lane per step; waves per row sized to the
+// row (1, 4 or 16), so a short row does not idle most of a workgroup.
 constexpr int kStreamU = 4;
 
-RowKernel stream_kernel(int dtype, bool al) {
-    if (dtype == OS_BF16)
-        return al ? k_stream<true, kStreamW, kStreamU, true> : k_stream<true, kStreamW, kStreamU, false>;
-    return al ? k_stream<false, kStreamW, kStreamU, true> : k_stream<false, kStreamW, kStreamU, false>;
+int stream_waves(int64_t cols, int dtype) {
+    const int64_t need = vectors_needed(cols, dtype);
+    if (need <= 64 * kStreamU) return 1;
+    if (need <= 4 * 64 * kStreamU) return 4;
+    return 16;
 }
 
-// Workgroups for a grid-stride launch over `groups` row groups.
-int grid_for(int64_t groups, int block, int cus, int requested) {
-    if (requested > 0) return static_cast<int>(groups < requested ? groups : requested);
-    // Enough workgroups for every CU to hold several at once; beyond that the
-    // kernels stride over the remaining rows.
-    const int64_t per_cu = block >= 1024 ? 2 : (block >= 512 ? 4 : 16);
-    int64_t cap = static_cast<int64_t>(cus) * per_cu * 8;
-    if (cap > INT32_MAX) cap = INT32_MAX;
-    return static_cast<int>(groups < cap ? groups : cap);
+template <int W>
+RowKernel stream_kernel_w(int dtype, bool al) {
+    if (dtype == OS_BF16) return al ? k_stream<true, W, kStreamU, true> : k_stream<true, W, kStreamU, false>;
+    return al ? k_stream<false, W, kStreamU, true> : k_stream<false, W, kStreamU, false>;
+}
+
+RowKernel stream_kernel(int w, int dtype, bool al) {
+    if (w == 1) return stream_kernel_w<1>(dtype, al);
+    if (w == 4) return stream_kernel_w<4>(dtype, al);
+    return stream_kernel_w<16>(dtype, al);
+}
+
+typedef void (*SafeKernel)(const void*, void*, int64_t, int);
+
+template <int W>
+SafeKernel safe_kernel_w(int dtype, bool al) {
+    if (dtype == OS_BF16) return al ? k_safe3<true, W, kStreamU, true> : k_safe3<true, W, kStreamU, false>;
+    return al ? k_safe3<false, W, kStreamU, true> : k_safe3<false, W, kStreamU, false>;
+}
+
+SafeKernel safe_kernel(int w, int dtype, bool al) {
+    if (w == 1) return safe_kernel_w<1>(dtype, al);
+    if (w == 4) return safe_kernel_w<4>(dtype, al);
+    return safe_kernel_w<16>(dtype, al);
+}
+
+// A launch may hold at most 2^32 - 1 threads in total; stay below 2^31.
+int grid_for(int64_t groups, int block, int requested) {
+    const int64_t max_grid = (int64_t(1) << 31) / block;
+    int64_t g = requested > 0 ? requested : max_grid;
+    if (g > max_grid) g = max_grid;
+    if (g > groups) g = groups;
+    return static_cast<int>(g);
 }
 
 int run_rows(const char* fn, const void* in, void* out, float* st_m, float* st_d, int64_t rows,
@@ -192,24 +209,22 @@ int run_rows(const char* fn, const void* in, void* out, float* st_m, float* st_d
             return fail(OS_EINVAL, "%s: lanes_per_row=%d x vecs_per_lane=%d cannot hold %lld columns", fn, lpr,
                         vpl, (long long)cols);
     }
-    int cus = 0;
-    int rc = compute_units(&cus);
-    if (rc != OS_OK) return rc;
     const bool al = vector_ok(in, out, cols, dtype);
     const int bf = dtype == OS_BF16 ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape == nullptr) {
-        const int block = kStreamW * 64;
-        const int grid = grid_for(rows, block, cus, grid_req);
-        hipLaunchKernelGGL(stream_kernel(dtype, al), dim3(grid), dim3(block), 0, st, in, out, st_m, st_d,
+        const int w = stream_waves(cols, dtype);
+        const int block = w * 64;
+        const int grid = grid_for(rows, block, grid_req);
+        hipLaunchKernelGGL(stream_kernel(w, dtype, al), dim3(grid), dim3(block), 0, st, in, out, st_m, st_d,
                            rows, static_cast<int>(cols));
         return launched(fn);
     }
     const int block = lpr <= 64 ? 256 : lpr;
     const int rpb = block / lpr;
     const int64_t groups = (rows + rpb - 1) / rpb;
-    const int grid = grid_for(groups, block, cus, grid_req);
+    const int grid = grid_for(groups, block, grid_req);
     hipLaunchKernelGGL(shape->fn[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, st_m, st_d, rows,
                        static_cast<int>(cols));
     return launched(fn);
@@ -275,20 +290,13 @@ int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, 
     int rc = check_problem(fn, in, out, true, rows, cols, dtype);
     if (rc == 1) return ok();
     if (rc != OS_OK) return rc;
-    int cus = 0;
-    rc = compute_units(&cus);
-    if (rc != OS_OK) return rc;
     const bool al = vector_ok(in, out, cols, dtype);
-    const int block = kStreamW * 64;
-    const int grid = grid_for(rows, block, cus, 0);
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int w = stream_waves(cols, dtype);
+    const int block = w * 64;
+    const int grid = grid_for(rows, block, 0);
     (void)hipGetLastError();
-    void (*k)(const void*, void*, int64_t, int);
-    if (dtype == OS_BF16)
-        k = al ? k_safe3<true, kStreamW, kStreamU, true> : k_safe3<true, kStreamW, kStreamU, false>;
-    else
-        k = al ? k_safe3<false, kStreamW, kStreamU, true> : k_safe3<false, kStreamW, kStreamU, false>;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, st, in, out, rows, static_cast<int>(cols));
+    hipLaunchKernelGGL(safe_kernel(w, dtype, al), dim3(grid), dim3(block), 0, static_cast<hipStream_t>(stream), in,
+                       out, rows, static_cast<int>(cols));
     return launched(fn);
 }
 
@@ -304,12 +312,9 @@ int os_softmax_topk(const float* in, float* probs, int32_t* idx, int64_t rows, i
     if (in == nullptr || probs == nullptr || idx == nullptr) return fail(OS_EINVAL, "%s: NULL pointer", fn);
     if (!aligned(in, 4) || !aligned(probs, 4) || !aligned(idx, 4))
         return fail(OS_EINVAL, "%s: pointers must be 4-byte aligned", fn);
-    int cus = 0;
-    int rc = compute_units(&cus);
-    if (rc != OS_OK) return rc;
     const bool al = aligned(in, 16) && (cols % 4) == 0;
     constexpr int W = 16, U = 4;
-    const int grid = grid_for(rows, W * 64, cus, 0);
+    const int grid = grid_for(rows, W * 64, 0);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (al)
@@ -330,13 +335,11 @@ int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     const char* s = static_cast<const char*>(src);
     const char* d = static_cast<const char*>(dst);
     if (s < d + bytes && d < s + bytes) return fail(OS_EINVAL, "%s: source and destination overlap", fn);
-    const int64_t n16 = bytes / 16;
-    const int64_t tiles = (n16 + 256 * kCopyVecs - 1) / (256 * kCopyVecs);
+    const int64_t tiles = (bytes + 4095) / 4096;
     if (tiles > INT32_MAX) return fail(OS_EINVAL, "%s: copy too large", fn);
-    const int grid = static_cast<int>(tiles);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_copy, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+    hipLaunchKernelGGL(k_copy, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const char*>(src), static_cast<char*>(dst), bytes);
     return launched(fn);
 }
 

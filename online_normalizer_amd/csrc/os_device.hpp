@@ -107,34 +107,101 @@ __device__ __forceinline__ State group_oplus(State s) {
     return s;
 }
 
-// Plain maximum / sum over the whole wave (for the three-pass baseline and
-// the top-K threshold); every lane ends with the same bits.
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp<kDppXor1>(v));
-    v = fmaxf(v, dpp<kDppXor2>(v));
-    v = fmaxf(v, dpp<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp<kDppMirror>(v));
-    f32x2 t = swap_rows16(v);
-    v = fmaxf(t[0], t[1]);
-    t = swap_rows32(v);
-    return fmaxf(t[0], t[1]);
+// Maximum / sum over an aligned group of G lanes (1..64), same bits in every lane.
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (G >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+    if constexpr (G >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+    if constexpr (G >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    if constexpr (G >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+    if constexpr (G >= 32) {
+        const f32x2 t = swap_rows16(v);
+        v = fmaxf(t[0], t[1]);
+    }
+    if constexpr (G >= 64) {
+        const f32x2 t = swap_rows32(v);
+        v = fmaxf(t[0], t[1]);
+    }
+    return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    v = v + dpp<kDppXor1>(v);
-    v = v + dpp<kDppXor2>(v);
-    v = v + dpp<kDppHalfMirror>(v);
-    v = v + dpp<kDppMirror>(v);
-    f32x2 t = swap_rows16(v);
-    v = t[0] + t[1];
-    t = swap_rows32(v);
-    return t[0] + t[1];
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (G >= 2) v = v + dpp<kDppXor1>(v);
+    if constexpr (G >= 4) v = v + dpp<kDppXor2>(v);
+    if constexpr (G >= 8) v = v + dpp<kDppHalfMirror>(v);
+    if constexpr (G >= 16) v = v + dpp<kDppMirror>(v);
+    if constexpr (G >= 32) {
+        const f32x2 t = swap_rows16(v);
+        v = t[0] + t[1];
+    }
+    if constexpr (G >= 64) {
+        const f32x2 t = swap_rows32(v);
+        v = t[0] + t[1];
+    }
+    return v;
 }
+
+// (+) over the G lane states of a group, applied to all G operands at once:
+// m = max_l m_l, d = sum_l d_l e^{m_l - m}.  By associativity and
+// commutativity this equals any bracketing of the binary operator; it costs
+// one exponential per lane plus a max and a sum reduction, instead of one
+// exponential and a select per butterfly step.
+template <int G>
+__device__ __forceinline__ State group_merge(State s) {
+    const float m = group_max<G>(s.m);
+    return State{m, group_sum<G>(s.d * exp_e(s.m - m))};
+}
+
+// Plain maximum / sum over the whole wave (for the three-pass baseline and
+// the top-K threshold); every lane ends with the same bits.
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 __device__ __forceinline__ float readlane(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 __device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// ---------------------------------------------------------------------------
+// Buffer access.  Every kernel reads and writes through a buffer resource
+// that covers exactly the bytes it may touch (one row, or one copy tile).
+// The hardware range check turns out-of-range loads into 0 and drops
+// out-of-range stores, so tails need no branches; loads therefore issue
+// back to back instead of each waiting behind a bounds-check branch.
+// Offsets are 32-bit bytes; every resource spans at most 2^30 bytes (rows
+// are at most 2^28 elements), so offset 2^31 is always outside.
+// ---------------------------------------------------------------------------
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer: 32-bit data format
+constexpr int kNonTemporal = 2;           // cache-policy bit: streaming (nt)
+
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ Buf(const void* base, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                              kBufferWord3)) {}
+    // STREAM = true: data touched once (non-temporal).  A pass whose data is
+    // read again later uses plain loads so the re-read can hit in cache.
+    template <bool STREAM>
+    __device__ __forceinline__ u32x4 load16(uint32_t off) const {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, STREAM ? kNonTemporal : 0);
+    }
+    __device__ __forceinline__ uint32_t load4(uint32_t off) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+    __device__ __forceinline__ uint16_t load2(uint32_t off) const {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    }
+    __device__ __forceinline__ void store16(uint32_t off, u32x4 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNonTemporal);
+    }
+    __device__ __forceinline__ void store4(uint32_t off, uint32_t v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+    }
+    __device__ __forceinline__ void store2(uint32_t off, uint16_t v) const {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Element access.  A 16-byte vector holds 4 fp32 or 8 bf16 values.
@@ -154,11 +221,12 @@ struct Elt<false> {
         return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                      __float_as_uint(v[3])};
     }
-    __device__ static __forceinline__ float load1(const void* row, int e) {
-        return static_cast<const float*>(row)[e];
+    // byte offsets; an offset outside the resource reads 0 / is dropped
+    __device__ static __forceinline__ float load1(const Buf& b, uint32_t off) {
+        return __uint_as_float(b.load4(off));
     }
-    __device__ static __forceinline__ void store1(void* row, int e, float v) {
-        static_cast<float*>(row)[e] = v;
+    __device__ static __forceinline__ void store1(const Buf& b, uint32_t off, float v) {
+        b.store4(off, __float_as_uint(v));
     }
 };
 
@@ -185,26 +253,12 @@ struct Elt<true> {
         return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                      pack_bf16x2(v[6], v[7])};
     }
-    __device__ static __forceinline__ float load1(const void* row, int e) {
-        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[e]) << 16);
+    __device__ static __forceinline__ float load1(const Buf& b, uint32_t off) {
+        return __uint_as_float(static_cast<uint32_t>(b.load2(off)) << 16);
     }
-    __device__ static __forceinline__ void store1(void* row, int e, float v) {
-        static_cast<uint16_t*>(row)[e] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    __device__ static __forceinline__ void store1(const Buf& b, uint32_t off, float v) {
+        b.store2(off, static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu));
     }
 };
-
-// 128-bit global loads and stores.  STREAM = true marks data touched once
-// (non-temporal hint); a pass whose data is read again later uses plain
-// loads so that the re-read can hit in L2 / Infinity Cache.
-template <bool STREAM>
-__device__ __forceinline__ u32x4 load16(const void* p) {
-    if constexpr (STREAM)
-        return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
-    else
-        return *static_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ void store16(void* p, u32x4 v) {
-    __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
-}
 
 }  // namespace onorm

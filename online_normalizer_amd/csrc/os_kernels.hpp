@@ -6,10 +6,11 @@
 //
 // Row layout: row-major, stride == cols.  Lanes address a row in 16-byte
 // vectors: vector slot vi covers elements [vi*VEC, vi*VEC + VEC).  ALIGNED
-// kernels move whole vectors with 128-bit accesses (row starts 16-byte
+// kernels move whole vectors with 128-bit buffer accesses (row starts 16-byte
 // aligned, cols a multiple of VEC); the others move the same slots element by
-// element with bounds checks.  Missing elements read as -inf, which adds
-// e^{-inf} = 0 to any state.
+// element.  Every row is read and written through a buffer resource that
+// covers that row only; elements past the end read as -inf (e^{-inf} adds 0
+// to any state) and stores past the end are dropped by the hardware.
 #pragma once
 
 #include "os_device.hpp"
@@ -24,39 +25,77 @@ __device__ __forceinline__ int vec_count(int cols) {
     return ALIGNED ? cols / VEC : (cols + VEC - 1) / VEC;
 }
 
-// Load vector slot vi of a row into v[VEC] (-inf where out of range).
+// An offset no buffer resource here reaches: accesses there are dropped.
+constexpr uint32_t kOutside = 0x80000000u;
+
+// Load vector slot vi of a row into v[VEC]; -inf where the slot or element is
+// outside the row (or the row is not live).  `row_off` is the byte offset of
+// the row inside the buffer resource.
 template <bool BF16, bool ALIGNED, bool STREAM>
-__device__ __forceinline__ void load_slot(const char* row, int vi, int nvec, int cols, bool live,
+__device__ __forceinline__ void load_slot(const Buf& b, uint32_t row_off, int vi, int nvec, int cols, bool live,
                                           float* v) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     if constexpr (ALIGNED) {
-        if (live && vi < nvec) {
-            E::unpack(load16<STREAM>(row + static_cast<int64_t>(vi) * 16), v);
-        } else {
+        E::unpack(b.load16<STREAM>(row_off + static_cast<uint32_t>(vi) * 16u), v);
+        const bool ok = live && vi < nvec;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) v[k] = -INFINITY;
-        }
+        for (int k = 0; k < VEC; ++k) v[k] = ok ? v[k] : -INFINITY;
     } else {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const int e = vi * VEC + k;
-            v[k] = (live && e < cols) ? E::load1(row, e) : -INFINITY;
+            const bool ok = live && e < cols;
+            const float t = E::load1(b, ok ? row_off + static_cast<uint32_t>(e) * E::kSize : kOutside);
+            v[k] = ok ? t : -INFINITY;
         }
     }
 }
 
-template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ void store_slot(char* row, int vi, int nvec, int cols, const float* v) {
+// Two-phase form used by the register-resident kernels: issue the raw 128-bit
+// loads of all VPL slots, fence the scheduler, then unpack.  Without the
+// fence the scheduler may sink each load next to its unpack code, and every
+// load then waits for the previous one to return.
+template <bool BF16, int VPL, bool ALIGNED, bool STREAM>
+__device__ __forceinline__ void load_slots(const Buf& b, uint32_t row_off, int first, int stride, int nvec,
+                                           int cols, bool live, float (&x)[VPL][Elt<BF16>::kVec]) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     if constexpr (ALIGNED) {
-        if (vi < nvec) store16(row + static_cast<int64_t>(vi) * 16, E::pack(v));
+        u32x4 raw[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            raw[v] = b.load16<STREAM>(row_off + static_cast<uint32_t>(first + v * stride) * 16u);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            E::unpack(raw[v], x[v]);
+            const bool ok = live && (first + v * stride) < nvec;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) x[v][k] = ok ? x[v][k] : -INFINITY;
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) load_slot<BF16, false, STREAM>(b, row_off, first + v * stride, nvec, cols, live, x[v]);
+    }
+}
+
+// Store slot vi of a row; slots / elements outside the row are sent to an
+// offset outside the resource, which the hardware drops.
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ void store_slot(const Buf& b, uint32_t row_off, int vi, int nvec, int cols, bool live,
+                                           const float* v) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    if constexpr (ALIGNED) {
+        const bool ok = live && vi < nvec;
+        b.store16(ok ? row_off + static_cast<uint32_t>(vi) * 16u : kOutside, E::pack(v));
     } else {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const int e = vi * VEC + k;
-            if (e < cols) E::store1(row, e, v[k]);
+            const bool ok = live && e < cols;
+            E::store1(b, ok ? row_off + static_cast<uint32_t>(e) * E::kSize : kOutside, v[k]);
         }
     }
 }
@@ -65,11 +104,10 @@ __device__ __forceinline__ void store_slot(char* row, int vi, int nvec, int cols
 // Register-resident forward: the row is read from HBM once.
 //
 // LPR lanes share a row and each holds VPL vectors of it in VGPRs.  LPR <= 64:
-// 256-thread workgroups carry 256/LPR rows, the merge stays inside the
-// wavefront (DPP / permlane).  LPR = 64*W: one row per W-wave workgroup, and
-// the W wave states meet once in LDS (one barrier per row; the LDS slots
-// alternate between rows so the next row's writes never race this row's
-// reads).
+// 256-thread workgroups carry 256/LPR rows and the merge stays inside the
+// wavefront.  LPR = 64*W: one row per W-wave workgroup; the W wave states meet
+// once in LDS (one barrier per row; the LDS slots alternate between rows so
+// the next row's writes never race this row's reads).
 //
 // Pass 1 per lane (the tile form of the recurrence, with the lane's slice as
 // one tile): m_l = max of the slice, e_k = e^{x_k - m_l}, d_l = sum e_k; the
@@ -92,17 +130,21 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
     const int j = tid % LPR;
     const int g = tid / LPR;
     const int nvec = vec_count<BF16, ALIGNED>(cols);
-    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
     int par = 0;
 
     for (int64_t rb = blockIdx.x; rb * RPB < rows; rb += gridDim.x) {
-        const int64_t row = rb * RPB + g;
-        const bool live = row < rows;
-        const char* rin = static_cast<const char*>(in) + (live ? row : 0) * row_bytes;
+        // One buffer resource per workgroup, over its (up to RPB) rows: the
+        // descriptor is uniform, and rows past the end fall outside it.
+        const int64_t row0 = rb * RPB;
+        const int64_t nrows = (rows - row0) < RPB ? (rows - row0) : RPB;
+        const int64_t row = row0 + g;
+        const bool live = g < nrows;
+        const uint32_t row_off = static_cast<uint32_t>(g) * row_bytes;
+        const Buf bin(static_cast<const char*>(in) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
 
         float x[VPL][VEC];
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) load_slot<BF16, ALIGNED, true>(rin, v * LPR + j, nvec, cols, live, x[v]);
+        load_slots<BF16, VPL, ALIGNED, true>(bin, row_off, j, LPR, nvec, cols, live, x);
 
         float ml = kFloor;
 #pragma unroll
@@ -118,7 +160,7 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
                 dl += x[v][k];
             }
 
-        State s = group_oplus<GROUP>(State{ml, dl});
+        State s = group_merge<GROUP>(State{ml, dl});
         if constexpr (W > 1) {
             if ((tid & (kWave - 1)) == 0) lds[par][tid / kWave] = s;
             __syncthreads();
@@ -128,20 +170,18 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
             par ^= 1;
         }
 
-        if (live) {
-            if (st_m != nullptr && j == 0) {
-                st_m[row] = (s.d == 0.0f) ? -INFINITY : s.m;
-                st_d[row] = s.d;
-            }
-            if (out != nullptr) {
-                const float scale = exp_e(ml - s.m) * rcp(s.d);
-                char* rout = static_cast<char*>(out) + row * row_bytes;
+        if (st_m != nullptr && live && j == 0) {
+            st_m[row] = (s.d == 0.0f) ? -INFINITY : s.m;
+            st_d[row] = s.d;
+        }
+        if (out != nullptr) {
+            const float scale = exp_e(ml - s.m) * rcp(s.d);
+            const Buf bout(static_cast<char*>(out) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
 #pragma unroll
-                for (int v = 0; v < VPL; ++v) {
+            for (int v = 0; v < VPL; ++v) {
 #pragma unroll
-                    for (int k = 0; k < VEC; ++k) x[v][k] *= scale;
-                    store_slot<BF16, ALIGNED>(rout, v * LPR + j, nvec, cols, x[v]);
-                }
+                for (int k = 0; k < VEC; ++k) x[v][k] *= scale;
+                store_slot<BF16, ALIGNED>(bout, row_off, v * LPR + j, nvec, cols, live, x[v]);
             }
         }
     }
@@ -165,16 +205,15 @@ __global__ void __launch_bounds__(W * 64)
 
     const int tid = threadIdx.x;
     const int nvec = vec_count<BF16, ALIGNED>(cols);
-    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
     int par = 0;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const char* rin = static_cast<const char*>(in) + row * row_bytes;
+        const Buf bin(static_cast<const char*>(in) + row * row_bytes, row_bytes);
         float ml = kFloor, dl = 0.0f;
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-#pragma unroll
-            for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, false>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+            load_slots<BF16, U, ALIGNED, false>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
             float mc = kFloor;
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -189,7 +228,7 @@ __global__ void __launch_bounds__(W * 64)
             dl = acc;
             ml = mn;
         }
-        State s = group_oplus<64>(State{ml, dl});
+        State s = group_merge<64>(State{ml, dl});
         if constexpr (W > 1) {
             if ((tid & (kWave - 1)) == 0) lds[par][tid / kWave] = s;
             __syncthreads();
@@ -204,16 +243,15 @@ __global__ void __launch_bounds__(W * 64)
         }
         if (out != nullptr) {
             const float inv_d = rcp(s.d);
-            char* rout = static_cast<char*>(out) + row * row_bytes;
+            const Buf bout(static_cast<char*>(out) + row * row_bytes, row_bytes);
             for (int base = 0; base < nvec; base += BLOCK * U) {
                 float x[U][VEC];
-#pragma unroll
-                for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, true>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                load_slots<BF16, U, ALIGNED, true>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - s.m) * inv_d;
-                    store_slot<BF16, ALIGNED>(rout, base + u * BLOCK + tid, nvec, cols, x[u]);
+                    store_slot<BF16, ALIGNED>(bout, 0u, base + u * BLOCK + tid, nvec, cols, true, x[u]);
                 }
             }
         }
@@ -236,17 +274,16 @@ __global__ void __launch_bounds__(W * 64)
 
     const int tid = threadIdx.x;
     const int nvec = vec_count<BF16, ALIGNED>(cols);
-    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
     int par = 0;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const char* rin = static_cast<const char*>(in) + row * row_bytes;
+        const Buf bin(static_cast<const char*>(in) + row * row_bytes, row_bytes);
         // pass 1: maximum
         float m = kFloor;
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-#pragma unroll
-            for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, false>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+            load_slots<BF16, U, ALIGNED, false>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -264,8 +301,7 @@ __global__ void __launch_bounds__(W * 64)
         float d = 0.0f;
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-#pragma unroll
-            for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, false>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+            load_slots<BF16, U, ALIGNED, false>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -282,16 +318,15 @@ __global__ void __launch_bounds__(W * 64)
         }
         // pass 3: normalise and store
         const float inv_d = rcp(d);
-        char* rout = static_cast<char*>(out) + row * row_bytes;
+        const Buf bout(static_cast<char*>(out) + row * row_bytes, row_bytes);
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-#pragma unroll
-            for (int u = 0; u < U; ++u) load_slot<BF16, ALIGNED, true>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+            load_slots<BF16, U, ALIGNED, true>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - m) * inv_d;
-                store_slot<BF16, ALIGNED>(rout, base + u * BLOCK + tid, nvec, cols, x[u]);
+                store_slot<BF16, ALIGNED>(bout, 0u, base + u * BLOCK + tid, nvec, cols, true, x[u]);
             }
         }
     }
@@ -370,6 +405,7 @@ __global__ void __launch_bounds__(W * 64)
     static_assert(W <= 16, "the final selection runs inside one 16-lane DPP row");
     constexpr int BLOCK = W * 64;
     constexpr int VEC = 4;
+    constexpr int STEP = BLOCK * U;
     __shared__ float s_val[W][kTopKMax];
     __shared__ int s_idx[W][kTopKMax];
     __shared__ State s_md[W];
@@ -380,9 +416,10 @@ __global__ void __launch_bounds__(W * 64)
     const int w = tid / kWave;
     const uint64_t kmask = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
     const int nvec = vec_count<false, ALIGNED>(cols);
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * 4u;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const char* rin = reinterpret_cast<const char*>(in + row * static_cast<int64_t>(cols));
+        const Buf bin(in + row * static_cast<int64_t>(cols), row_bytes);
         if (tid == 0) s_thr = ordered_bits(-INFINITY);
         __syncthreads();
 
@@ -391,10 +428,32 @@ __global__ void __launch_bounds__(W * 64)
         int I = 0x7FFFFFFF;
         float T = -INFINITY;
         bool first = true;
-        for (int base = 0; base < nvec; base += BLOCK * U) {
-            float x[U][VEC];
+        // Software pipeline: the raw loads of the next tile are issued before
+        // the current tile is folded, so they are in flight during the
+        // compute.  Loads past the end of the row touch no memory (buffer
+        // range check) and are masked to -inf.
+        u32x4 raw[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) load_slot<false, ALIGNED, true>(rin, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+        for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(u * BLOCK + tid) * 16u);
+        for (int base = 0; base < nvec; base += STEP) {
+            float x[U][VEC];
+            if constexpr (ALIGNED) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    Elt<false>::unpack(raw[u], x[u]);
+                    const bool ok = base + u * BLOCK + tid < nvec;
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) x[u][k] = ok ? x[u][k] : -INFINITY;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    raw[u] = bin.load16<true>(static_cast<uint32_t>(base + STEP + u * BLOCK + tid) * 16u);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) load_slot<false, false, true>(bin, 0u, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+            }
+
             float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -444,7 +503,7 @@ __global__ void __launch_bounds__(W * 64)
             }
         }
 
-        const State s = group_oplus<64>(State{ml, dl});
+        const State s = group_merge<64>(State{ml, dl});
         if (lane < K) {
             s_val[w][lane] = L;
             s_idx[w][lane] = I;
@@ -500,25 +559,16 @@ __global__ void __launch_bounds__(W * 64)
 }
 
 // ---------------------------------------------------------------------------
-// Plain 128-bit copy (bandwidth reference and counter calibration).
+// Plain 128-bit copy (bandwidth reference and counter calibration): each
+// thread moves one 16-byte vector, 256-thread workgroups, one tile each.
 // ---------------------------------------------------------------------------
-// Each thread moves kCopyVecs 16-byte vectors, all loads issued before the
-// stores, one 256-thread workgroup per tile of 256 * kCopyVecs vectors.
-constexpr int kCopyVecs = 8;
-
-__global__ void __launch_bounds__(256) k_copy(const u32x4* src, u32x4* dst, int64_t n16) {
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * (256 * kCopyVecs) + threadIdx.x;
-    u32x4 v[kCopyVecs];
-#pragma unroll
-    for (int u = 0; u < kCopyVecs; ++u) {
-        const int64_t i = base + u * 256;
-        if (i < n16) v[u] = load16<true>(src + i);
-    }
-#pragma unroll
-    for (int u = 0; u < kCopyVecs; ++u) {
-        const int64_t i = base + u * 256;
-        if (i < n16) store16(dst + i, v[u]);
-    }
+__global__ void __launch_bounds__(256) k_copy(const char* src, char* dst, int64_t bytes) {
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 4096;
+    const int64_t left = bytes - t0;
+    const uint32_t tile = static_cast<uint32_t>(left < 4096 ? left : 4096);
+    const Buf bs(src + t0, tile), bd(dst + t0, tile);
+    const uint32_t off = threadIdx.x * 16u;
+    bd.store16(off, bs.load16<true>(off));
 }
 
 }  // namespace onorm

@@ -65,7 +65,7 @@ FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced (validati
     ((FAKE, FAKE, -1, 4, F32), EINVAL),       # negative rows
     ((FAKE, FAKE, 4, -1, F32), EINVAL),       # negative cols
     ((FAKE, FAKE, 4, 4, 7), EINVAL),          # unknown dtype
-    ((FAKE, FAKE, 4, (1 << 30) + 1, F32), EINVAL),  # cols beyond OS_MAX_COLS
+    ((FAKE, FAKE, 4, (1 << 28) + 1, F32), EINVAL),  # cols beyond OS_MAX_COLS
     ((FAKE, FAKE, 1 << 62, 1 << 20, F32), EINVAL),  # rows*cols overflow
     ((FAKE + 2, FAKE, 4, 4, F32), EINVAL),    # fp32 pointer not 4-byte aligned
     ((FAKE + 1, FAKE, 4, 4, BF16), EINVAL),   # bf16 pointer not 2-byte aligned
@@ -111,7 +111,7 @@ def test_stats_validation(L):
     ((FAKE, FAKE, None, 4, 100, 8), EINVAL),
     ((FAKE + 2, FAKE, FAKE, 4, 100, 8), EINVAL),
     ((FAKE, FAKE, FAKE, -3, 100, 8), EINVAL),
-    ((FAKE, FAKE, FAKE, 4, (1 << 30) + 1, 8), EINVAL),  # cols beyond OS_MAX_COLS
+    ((FAKE, FAKE, FAKE, 4, (1 << 28) + 1, 8), EINVAL),  # cols beyond OS_MAX_COLS
     ((None, None, None, 0, 100, 8), 0),
 ])
 def test_topk_validation(L, args, code):
@@ -127,10 +127,16 @@ def test_copy_validation(L):
 
 def test_forward_plan(ons):
     import torch
-    assert ons.os_forward_plan(1) == (4, 2)
-    assert ons.os_forward_plan(128) == (8, 4)
-    assert ons.os_forward_plan(1024) == (64, 4)
-    assert ons.os_forward_plan(2048, torch.bfloat16) == (64, 4)
+    assert ons.os_forward_plan(1) == (4, 1)
+    assert ons.os_forward_plan(128) == (32, 1)
+    assert ons.os_forward_plan(1024) == (128, 2)
+    assert ons.os_forward_plan(2048, torch.bfloat16) == (128, 2)
+    assert ons.os_forward_plan(4096) == (512, 2)
+    assert ons.os_forward_plan(4097) == (1024, 2)
+    for cols in range(1, 70000, 97):  # every automatic shape holds its row
+        for dt, vec in ((torch.float32, 4), (torch.bfloat16, 8)):
+            lanes, vecs = ons.os_forward_plan(cols, dt)
+            assert lanes == 0 or lanes * vecs * vec >= cols
     assert ons.os_forward_plan(32000) == (1024, 8)
     assert ons.os_forward_plan(65536) == (1024, 16)
     assert ons.os_forward_plan(65537) == (0, 0)

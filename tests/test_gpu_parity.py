@@ -82,8 +82,8 @@ def test_config1(ons, orc):
 
 # -- every kernel shape, ragged and unaligned tails ---------------------------------
 
-SHAPES = [(4, 2), (4, 4), (8, 2), (8, 4), (16, 2), (16, 4), (32, 4), (64, 2), (64, 4), (64, 8),
-          (128, 8), (256, 8), (512, 8), (1024, 8), (1024, 16)]
+SHAPES = [(lanes, vecs) for lanes in (4, 8, 16, 32) for vecs in (1, 2, 4)] + \
+    [(lanes, vecs) for lanes in (64, 128, 256, 512, 1024) for vecs in (1, 2, 4, 8)] + [(1024, 16)]
 
 
 @pytest.mark.parametrize("lanes,vecs", SHAPES, ids=[f"{a}x{b}" for a, b in SHAPES])
@@ -142,6 +142,23 @@ def test_grid_stride_with_few_blocks(ons, orc):
     say("grid-stride stream")
     x = workloads.normal(33, 70000, seed=3, scale=2.0)
     assert_fp32_parity(run_forward(ons, x, lanes=0, grid=2), orc.softmax(x), "stream grid=2")
+
+
+def test_many_rows_cap_the_grid(ons):
+    """More rows than a single launch can hold threads for: the grid is capped
+    and the kernels stride over the rest (cols = 1, so every output is 1)."""
+    rows = 40_000_000
+    x = torch.randn(rows, 1, device="cuda")
+    for kw in ({"lanes": 0}, {"safe": True}, {}):
+        say(f"many rows {rows}x1 {kw}")
+        if "lanes" in kw:
+            y = ons.os_softmax_forward_tuned(x, 0, 0)
+        elif kw:
+            y = ons.safe_softmax_forward(x)
+        else:
+            y = ons.os_softmax_forward(x)
+        torch.cuda.synchronize()
+        assert bool((y == 1.0).all()), kw
 
 
 def test_misaligned_base_and_in_place(ons, orc):
