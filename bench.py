@@ -118,6 +118,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true", help="skip the comparison legs")
+    ap.add_argument("--all-configs", metavar="FILE", default=None,
+                    help="also time every workload (forward, three-pass baseline, copy; top-K for the "
+                         "top-K workload) and write the table to FILE as JSON")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
@@ -213,8 +216,56 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_host, cols * 8)
 
+    if args.all_configs:
+        with open(args.all_configs, "w") as f:
+            json.dump(all_configs(ons, stream), f, indent=1)
+
     print(json.dumps(out), flush=True)
     return 0
+
+
+def all_configs(ons, stream):
+    """Per-workload kernel times (median of HIP-event timed launches)."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    table = []
+    for n in (1, 2, 3, 4):
+        xh = workloads.config(n)
+        if xh.dtype == np.uint16:
+            x = torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            x = torch.from_numpy(xh).cuda()
+        del xh
+        y = torch.empty_like(x)
+        rows, cols = x.shape
+        nbytes = rows * cols * x.element_size() * 2
+        reps = 200 if n == 1 else 30
+        entry = {"workload": n, "rows": rows, "cols": cols, "dtype": str(x.dtype).replace("torch.", ""),
+                 "shape": list(ons.os_forward_plan(cols, x.dtype)), "algorithmic_bytes": nbytes}
+        for name, fn in (("online", lambda: ons.os_softmax_forward(x, out=y)),
+                         ("safe_3pass", lambda: ons.safe_softmax_forward(x, out=y)),
+                         ("copy", lambda: ons.os_device_copy(x, y))):
+            _, per = time_launches(fn, reps, 5, stream)
+            t = sorted(per)[len(per) // 2]
+            entry[name] = {"us": round(t * 1e6, 2), "GBs": round(nbytes / t / 1e9, 1),
+                           "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1)}
+        entry["online"]["rows_per_s"] = round(rows / (entry["online"]["us"] * 1e-6), 1)
+        table.append(entry)
+        del x, y
+    xt = torch.from_numpy(workloads.config(5)).cuda()
+    rows, cols = xt.shape
+    _, per = time_launches(lambda: ons.os_softmax_topk(xt, workloads.TOPK_K), 200, 5, stream)
+    t = sorted(per)[len(per) // 2]
+    nbytes = rows * cols * 4 + rows * workloads.TOPK_K * 8
+    table.append({"workload": 5, "rows": rows, "cols": cols, "dtype": "float32", "K": workloads.TOPK_K,
+                  "algorithmic_bytes": nbytes,
+                  "topk": {"us": round(t * 1e6, 2), "GBs": round(nbytes / t / 1e9, 1),
+                           "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1),
+                           "rows_per_s": round(rows / t, 1)}})
+    return table
 
 
 if __name__ == "__main__":

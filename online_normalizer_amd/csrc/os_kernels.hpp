@@ -341,8 +341,9 @@ __global__ void __launch_bounds__(W * 64)
 // rank k) under the total order (value desc, index asc).  Most elements are
 // rejected by a compare with a wave-uniform threshold T, a lower bound on the
 // row's K-th largest value:
-//   - first tile: the K-th largest of the 64 lane maxima (K lanes each hold
-//     an element at least that large);
+//   - first tile: the smallest of >= K group maxima of the lane maxima (so at
+//     least K elements are that large), the largest such bound over the
+//     workgroup's waves (LDS atomic max, one barrier), before any insert;
 //   - then: the K-th entry of the wave's own list, and the largest K-th entry
 //     published by any wave of the workgroup (an LDS atomic max).
 // Survivors (x >= T, so ties at T are kept) are inserted one at a time:
@@ -383,20 +384,26 @@ __device__ __forceinline__ void list_insert(float& L, int& I, float v, int i, in
     }
 }
 
-// K-th largest of one value per lane (lanes with equal values count
-// separately); -inf when fewer than K lanes hold a value above -inf.
-__device__ __forceinline__ float kth_largest_lane_value(float v, int K) {
-    float t = -INFINITY;
-    int need = K;
-    for (int r = 0; r < K; ++r) {
-        const float top = wave_max(v);
-        if (top == -INFINITY) break;
-        need -= __popcll(__ballot(v == top));
-        t = top;
-        if (need <= 0) break;
-        v = (v == top) ? -INFINITY : v;
+// A lower bound on the K-th largest element of a wave's tile from one value
+// per lane (its tile maximum): split the wave into G-lane groups with
+// 64 / G >= K, take each group's maximum (an element of the tile) and return
+// the smallest of them.  At least K distinct elements are >= the result.
+// G = the largest power of two <= 64 / K (K <= 32, so G >= 2).
+__device__ __forceinline__ float group_bound(float v, int K) {
+    const int G = 1 << (31 - __builtin_clz(64 / K));
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    if (G >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+    if (G >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    if (G >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+    if (G >= 32) {
+        const f32x2 t = swap_rows16(v);
+        v = fmaxf(t[0], t[1]);
     }
-    return need > 0 ? -INFINITY : t;
+    if (G >= 64) {
+        const f32x2 t = swap_rows32(v);
+        v = fmaxf(t[0], t[1]);
+    }
+    return -wave_max(-v);
 }
 
 template <int W, int U, bool ALIGNED>
@@ -470,7 +477,13 @@ __global__ void __launch_bounds__(W * 64)
             ml = mn;
             // candidates
             if (first) {
-                T = kth_largest_lane_value(mx, K);
+                // every wave runs the first tile (cols >= K >= 1), so all
+                // reach the barrier
+                const float t0 = group_bound(mx, K);
+                if (lane == 0)
+                    __hip_atomic_fetch_max(&s_thr, ordered_bits(t0), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                __syncthreads();
                 first = false;
             }
             T = fmaxf(T, from_ordered_bits(__hip_atomic_load(&s_thr, __ATOMIC_RELAXED,

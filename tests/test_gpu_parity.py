@@ -295,6 +295,14 @@ def test_topk_special_rows(ons, orc):
     check_topk(ons, orc, x[:, 1:4999], 8, "unaligned cols")
 
 
+def test_topk_many_rows(ons, orc):
+    """Enough rows for the 8-wave-per-row launch, with ties and a ragged K."""
+    x = workloads.normal(1500, 3001, seed=99, scale=3.0)
+    x[::7, 100:140] = 9.5
+    check_topk(ons, orc, x, 8, "many rows")
+    check_topk(ons, orc, x[:, :3000], 13, "many rows aligned K=13")
+
+
 def test_topk_matches_forward(ons):
     """The fused probabilities equal the full softmax at the selected indices."""
     x = workloads.config(5, 0, 16)
