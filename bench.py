@@ -260,11 +260,22 @@ def all_configs(ons, stream):
     _, per = time_launches(lambda: ons.os_softmax_topk(xt, workloads.TOPK_K), 200, 5, stream)
     t = sorted(per)[len(per) // 2]
     nbytes = rows * cols * 4 + rows * workloads.TOPK_K * 8
-    table.append({"workload": 5, "rows": rows, "cols": cols, "dtype": "float32", "K": workloads.TOPK_K,
-                  "algorithmic_bytes": nbytes,
-                  "topk": {"us": round(t * 1e6, 2), "GBs": round(nbytes / t / 1e9, 1),
-                           "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1),
-                           "rows_per_s": round(rows / t, 1)}})
+    entry = {"workload": 5, "rows": rows, "cols": cols, "dtype": "float32", "K": workloads.TOPK_K,
+             "algorithmic_bytes": nbytes,
+             "topk": {"us": round(t * 1e6, 2), "GBs": round(nbytes / t / 1e9, 1),
+                      "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1),
+                      "rows_per_s": round(rows / t, 1)}}
+    # the unfused pipelines of the fusion comparison: softmax written out, then
+    # top-K over the probabilities (online: 2R+1W then 1R; safe: 3R+1W then 1R)
+    yt = torch.empty_like(xt)
+    for name, fwd in (("unfused_online", ons.os_softmax_forward), ("unfused_safe", ons.safe_softmax_forward)):
+        def pipeline(fwd=fwd):
+            fwd(xt, out=yt)
+            ons.os_softmax_topk(yt, workloads.TOPK_K)
+        _, per = time_launches(pipeline, 100, 5, stream)
+        tu = sorted(per)[len(per) // 2]
+        entry[name] = {"us": round(tu * 1e6, 2), "fused_speedup": round(tu / t, 2)}
+    table.append(entry)
     return table
 
 

@@ -67,6 +67,9 @@ extern "C" {
 /* largest K accepted by os_softmax_topk */
 #define OS_TOPK_KMAX 32
 
+/* most workgroups one row may be split over in os_softmax_topk_split */
+#define OS_TOPK_MAX_SPLITS 16
+
 /* largest row length (columns) accepted by every entry point: 2^28 */
 #define OS_MAX_COLS (1LL << 28)
 
@@ -136,10 +139,39 @@ int os_softmax_topk(const float *in, float *probs, int32_t *idx, int64_t rows, i
                     void *stream);
 
 /*
- * Baseline: safe softmax in three streaming passes over the input (maximum,
- * sum of e^{x-m}, normalise and store), as in the paper summary, section 2,
- * and "5.2 Hiện thực và tối ưu CUDA Online Softmax", section 1.1.  It reads
- * every row three times; same arguments and results as os_softmax_forward.
+ * os_softmax_topk with each row split over `splits` workgroups, for batches
+ * too small to occupy the GPU with one workgroup per row (the pages' "several
+ * blocks per row": "5.2 Hiện thực và tối ưu CUDA Online Softmax", section
+ * 7.1).  Each workgroup folds a contiguous slice of the row into a state
+ * (m, d) and a sorted candidate list and writes both to `workspace`; a
+ * second launch on the same stream merges, per row, the slice states with
+ * (+) (paper summary, section 3.3) and the lists, in slice order, so results
+ * are identical to os_softmax_topk's.
+ *   splits      1..OS_TOPK_MAX_SPLITS (1 = os_softmax_topk; workspace unused).
+ *   workspace   device memory of at least os_softmax_topk_workspace_bytes()
+ *               bytes, 256-byte aligned, owned by the caller; no
+ *               initialisation needed.  Calls that may overlap in time
+ *               (different streams) need separate workspaces.
+ *   Other arguments, results and errors as os_softmax_topk; a missing or
+ *   short workspace is OS_EINVAL.
+ */
+int os_softmax_topk_split(const float *in, float *probs, int32_t *idx, int64_t rows, int64_t cols, int K,
+                          int splits, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace os_softmax_topk_split needs (0 for splits == 1), or
+ * OS_EINVAL for bad arguments.  Host only. */
+int64_t os_softmax_topk_workspace_bytes(int64_t rows, int K, int splits);
+
+/* Suggested `splits` for a top-K batch (1 = no split).  Host only. */
+int os_topk_plan(int64_t rows, int64_t cols, int K);
+
+/*
+ * Baseline: safe softmax in three passes over the input in global memory
+ * (maximum, sum of e^{x-m}, normalise and store), as in the paper summary,
+ * section 2, and "5.2 Hiện thực và tối ưu CUDA Online Softmax", section 1.1.
+ * It reads every row three times (re-reads of short rows may hit in cache),
+ * with the same lanes-per-row geometry os_softmax_forward picks; same
+ * arguments and results as os_softmax_forward.
  *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
  */
 int safe_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, int dtype,

@@ -11,7 +11,9 @@ Entry points (same names as the C ABI):
   os_softmax_forward(x, out=None)              y = softmax(x) over the last dim
   os_softmax_forward_tuned(x, lanes_per_row, vecs_per_lane, grid_blocks=0, out=None)
   os_softmax_stats(x) -> (m, d)                per-row normaliser state
-  os_softmax_topk(x, K) -> (probs, idx)        fused softmax + top-K
+  os_softmax_topk(x, K, splits=None) -> (probs, idx)   fused softmax + top-K
+  os_softmax_topk_split(x, K, splits, workspace) -> (probs, idx)
+  os_softmax_topk_workspace_bytes(rows, K, splits), os_topk_plan(rows, cols, K)
   safe_softmax_forward(x, out=None)            three-pass baseline
   os_device_copy(src, dst)                     plain copy (bandwidth reference)
   os_forward_plan(cols, dtype) -> (lanes_per_row, vecs_per_lane)
@@ -31,6 +33,7 @@ __all__ = [
     "OS_F32", "OS_BF16", "OS_TOPK_KMAX", "OnlineSoftmaxError", "LIB_PATH", "lib",
     "os_softmax_forward", "os_softmax_forward_tuned", "os_softmax_stats", "os_softmax_topk",
     "safe_softmax_forward", "os_device_copy", "os_forward_plan", "os_last_error", "os_version",
+    "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan",
 ]
 
 OS_OK, OS_EINVAL, OS_EUNSUPPORTED, OS_ELAUNCH = 0, -1, -2, -3
@@ -78,11 +81,15 @@ def _load() -> ctypes.CDLL:
         "safe_softmax_forward": [vp, vp, i64, i64, i32, vp],
         "os_device_copy": [vp, vp, i64, vp],
         "os_version": [],
+        "os_softmax_topk_split": [vp, vp, vp, i64, i64, i32, i32, vp, i64, vp],
+        "os_topk_plan": [i64, i64, i32],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = i32
+    L.os_softmax_topk_workspace_bytes.argtypes = [i64, i32, i32]
+    L.os_softmax_topk_workspace_bytes.restype = i64
     L.os_last_error.argtypes = []
     L.os_last_error.restype = ctypes.c_char_p
     return L
@@ -183,16 +190,63 @@ def os_softmax_stats(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     return m, d
 
 
-def os_softmax_topk(x: torch.Tensor, K: int) -> tuple[torch.Tensor, torch.Tensor]:
+def os_topk_plan(rows: int, cols: int, K: int) -> int:
+    return lib().os_topk_plan(rows, cols, K)
+
+
+def os_softmax_topk_workspace_bytes(rows: int, K: int, splits: int) -> int:
+    n = lib().os_softmax_topk_workspace_bytes(rows, K, splits)
+    if n < 0:
+        raise OnlineSoftmaxError("os_softmax_topk_workspace_bytes", n, os_last_error())
+    return n
+
+
+# Split top-K workspaces, one per (device, stream) (calls on one stream run
+# in order, so they can share it).
+_TOPK_WS: dict[tuple[int, int], torch.Tensor] = {}
+
+
+def _topk_workspace(x: torch.Tensor, nbytes: int) -> torch.Tensor:
+    key = (x.device.index, _stream(x))
+    ws = _TOPK_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+        _TOPK_WS[key] = ws
+    return ws
+
+
+def _topk_out(x, K):
     rows, cols = _rows_cols(x)
     if x.dtype != torch.float32:
-        raise TypeError("os_softmax_topk takes float32 input")
+        raise TypeError("top-K takes float32 input")
     shape = (*x.shape[:-1], K)
     probs = torch.empty(shape, dtype=torch.float32, device=x.device)
     idx = torch.empty(shape, dtype=torch.int32, device=x.device)
-    _check("os_softmax_topk",
-           lib().os_softmax_topk(x.data_ptr(), probs.data_ptr(), idx.data_ptr(), rows, cols, K, _stream(x)))
+    return rows, cols, probs, idx
+
+
+def os_softmax_topk_split(x: torch.Tensor, K: int, splits: int,
+                          workspace: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    rows, cols, probs, idx = _topk_out(x, K)
+    _check("os_softmax_topk_split",
+           lib().os_softmax_topk_split(x.data_ptr(), probs.data_ptr(), idx.data_ptr(), rows, cols, K, splits,
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream(x)))
     return probs, idx
+
+
+def os_softmax_topk(x: torch.Tensor, K: int, splits: int | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Fused softmax + top-K.  splits=None asks the library's plan; a split
+    launch uses a workspace cached per (device, stream)."""
+    rows, cols, probs, idx = _topk_out(x, K)
+    if splits is None:
+        splits = os_topk_plan(rows, cols, K)
+    if splits == 1:
+        _check("os_softmax_topk",
+               lib().os_softmax_topk(x.data_ptr(), probs.data_ptr(), idx.data_ptr(), rows, cols, K, _stream(x)))
+        return probs, idx
+    ws = _topk_workspace(x, os_softmax_topk_workspace_bytes(rows, K, splits))
+    return os_softmax_topk_split(x, K, splits, ws)
 
 
 def safe_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -73,26 +73,38 @@ int launched(const char* fn) {
 // Register-resident shapes built into the library.
 // ---------------------------------------------------------------------------
 typedef void (*RowKernel)(const void*, void*, float*, float*, int64_t, int);
+typedef void (*SafeKernel)(const void*, void*, int64_t, int);
 
 struct ResidentShape {
     int lpr, vpl;
-    RowKernel fn[2][2];  // [bf16][aligned]
+    RowKernel fn[2][2];     // [bf16][aligned]
+    SafeKernel safe[2][2];  // the three-pass baseline with the same geometry
 };
 
 #define ONORM_RESIDENT(L, V)                                                         \
     {                                                                                \
-        L, V, {                                                                      \
-            {k_resident<false, L, V, false>, k_resident<false, L, V, true>},         \
-            {k_resident<true, L, V, false>, k_resident<true, L, V, true>},           \
+        L, V,                                                                        \
+            {                                                                        \
+                {k_resident<false, L, V, false>, k_resident<false, L, V, true>},     \
+                {k_resident<true, L, V, false>, k_resident<true, L, V, true>},       \
+            },                                                                       \
+        {                                                                            \
+            {k_safe3_rows<false, L, V, false>, k_safe3_rows<false, L, V, true>},     \
+                {k_safe3_rows<true, L, V, false>, k_safe3_rows<true, L, V, true>},   \
         }                                                                            \
     }
 // fp32 only: 16 vectors of bf16 are 128 fp32 values per lane, more than a
 // 1024-thread workgroup's 128-VGPR budget, so bf16 rows this long stream.
 #define ONORM_RESIDENT_F32(L, V)                                                     \
     {                                                                                \
-        L, V, {                                                                      \
-            {k_resident<false, L, V, false>, k_resident<false, L, V, true>},         \
-            {nullptr, nullptr},                                                      \
+        L, V,                                                                        \
+            {                                                                        \
+                {k_resident<false, L, V, false>, k_resident<false, L, V, true>},     \
+                {nullptr, nullptr},                                                  \
+            },                                                                       \
+        {                                                                            \
+            {k_safe3_rows<false, L, V, false>, k_safe3_rows<false, L, V, true>},     \
+                {nullptr, nullptr},                                                  \
         }                                                                            \
     }
 
@@ -172,8 +184,6 @@ RowKernel stream_kernel(int w, int dtype, bool al) {
     if (w == 4) return stream_kernel_w<4>(dtype, al);
     return stream_kernel_w<16>(dtype, al);
 }
-
-typedef void (*SafeKernel)(const void*, void*, int64_t, int);
 
 template <int W>
 SafeKernel safe_kernel_w(int dtype, bool al) {
@@ -291,42 +301,151 @@ int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, 
     if (rc == 1) return ok();
     if (rc != OS_OK) return rc;
     const bool al = vector_ok(in, out, cols, dtype);
-    const int w = stream_waves(cols, dtype);
-    const int block = w * 64;
-    const int grid = grid_for(rows, block, 0);
+    const int bf = dtype == OS_BF16 ? 1 : 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int lpr = 0, vpl = 0;
+    auto_plan(cols, dtype, &lpr, &vpl);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(safe_kernel(w, dtype, al), dim3(grid), dim3(block), 0, static_cast<hipStream_t>(stream), in,
-                       out, rows, static_cast<int>(cols));
+    if (lpr != 0) {
+        // rows that fit the register-resident geometry: same lanes and
+        // vectors as the forward, three passes over global memory
+        const ResidentShape* shape = find_shape(lpr, vpl, dtype);
+        const int block = lpr <= 64 ? 256 : lpr;
+        const int rpb = block / lpr;
+        const int grid = grid_for((rows + rpb - 1) / rpb, block, 0);
+        hipLaunchKernelGGL(shape->safe[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, rows,
+                           static_cast<int>(cols));
+    } else {
+        const int w = stream_waves(cols, dtype);
+        const int block = w * 64;
+        const int grid = grid_for(rows, block, 0);
+        hipLaunchKernelGGL(safe_kernel(w, dtype, al), dim3(grid), dim3(block), 0, st, in, out, rows,
+                           static_cast<int>(cols));
+    }
     return launched(fn);
 }
 
-int os_softmax_topk(const float* in, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K, void* stream) {
-    const char* fn = "os_softmax_topk";
+}  // extern "C"
+
+namespace {
+
+int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Workspace of the split launch: [rows*S] states | [rows*S*K] list entries,
+// each part 256-byte aligned.
+struct TopkWorkspace {
+    int64_t states_off, lists_off, bytes;
+};
+
+TopkWorkspace topk_workspace(int64_t rows, int K, int S) {
+    TopkWorkspace w;
+    w.states_off = 0;
+    w.lists_off = align256(rows * S * static_cast<int64_t>(sizeof(State)));
+    w.bytes = w.lists_off + rows * S * K * static_cast<int64_t>(sizeof(TopkEntry));
+    return w;
+}
+
+int check_topk(const char* fn, const float* in, const float* probs, const int32_t* idx, int64_t rows,
+               int64_t cols, int K) {
     if (rows < 0 || cols < 0) return fail(OS_EINVAL, "%s: rows and cols must be >= 0", fn);
     if (cols > OS_MAX_COLS) return fail(OS_EINVAL, "%s: cols %lld exceeds OS_MAX_COLS", fn, (long long)cols);
     if (K < 1 || K > OS_TOPK_KMAX) return fail(OS_EINVAL, "%s: K=%d outside [1, %d]", fn, K, OS_TOPK_KMAX);
-    if (rows == 0) return ok();
-    if (static_cast<int64_t>(K) > cols)
-        return fail(OS_EINVAL, "%s: K=%d exceeds cols=%lld", fn, K, (long long)cols);
+    if (rows == 0) return 1;
+    if (static_cast<int64_t>(K) > cols) return fail(OS_EINVAL, "%s: K=%d exceeds cols=%lld", fn, K, (long long)cols);
     if (rows > INT64_MAX / cols / 4) return fail(OS_EINVAL, "%s: rows * cols overflows", fn);
     if (in == nullptr || probs == nullptr || idx == nullptr) return fail(OS_EINVAL, "%s: NULL pointer", fn);
     if (!aligned(in, 4) || !aligned(probs, 4) || !aligned(idx, 4))
         return fail(OS_EINVAL, "%s: pointers must be 4-byte aligned", fn);
+    return OS_OK;
+}
+
+typedef void (*TopkKernel)(const float*, float*, int*, int64_t, int, int, int, State*, TopkEntry*);
+
+template <int W>
+TopkKernel topk_kernel(bool al, bool split) {
+    if (split) return al ? k_topk<W, 4, true, true> : k_topk<W, 4, false, true>;
+    return al ? k_topk<W, 4, true, false> : k_topk<W, 4, false, false>;
+}
+
+int launch_topk(const char* fn, const float* in, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K,
+                int S, void* workspace, void* stream) {
     const bool al = aligned(in, 16) && (cols % 4) == 0;
-    // A few hundred rows: 16 waves per row keep every CU busy on its row.
-    // Many rows: 8 waves per row, two rows per CU (measured faster).
-    const bool wide = rows < 1024;
+    const int64_t units = rows * S;
+    // A few hundred workgroups: 16 waves each keep every CU busy.  Many:
+    // 8 waves each, two per CU (measured faster).
+    const bool wide = units < 1024;
     const int block = wide ? 1024 : 512;
-    const int grid = grid_for(rows, block, 0);
+    const int grid = grid_for(units, block, 0);
+    const TopkKernel k = wide ? topk_kernel<16>(al, S > 1) : topk_kernel<8>(al, S > 1);
+    State* states = nullptr;
+    TopkEntry* lists = nullptr;
+    if (S > 1) {
+        const TopkWorkspace w = topk_workspace(rows, K, S);
+        char* base = static_cast<char*>(workspace);
+        states = reinterpret_cast<State*>(base + w.states_off);
+        lists = reinterpret_cast<TopkEntry*>(base + w.lists_off);
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    void (*k)(const float*, float*, int*, int64_t, int, int);
-    if (wide)
-        k = al ? k_topk<16, 4, true> : k_topk<16, 4, false>;
-    else
-        k = al ? k_topk<8, 4, true> : k_topk<8, 4, false>;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, st, in, probs, idx, rows, static_cast<int>(cols), K);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, st, in, probs, idx, rows, static_cast<int>(cols), K, S,
+                       states, lists);
+    if (S > 1) {
+        const int rc = launched(fn);
+        if (rc != OS_OK) return rc;
+        const int mgrid = grid_for((rows + 3) / 4, 256, 0);
+        hipLaunchKernelGGL(k_topk_merge, dim3(mgrid), dim3(256), 0, st, probs, idx, rows, K, S, states, lists);
+    }
     return launched(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int os_softmax_topk(const float* in, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K, void* stream) {
+    const char* fn = "os_softmax_topk";
+    const int rc = check_topk(fn, in, probs, idx, rows, cols, K);
+    if (rc == 1) return ok();
+    if (rc != OS_OK) return rc;
+    return launch_topk(fn, in, probs, idx, rows, cols, K, 1, nullptr, stream);
+}
+
+int64_t os_softmax_topk_workspace_bytes(int64_t rows, int K, int splits) {
+    if (rows < 0 || K < 1 || K > OS_TOPK_KMAX || splits < 1 || splits > OS_TOPK_MAX_SPLITS) {
+        fail(OS_EINVAL, "os_softmax_topk_workspace_bytes: bad rows, K or splits");
+        return OS_EINVAL;
+    }
+    ok();
+    return splits == 1 ? 0 : topk_workspace(rows, K, splits).bytes;
+}
+
+int os_topk_plan(int64_t rows, int64_t cols, int K) {
+    if (rows <= 0 || cols <= 0 || K < 1) return 1;
+    // Splitting pays only for batches far smaller than the CU count (measured
+    // on MI355X: 16 rows x 128256 best at 8 slices, 64 rows at 4, 256 rows
+    // unsplit): at most 256 workgroups and 8 slices, each >= 8K columns.
+    int S = 1;
+    while (S < 8 && rows * S * 2 <= 256 && cols / (S * 2) >= 8192) S *= 2;
+    return S;
+}
+
+int os_softmax_topk_split(const float* in, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K, int splits,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+    const char* fn = "os_softmax_topk_split";
+    if (splits < 1 || splits > OS_TOPK_MAX_SPLITS)
+        return fail(OS_EINVAL, "%s: splits=%d outside [1, %d]", fn, splits, OS_TOPK_MAX_SPLITS);
+    const int rc = check_topk(fn, in, probs, idx, rows, cols, K);
+    if (rc == 1) return ok();
+    if (rc != OS_OK) return rc;
+    if (splits > 1) {
+        if (workspace == nullptr) return fail(OS_EINVAL, "%s: workspace is NULL", fn);
+        if (!aligned(workspace, 256)) return fail(OS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+        const int64_t need = topk_workspace(rows, K, splits).bytes;
+        if (workspace_bytes < need)
+            return fail(OS_EINVAL, "%s: workspace has %lld bytes, needs %lld", fn, (long long)workspace_bytes,
+                        (long long)need);
+    }
+    return launch_topk(fn, in, probs, idx, rows, cols, K, splits, workspace, stream);
 }
 
 int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {

@@ -333,6 +333,85 @@ __global__ void __launch_bounds__(W * 64)
 }
 
 // ---------------------------------------------------------------------------
+// Baseline with the register-resident geometry: safe softmax in three passes
+// over global memory (maximum; sum of e^{x - m}; normalise and store), LPR
+// lanes per row and VPL vectors per lane exactly as k_resident, but every
+// pass reloads the row's slots instead of keeping them in registers.  Pass 1
+// and 2 use plain loads, so re-reads of short rows can hit in cache, which is
+// the regime the pages' benchmark describes for short vectors.
+// ---------------------------------------------------------------------------
+template <bool BF16, int LPR, int VPL, bool ALIGNED>
+__global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
+    k_safe3_rows(const void* in, void* out, int64_t rows, int cols) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    constexpr int BLOCK = LPR <= 64 ? 256 : LPR;
+    constexpr int RPB = BLOCK / LPR;
+    constexpr int W = LPR > 64 ? LPR / 64 : 1;
+    constexpr int GROUP = LPR < 64 ? LPR : 64;
+    __shared__ float lds_m[2][W];
+    __shared__ float lds_d[2][W];
+
+    const int tid = threadIdx.x;
+    const int j = tid % LPR;
+    const int g = tid / LPR;
+    const int nvec = vec_count<BF16, ALIGNED>(cols);
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    int par = 0;
+
+    for (int64_t rb = blockIdx.x; rb * RPB < rows; rb += gridDim.x) {
+        const int64_t row0 = rb * RPB;
+        const int64_t nrows = (rows - row0) < RPB ? (rows - row0) : RPB;
+        const bool live = g < nrows;
+        const uint32_t row_off = static_cast<uint32_t>(g) * row_bytes;
+        const Buf bin(static_cast<const char*>(in) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
+        float x[VPL][VEC];
+
+        // pass 1: maximum
+        load_slots<BF16, VPL, ALIGNED, false>(bin, row_off, j, LPR, nvec, cols, live, x);
+        float m = kFloor;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[v][k]);
+        m = group_max<GROUP>(m);
+        if constexpr (W > 1) {
+            if ((tid & (kWave - 1)) == 0) lds_m[par][tid / kWave] = m;
+            __syncthreads();
+            m = lds_m[par][0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) m = fmaxf(m, lds_m[par][w]);
+        }
+        // pass 2: sum of e^{x - m}
+        load_slots<BF16, VPL, ALIGNED, false>(bin, row_off, j, LPR, nvec, cols, live, x);
+        float d = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) d += exp_e(x[v][k] - m);
+        d = group_sum<GROUP>(d);
+        if constexpr (W > 1) {
+            if ((tid & (kWave - 1)) == 0) lds_d[par][tid / kWave] = d;
+            __syncthreads();
+            d = lds_d[par][0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) d += lds_d[par][w];
+            par ^= 1;
+        }
+        // pass 3: normalise and store
+        load_slots<BF16, VPL, ALIGNED, true>(bin, row_off, j, LPR, nvec, cols, live, x);
+        const float inv_d = rcp(d);
+        const Buf bout(static_cast<char*>(out) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) x[v][k] = exp_e(x[v][k] - m) * inv_d;
+            store_slot<BF16, ALIGNED>(bout, row_off, v * LPR + j, nvec, cols, live, x[v]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fused softmax + top-K (paper summary, section 4), one read of the input.
 //
 // One W-wave workgroup per row.  Every lane folds (m, d) over its slots as in
@@ -406,9 +485,66 @@ __device__ __forceinline__ float group_bound(float v, int K) {
     return -wave_max(-v);
 }
 
-template <int W, int U, bool ALIGNED>
+// One (value, index) entry of a segment's partial top-K list.
+struct TopkEntry {
+    float v;
+    int i;
+};
+
+// K rounds of a 16-lane argmax over up to 16 sorted lists whose heads sit in
+// lanes 0..n-1 (list `lane` read through get(lane, pos)); lane k ends with
+// the k-th best entry.  Lanes >= n hold the sentinel (-inf, INT_MAX), which
+// ranks after every real entry.
+template <typename Get>
+__device__ __forceinline__ void merge_sorted_lists(int n, int K, int lane, Get get, float& out_v, int& out_i) {
+    int pos = 0;
+    float hv = -INFINITY;
+    int hi = 0x7FFFFFFF;
+    if (lane < n) get(lane, 0, hv, hi);
+    out_v = -INFINITY;
+    out_i = 0x7FFFFFFF;
+    for (int k = 0; k < K; ++k) {
+        float bv = hv;
+        int bi = hi;
+        float ov = dpp<kDppXor1>(bv);
+        int oi = dpp<kDppXor1>(bi);
+        if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        ov = dpp<kDppXor2>(bv);
+        oi = dpp<kDppXor2>(bi);
+        if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        ov = dpp<kDppHalfMirror>(bv);
+        oi = dpp<kDppHalfMirror>(bi);
+        if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        ov = dpp<kDppMirror>(bv);
+        oi = dpp<kDppMirror>(bi);
+        if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        bv = readlane(bv, 0);
+        bi = readlane(bi, 0);
+        if (lane == k) {
+            out_v = bv;
+            out_i = bi;
+        }
+        if (lane < n && hi == bi) {
+            ++pos;
+            if (pos < K) {
+                get(lane, pos, hv, hi);
+            } else {
+                hv = -INFINITY;
+                hi = 0x7FFFFFFF;
+            }
+        }
+    }
+}
+
+// SPLIT = false: one workgroup per row, results written directly.
+// SPLIT = true: S workgroups per row, each over a contiguous slice of the
+// row's vector slots, each writing its state (m, d) and its sorted K-list to
+// the workspace; k_topk_merge (the next launch on the stream, so every
+// partial is visible) combines them.
+template <int W, int U, bool ALIGNED, bool SPLIT>
 __global__ void __launch_bounds__(W * 64)
-    k_topk(const float* in, float* probs, int* idx, int64_t rows, int cols, int K) {
+    k_topk(const float* in, float* probs, int* idx, int64_t rows, int cols, int K, int S, State* ws_state,
+           TopkEntry* ws_list) {
     static_assert(W <= 16, "the final selection runs inside one 16-lane DPP row");
     constexpr int BLOCK = W * 64;
     constexpr int VEC = 4;
@@ -423,9 +559,15 @@ __global__ void __launch_bounds__(W * 64)
     const int w = tid / kWave;
     const uint64_t kmask = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
     const int nvec = vec_count<false, ALIGNED>(cols);
+    const int seg_vec = SPLIT ? (nvec + S - 1) / S : nvec;
+    const int64_t units = SPLIT ? rows * S : rows;
     const uint32_t row_bytes = static_cast<uint32_t>(cols) * 4u;
 
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t row = SPLIT ? unit / S : unit;
+        const int seg = SPLIT ? static_cast<int>(unit - row * S) : 0;
+        const int v0 = seg * seg_vec;
+        const int v1 = (v0 + seg_vec < nvec) ? v0 + seg_vec : nvec;
         const Buf bin(in + row * static_cast<int64_t>(cols), row_bytes);
         if (tid == 0) s_thr = ordered_bits(-INFINITY);
         __syncthreads();
@@ -438,17 +580,17 @@ __global__ void __launch_bounds__(W * 64)
         // Software pipeline: the raw loads of the next tile are issued before
         // the current tile is folded, so they are in flight during the
         // compute.  Loads past the end of the row touch no memory (buffer
-        // range check) and are masked to -inf.
+        // range check); slots past the segment are masked to -inf.
         u32x4 raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(u * BLOCK + tid) * 16u);
-        for (int base = 0; base < nvec; base += STEP) {
+        for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(v0 + u * BLOCK + tid) * 16u);
+        for (int base = v0; base < v1; base += STEP) {
             float x[U][VEC];
             if constexpr (ALIGNED) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     Elt<false>::unpack(raw[u], x[u]);
-                    const bool ok = base + u * BLOCK + tid < nvec;
+                    const bool ok = base + u * BLOCK + tid < v1;
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) x[u][k] = ok ? x[u][k] : -INFINITY;
                 }
@@ -458,7 +600,10 @@ __global__ void __launch_bounds__(W * 64)
                 __builtin_amdgcn_sched_barrier(0);
             } else {
 #pragma unroll
-                for (int u = 0; u < U; ++u) load_slot<false, false, true>(bin, 0u, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                for (int u = 0; u < U; ++u) {
+                    const int slot = base + u * BLOCK + tid;
+                    load_slot<false, false, true>(bin, 0u, slot, v1, cols, slot < v1, x[u]);
+                }
             }
 
             float mx = -INFINITY;
@@ -477,8 +622,8 @@ __global__ void __launch_bounds__(W * 64)
             ml = mn;
             // candidates
             if (first) {
-                // every wave runs the first tile (cols >= K >= 1), so all
-                // reach the barrier
+                // every wave of the workgroup runs the segment's first tile
+                // (v0 < v1 is uniform), so all reach the barrier
                 const float t0 = group_bound(mx, K);
                 if (lane == 0)
                     __hip_atomic_fetch_max(&s_thr, ordered_bits(t0), __ATOMIC_RELAXED,
@@ -495,7 +640,7 @@ __global__ void __launch_bounds__(W * 64)
                     const int wave_slot0 = base + u * BLOCK + w * kWave;
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) {
-                        const bool hit = (slot * VEC + k < cols) && (x[u][k] >= T);
+                        const bool hit = slot < v1 && (slot * VEC + k < cols) && (x[u][k] >= T);
                         uint64_t mask = __ballot(hit);
                         while (mask != 0) {
                             const int l = __builtin_ctzll(mask);
@@ -516,58 +661,61 @@ __global__ void __launch_bounds__(W * 64)
             }
         }
 
-        const State s = group_merge<64>(State{ml, dl});
+        const State st = group_merge<64>(State{ml, dl});
         if (lane < K) {
             s_val[w][lane] = L;
             s_idx[w][lane] = I;
         }
-        if (lane == 0) s_md[w] = s;
+        if (lane == 0) s_md[w] = st;
         __syncthreads();
 
         if (w == 0) {
             State t = s_md[0];
 #pragma unroll
             for (int ww = 1; ww < W; ++ww) t = oplus(t, s_md[ww]);
-            const float inv_d = rcp(t.d);
-            int pos = 0;
-            float hv = (lane < W) ? s_val[lane][0] : -INFINITY;
-            int hi = (lane < W) ? s_idx[lane][0] : 0x7FFFFFFF;
-            float out_v = -INFINITY;
-            int out_i = 0;
-            for (int k = 0; k < K; ++k) {
-                float bv = hv;
-                int bi = hi;
-                {
-                    float ov = dpp<kDppXor1>(bv);
-                    int oi = dpp<kDppXor1>(bi);
-                    if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-                    ov = dpp<kDppXor2>(bv);
-                    oi = dpp<kDppXor2>(bi);
-                    if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-                    ov = dpp<kDppHalfMirror>(bv);
-                    oi = dpp<kDppHalfMirror>(bi);
-                    if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-                    ov = dpp<kDppMirror>(bv);
-                    oi = dpp<kDppMirror>(bi);
-                    if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+            float out_v;
+            int out_i;
+            merge_sorted_lists(
+                W, K, lane, [&](int l, int p, float& v, int& i) { v = s_val[l][p]; i = s_idx[l][p]; }, out_v,
+                out_i);
+            if constexpr (!SPLIT) {
+                if (lane < K) {
+                    probs[row * K + lane] = exp_e(out_v - t.m) * rcp(t.d);
+                    idx[row * K + lane] = out_i;
                 }
-                bv = readlane(bv, 0);
-                bi = readlane(bi, 0);
-                if (lane == k) {
-                    out_v = bv;
-                    out_i = bi;
-                }
-                if (lane < W && hi == bi) {
-                    ++pos;
-                    hv = (pos < K) ? s_val[lane][pos] : -INFINITY;
-                    hi = (pos < K) ? s_idx[lane][pos] : 0x7FFFFFFF;
-                }
-            }
-            if (lane < K) {
-                probs[row * K + lane] = exp_e(out_v - t.m) * inv_d;
-                idx[row * K + lane] = out_i;
+            } else {
+                if (lane < K) ws_list[unit * K + lane] = TopkEntry{out_v, out_i};
+                if (lane == 0) ws_state[unit] = t;
             }
         }
+    }
+}
+
+// Second launch of the split top-K: one wavefront per row folds the S slice
+// states with (+) in slice order and merges the S sorted lists (16-lane
+// argmax rounds), then writes the K probabilities and indices.
+__global__ void __launch_bounds__(256)
+    k_topk_merge(float* probs, int* idx, int64_t rows, int K, int S, const State* ws_state,
+                 const TopkEntry* ws_list) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+    if (row >= rows) return;  // whole wavefronts leave together
+    const int64_t u0 = row * S;
+    State r = ws_state[u0];
+    for (int q = 1; q < S; ++q) r = oplus(r, ws_state[u0 + q]);
+    float out_v;
+    int out_i;
+    merge_sorted_lists(
+        S, K, lane,
+        [&](int l, int p, float& v, int& i) {
+            const TopkEntry e = ws_list[(u0 + l) * K + p];
+            v = e.v;
+            i = e.i;
+        },
+        out_v, out_i);
+    if (lane < K) {
+        probs[row * K + lane] = exp_e(out_v - r.m) * rcp(r.d);
+        idx[row * K + lane] = out_i;
     }
 }
 

@@ -118,6 +118,27 @@ def test_topk_validation(L, args, code):
     assert L.os_softmax_topk(*args, None) == code
 
 
+def test_topk_split_validation(L, ons):
+    assert ons.os_softmax_topk_workspace_bytes(10, 8, 1) == 0
+    need = ons.os_softmax_topk_workspace_bytes(10, 8, 4)
+    assert need >= 10 * 4 * 8 + 10 * 4 * 8 * 8
+    with pytest.raises(ons.OnlineSoftmaxError):
+        ons.os_softmax_topk_workspace_bytes(10, 8, 17)
+    f = L.os_softmax_topk_split
+    assert f(FAKE, FAKE, FAKE, 10, 1000, 8, 0, FAKE, need, None) == EINVAL      # splits < 1
+    assert f(FAKE, FAKE, FAKE, 10, 1000, 8, 17, FAKE, need, None) == EINVAL     # splits > 16
+    assert f(FAKE, FAKE, FAKE, 10, 1000, 8, 4, None, need, None) == EINVAL      # no workspace
+    assert f(FAKE, FAKE, FAKE, 10, 1000, 8, 4, FAKE, need - 1, None) == EINVAL  # short workspace
+    assert f(FAKE, FAKE, FAKE, 10, 1000, 8, 4, FAKE + 16, need, None) == EINVAL  # misaligned workspace
+    assert f(FAKE, FAKE, FAKE, 10, 1000, 9, 4, FAKE, need, None) == EINVAL      # K changed: short
+    assert f(None, None, None, 0, 1000, 8, 4, None, 0, None) == 0               # empty
+    assert ons.os_topk_plan(256, 128256, 8) == 1
+    assert ons.os_topk_plan(16, 128256, 8) == 8
+    assert ons.os_topk_plan(64, 128256, 8) == 4
+    assert ons.os_topk_plan(4096, 128256, 8) == 1
+    assert ons.os_topk_plan(16, 1000, 8) == 1
+
+
 def test_copy_validation(L):
     assert L.os_device_copy(FAKE, FAKE + 4096, 20, None) == EINVAL      # not a multiple of 16
     assert L.os_device_copy(FAKE + 4, FAKE + 4096, 32, None) == EINVAL  # misaligned

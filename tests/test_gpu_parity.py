@@ -111,7 +111,9 @@ def test_auto_dispatch_edge_columns(ons, orc, bf16):
         say(f"auto bf16={bf16} rows={rows} cols={cols}")
         x32 = workloads.normal(rows, cols, seed=1000 + cols, scale=3.0)
         x = bf16_bits(x32) if bf16 else x32
-        assert_parity(run_forward(ons, x), orc.softmax(x), bf16, f"auto cols={cols}")
+        ref = orc.softmax(x)
+        assert_parity(run_forward(ons, x), ref, bf16, f"auto cols={cols}")
+        assert_parity(run_forward(ons, x, safe=True), ref, bf16, f"safe cols={cols}")
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
@@ -252,10 +254,10 @@ def test_stats_invariants(ons, orc):
 
 # -- fused softmax + top-K ---------------------------------------------------------
 
-def check_topk(ons, orc, x: np.ndarray, K: int, what: str):
-    say(f"topk {what} rows={x.shape[0]} cols={x.shape[1]} K={K}")
+def check_topk(ons, orc, x: np.ndarray, K: int, what: str, splits=None):
+    say(f"topk {what} rows={x.shape[0]} cols={x.shape[1]} K={K} splits={splits}")
     xd = to_device(np.ascontiguousarray(x))
-    p, i = ons.os_softmax_topk(xd, K)
+    p, i = ons.os_softmax_topk(xd, K, splits=splits)
     torch.cuda.synchronize()
     pr, ir = orc.topk(x, K, threads=8)
     i = to_host(i)
@@ -301,6 +303,40 @@ def test_topk_many_rows(ons, orc):
     x[::7, 100:140] = 9.5
     check_topk(ons, orc, x, 8, "many rows")
     check_topk(ons, orc, x[:, :3000], 13, "many rows aligned K=13")
+
+
+@pytest.mark.parametrize("splits", [2, 3, 4, 16])
+def test_topk_split_rows(ons, orc, splits):
+    """Rows split over several workgroups: empty and ragged slices, ties across
+    slices, unaligned rows, both launch widths."""
+    rng = np.random.Generator(np.random.PCG64(splits))
+    x = workloads.normal(40, 20000, seed=7 + splits, scale=3.0)
+    x[3, :] = 2.0
+    x[4, [5, 9000, 19999]] = 30.0
+    x[5, ::2] = -np.inf
+    check_topk(ons, orc, x, 8, f"split {splits}", splits=splits)
+    check_topk(ons, orc, x[:, 1:19998], 17, f"split {splits} unaligned", splits=splits)
+    xi = rng.integers(-3, 4, size=(9, 100)).astype(np.float32)
+    check_topk(ons, orc, xi, 8, f"split {splits} short rows", splits=splits)
+    xm = workloads.normal(1100, 3000, seed=3, scale=3.0)
+    check_topk(ons, orc, xm, 8, f"split {splits} many rows", splits=splits)
+    xl = workloads.normal(12, 70001, seed=11, scale=3.0)  # slices span several tiles
+    xl[2, [0, 35000, 70000]] = 25.0
+    check_topk(ons, orc, xl, 8, f"split {splits} long rows", splits=splits)
+
+
+def test_topk_split_reuses_workspace(ons):
+    """Back-to-back split calls on one (uninitialised) workspace give identical results."""
+    x = to_device(workloads.config(5, 0, 64))
+    say("topk split reuse")
+    ws = torch.full((ons.os_softmax_topk_workspace_bytes(64, 8, 4),), 0xAB, dtype=torch.uint8, device="cuda")
+    a = ons.os_softmax_topk_split(x, 8, 4, ws)
+    b = ons.os_softmax_topk_split(x, 8, 4, ws)
+    c = ons.os_softmax_topk(x, 8, splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[1], c[1])
+    assert torch.equal(a[0], b[0])
+    assert float((a[0] - c[0]).abs().max()) <= 1e-6
 
 
 def test_topk_matches_forward(ons):
@@ -357,4 +393,5 @@ def test_config4_full(ons, orc):
 
 def test_config5_topk_full(ons, orc):
     x = workloads.config(5)
-    check_topk(ons, orc, x, workloads.TOPK_K, "config5")
+    check_topk(ons, orc, x, workloads.TOPK_K, "config5")  # the benchmark's launch (planned split)
+    check_topk(ons, orc, x, workloads.TOPK_K, "config5 one workgroup per row", splits=1)
