@@ -66,6 +66,32 @@ def load_traffic(launch_bytes_alg: float):
     return fetch + write, None
 
 
+def time_graph(fn, steps: int, warmup: int, stream):
+    """Capture `steps` calls of fn() in one HIP graph and time a single replay.
+
+    Returns (wall seconds of the replay, average seconds per launch from HIP
+    events recorded on the stream around the replay)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            fn()
+    graph.replay()  # first replay uploads the graph
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) * 1e-3 / steps
+
+
 def time_launches(fn, steps: int, warmup: int, stream):
     """Run fn() warmup+steps times back to back; HIP events around each timed launch."""
     import torch
@@ -117,6 +143,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as individual launches instead of one HIP graph replay")
     ap.add_argument("--no-compare", action="store_true", help="skip the comparison legs")
     ap.add_argument("--all-configs", metavar="FILE", default=None,
                     help="also time every workload (forward, three-pass baseline, copy; top-K for the "
@@ -143,8 +171,15 @@ def main(argv=None) -> int:
     y = torch.empty_like(x)
     bytes_alg = rows * cols * (4 + 4)  # one read of the input, one write of the output
 
-    wall, per = time_launches(lambda: ons.os_softmax_forward(x, out=y), args.steps, args.warmup, stream)
-    avg = sum(per) / len(per)
+    step = lambda: ons.os_softmax_forward(x, out=y)  # noqa: E731
+    # per-launch kernel time of eager launches (HIP events around each launch)
+    _, per = time_launches(step, args.steps, args.warmup, stream)
+    eager_us = sorted(per)[len(per) // 2] * 1e6
+    if args.eager:
+        wall, per = time_launches(step, args.steps, args.warmup, stream)
+        avg = sum(per) / len(per)
+    else:
+        wall, avg = time_graph(step, args.steps, args.warmup, stream)
     value = bytes_alg * args.steps / wall / 1e9
     achieved = bytes_alg / avg / 1e9
     traffic, traffic_note = load_traffic(bytes_alg)
@@ -179,6 +214,10 @@ def main(argv=None) -> int:
             "kernel_us": round(avg * 1e6, 2),
             "algorithmic_bytes": bytes_alg,
         },
+        "timing": ("K steps as individual launches, HIP events around each" if args.eager else
+                   "K steps captured in one HIP graph, one replay timed; HIP events around the replay "
+                   "give the average launch duration"),
+        "kernel_us_eager_median": round(eager_us, 2),
     }
     if traffic_note:
         out["roofline"]["traffic_note"] = traffic_note

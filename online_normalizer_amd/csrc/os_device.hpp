@@ -88,25 +88,6 @@ __device__ __forceinline__ f32x2 swap_rows32(float v) {
     return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
-// Merge of the states of an aligned group of LANES lanes (1..64); every lane
-// of the group ends with the same bits.
-template <int LANES>
-__device__ __forceinline__ State group_oplus(State s) {
-    if constexpr (LANES >= 2) s = oplus(s, State{dpp<kDppXor1>(s.m), dpp<kDppXor1>(s.d)});
-    if constexpr (LANES >= 4) s = oplus(s, State{dpp<kDppXor2>(s.m), dpp<kDppXor2>(s.d)});
-    if constexpr (LANES >= 8) s = oplus(s, State{dpp<kDppHalfMirror>(s.m), dpp<kDppHalfMirror>(s.d)});
-    if constexpr (LANES >= 16) s = oplus(s, State{dpp<kDppMirror>(s.m), dpp<kDppMirror>(s.d)});
-    if constexpr (LANES >= 32) {
-        const f32x2 m = swap_rows16(s.m), d = swap_rows16(s.d);
-        s = oplus(State{m[0], d[0]}, State{m[1], d[1]});
-    }
-    if constexpr (LANES >= 64) {
-        const f32x2 m = swap_rows32(s.m), d = swap_rows32(s.d);
-        s = oplus(State{m[0], d[0]}, State{m[1], d[1]});
-    }
-    return s;
-}
-
 // Maximum / sum over an aligned group of G lanes (1..64), same bits in every lane.
 template <int G>
 __device__ __forceinline__ float group_max(float v) {

@@ -231,6 +231,40 @@ def test_deterministic(ons):
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+def test_graph_replays_match_eager(ons):
+    """The forward, the baseline and the top-K captured in a HIP graph: every
+    replay, with eager work and synchronisations between replays, equals the
+    eager result bit for bit."""
+    x = to_device(workloads.config(2, 0, 512))
+    xt = to_device(workloads.config(5, 0, 8))
+    say("graph capture")
+    y_ref = ons.os_softmax_forward(x)
+    s_ref = ons.safe_softmax_forward(x)
+    p_ref, i_ref = ons.os_softmax_topk(xt, 8)
+    torch.cuda.synchronize()
+    y = torch.empty_like(x)
+    s3 = torch.empty_like(x)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ons.os_softmax_forward(x, out=y)
+        ons.safe_softmax_forward(x, out=s3)
+        p, i = ons.os_softmax_topk(xt, 8)
+    for rep in range(4):
+        y.zero_()
+        s3.zero_()
+        p.zero_()
+        i.zero_()
+        junk = ons.os_softmax_forward(torch.randn(64, 1000, device="cuda"))  # eager work between replays
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), rep
+        assert torch.equal(s3.view(torch.int32), s_ref.view(torch.int32)), rep
+        assert torch.equal(p, p_ref) and torch.equal(i, i_ref), rep
+        del junk
+
+
 def test_stats_invariants(ons, orc):
     """1 <= d <= N (up to fp32 rounding), m is the exact row maximum, d matches the oracle."""
     for n in (1, 2, 4):
