@@ -421,9 +421,13 @@ int64_t os_softmax_topk_workspace_bytes(int64_t rows, int K, int splits) {
 
 int os_topk_plan(int64_t rows, int64_t cols, int K) {
     if (rows <= 0 || cols <= 0 || K < 1) return 1;
-    // Splitting pays only for batches far smaller than the CU count (measured
-    // on MI355X: 16 rows x 128256 best at 8 slices, 64 rows at 4, 256 rows
-    // unsplit): at most 256 workgroups and 8 slices, each >= 8K columns.
+    // Splitting pays only for batches far smaller than the CU count, and only
+    // for rows long enough that streaming one on a single CU outlasts the
+    // second (merge) launch (measured on MI355X: 16 rows x 128256 best at 8
+    // slices, 64 rows at 4, 256 rows unsplit; 64 rows x 32000 unsplit): at
+    // most 256 workgroups and 8 slices, rows of >= 64K columns, slices of
+    // >= 8K columns.
+    if (cols < 65536) return 1;
     int S = 1;
     while (S < 8 && rows * S * 2 <= 256 && cols / (S * 2) >= 8192) S *= 2;
     return S;

@@ -420,9 +420,9 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
 // rank k) under the total order (value desc, index asc).  Most elements are
 // rejected by a compare with a wave-uniform threshold T, a lower bound on the
 // row's K-th largest value:
-//   - first tile: the smallest of >= K group maxima of the lane maxima (so at
-//     least K elements are that large), the largest such bound over the
-//     workgroup's waves (LDS atomic max, one barrier), before any insert;
+//   - first tile: the workgroup's tile is cut into 64 disjoint parts of W
+//     lanes; the K-th largest of the 64 part maxima is a tile element with
+//     at least K elements at or above it (one barrier, before any insert);
 //   - then: the K-th entry of the wave's own list, and the largest K-th entry
 //     published by any wave of the workgroup (an LDS atomic max).
 // Survivors (x >= T, so ties at T are kept) are inserted one at a time:
@@ -441,48 +441,56 @@ __device__ __forceinline__ float from_ordered_bits(int i) {
 }
 
 // (a_v, a_i) ranks ahead of (b_v, b_i)
+// (bitwise, so it compiles to compares and mask logic, not branches)
 __device__ __forceinline__ bool ahead_of(float av, int ai, float bv, int bi) {
-    return (av > bv) || (av == bv && ai < bi);
+    return (av > bv) | ((av == bv) & (ai < bi));
 }
 
 // Insert the wave-uniform pair (v, i) into the lane-distributed sorted list.
 __device__ __forceinline__ void list_insert(float& L, int& I, float v, int i, int K, int lane,
                                             uint64_t kmask) {
-    const bool ahead = ahead_of(L, I, v, i);
-    const int p = __popcll(__ballot(ahead) & kmask);
+    const int p = __popcll(__ballot(ahead_of(L, I, v, i)) & kmask);
     if (p < K) {
         const float Ls = dpp<kDppWaveShr1>(L);
         const int Is = dpp<kDppWaveShr1>(I);
-        if (lane > p) {
-            L = Ls;
-            I = Is;
-        } else if (lane == p) {
-            L = v;
-            I = i;
-        }
+        const bool shift = lane > p, put = lane == p;
+        L = shift ? Ls : (put ? v : L);
+        I = shift ? Is : (put ? i : I);
     }
 }
 
-// A lower bound on the K-th largest element of a wave's tile from one value
-// per lane (its tile maximum): split the wave into G-lane groups with
-// 64 / G >= K, take each group's maximum (an element of the tile) and return
-// the smallest of them.  At least K distinct elements are >= the result.
-// G = the largest power of two <= 64 / K (K <= 32, so G >= 2).
-__device__ __forceinline__ float group_bound(float v, int K) {
-    const int G = 1 << (31 - __builtin_clz(64 / K));
-    v = fmaxf(v, dpp<kDppXor1>(v));
-    if (G >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
-    if (G >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
-    if (G >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-    if (G >= 32) {
-        const f32x2 t = swap_rows16(v);
-        v = fmaxf(t[0], t[1]);
+// A lower bound on the K-th largest element of a W-wave workgroup's tile,
+// from each lane's tile maximum mx: the tile is cut into 64 disjoint parts of
+// W lanes (64 / W parts per wave), each part's maximum is one of its elements,
+// so the K-th largest of the 64 part maxima (K <= 64) has at least K distinct
+// tile elements at or above it.  Ranks are taken under (value desc, part asc),
+// a permutation, so exactly one part has rank K - 1; wave w counts, for every
+// part, how many of its own 64 / W parts rank ahead, and the counts are summed
+// in s_rank (zeroed by the caller before a barrier that precedes this call).
+// A NaN maximum (a part of NaNs only) counts as -inf: NaN is never a
+// candidate.  Contains two workgroup barriers: every wave must call it.
+template <int W>
+__device__ __forceinline__ float tile_bound(float mx, int K, int w, int lane, float* s_sub, int* s_rank) {
+    constexpr int J = 64 / W;
+    float g = (mx == mx) ? mx : -INFINITY;
+    if constexpr (W >= 2) g = fmaxf(g, dpp<kDppXor1>(g));
+    if constexpr (W >= 4) g = fmaxf(g, dpp<kDppXor2>(g));
+    if constexpr (W >= 8) g = fmaxf(g, dpp<kDppHalfMirror>(g));
+    if constexpr (W >= 16) g = fmaxf(g, dpp<kDppMirror>(g));
+    if ((lane & (W - 1)) == 0) s_sub[w * J + lane / W] = g;
+    __syncthreads();
+    const float a = s_sub[lane];
+    int r = 0;
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+        const int j = w * J + jj;
+        const float b = s_sub[j];
+        r += static_cast<int>((b > a) | ((b == a) & (j < lane)));
     }
-    if (G >= 64) {
-        const f32x2 t = swap_rows32(v);
-        v = fmaxf(t[0], t[1]);
-    }
-    return -wave_max(-v);
+    if (r != 0) __hip_atomic_fetch_add(&s_rank[lane], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();
+    const int rank = __hip_atomic_load(&s_rank[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return readlane(a, __builtin_ctzll(__ballot(rank == K - 1)));
 }
 
 // One (value, index) entry of a segment's partial top-K list.
@@ -494,13 +502,17 @@ struct TopkEntry {
 // K rounds of a 16-lane argmax over up to 16 sorted lists whose heads sit in
 // lanes 0..n-1 (list `lane` read through get(lane, pos)); lane k ends with
 // the k-th best entry.  Lanes >= n hold the sentinel (-inf, INT_MAX), which
-// ranks after every real entry.
+// ranks after every real entry.  Each list lane also holds the entry after
+// its head, read one round early, so a round never waits on get().
 template <typename Get>
 __device__ __forceinline__ void merge_sorted_lists(int n, int K, int lane, Get get, float& out_v, int& out_i) {
     int pos = 0;
-    float hv = -INFINITY;
-    int hi = 0x7FFFFFFF;
-    if (lane < n) get(lane, 0, hv, hi);
+    float hv = -INFINITY, nv = -INFINITY;
+    int hi = 0x7FFFFFFF, ni = 0x7FFFFFFF;
+    if (lane < n) {
+        get(lane, 0, hv, hi);
+        if (K > 1) get(lane, 1, nv, ni);
+    }
     out_v = -INFINITY;
     out_i = 0x7FFFFFFF;
     for (int k = 0; k < K; ++k) {
@@ -508,29 +520,40 @@ __device__ __forceinline__ void merge_sorted_lists(int n, int K, int lane, Get g
         int bi = hi;
         float ov = dpp<kDppXor1>(bv);
         int oi = dpp<kDppXor1>(bi);
-        if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        bool t = ahead_of(ov, oi, bv, bi);
+        bv = t ? ov : bv;
+        bi = t ? oi : bi;
         ov = dpp<kDppXor2>(bv);
         oi = dpp<kDppXor2>(bi);
-        if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        t = ahead_of(ov, oi, bv, bi);
+        bv = t ? ov : bv;
+        bi = t ? oi : bi;
         ov = dpp<kDppHalfMirror>(bv);
         oi = dpp<kDppHalfMirror>(bi);
-        if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        t = ahead_of(ov, oi, bv, bi);
+        bv = t ? ov : bv;
+        bi = t ? oi : bi;
         ov = dpp<kDppMirror>(bv);
         oi = dpp<kDppMirror>(bi);
-        if (ahead_of(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        t = ahead_of(ov, oi, bv, bi);
+        bv = t ? ov : bv;
+        bi = t ? oi : bi;
         bv = readlane(bv, 0);
         bi = readlane(bi, 0);
         if (lane == k) {
             out_v = bv;
             out_i = bi;
         }
+        // the winning list (indices are distinct) advances
         if (lane < n && hi == bi) {
             ++pos;
-            if (pos < K) {
-                get(lane, pos, hv, hi);
+            hv = nv;
+            hi = ni;
+            if (pos + 1 < K) {
+                get(lane, pos + 1, nv, ni);
             } else {
-                hv = -INFINITY;
-                hi = 0x7FFFFFFF;
+                nv = -INFINITY;
+                ni = 0x7FFFFFFF;
             }
         }
     }
@@ -552,6 +575,8 @@ __global__ void __launch_bounds__(W * 64)
     __shared__ float s_val[W][kTopKMax];
     __shared__ int s_idx[W][kTopKMax];
     __shared__ State s_md[W];
+    __shared__ float s_sub[64];
+    __shared__ int s_rank[64];
     __shared__ int s_thr;
 
     const int tid = threadIdx.x;
@@ -568,8 +593,12 @@ __global__ void __launch_bounds__(W * 64)
         const int seg = SPLIT ? static_cast<int>(unit - row * S) : 0;
         const int v0 = seg * seg_vec;
         const int v1 = (v0 + seg_vec < nvec) ? v0 + seg_vec : nvec;
-        const Buf bin(in + row * static_cast<int64_t>(cols), row_bytes);
+        // The resource ends with the segment, so loads issued ahead past its
+        // end (into the next segment or past the row) touch no memory.
+        const uint32_t seg_end = static_cast<uint32_t>(v1) * 16u;
+        const Buf bin(in + row * static_cast<int64_t>(cols), seg_end < row_bytes ? seg_end : row_bytes);
         if (tid == 0) s_thr = ordered_bits(-INFINITY);
+        if (tid < 64) s_rank[tid] = 0;
         __syncthreads();
 
         float ml = kFloor, dl = 0.0f;
@@ -577,14 +606,11 @@ __global__ void __launch_bounds__(W * 64)
         int I = 0x7FFFFFFF;
         float T = -INFINITY;
         bool first = true;
-        // Software pipeline: the raw loads of the next tile are issued before
-        // the current tile is folded, so they are in flight during the
-        // compute.  Loads past the end of the row touch no memory (buffer
-        // range check); slots past the segment are masked to -inf.
-        u32x4 raw[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(v0 + u * BLOCK + tid) * 16u);
-        for (int base = v0; base < v1; base += STEP) {
+
+        // One tile: unpack the raw loads (slots past the segment become
+        // -inf), issue the next tile's loads into the same registers, fold
+        // (m, d), then look for candidates.
+        auto tile = [&](u32x4 (&raw)[U], const int base) {
             float x[U][VEC];
             if constexpr (ALIGNED) {
 #pragma unroll
@@ -623,12 +649,8 @@ __global__ void __launch_bounds__(W * 64)
             // candidates
             if (first) {
                 // every wave of the workgroup runs the segment's first tile
-                // (v0 < v1 is uniform), so all reach the barrier
-                const float t0 = group_bound(mx, K);
-                if (lane == 0)
-                    __hip_atomic_fetch_max(&s_thr, ordered_bits(t0), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-                __syncthreads();
+                // (v0 < v1 is uniform), so all reach the barriers inside
+                T = tile_bound<W>(mx, K, w, lane, s_sub, s_rank);
                 first = false;
             }
             T = fmaxf(T, from_ordered_bits(__hip_atomic_load(&s_thr, __ATOMIC_RELAXED,
@@ -636,18 +658,18 @@ __global__ void __launch_bounds__(W * 64)
             if (__ballot(mx >= T) != 0) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int slot = base + u * BLOCK + tid;
                     const int wave_slot0 = base + u * BLOCK + w * kWave;
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) {
-                        const bool hit = slot < v1 && (slot * VEC + k < cols) && (x[u][k] >= T);
-                        uint64_t mask = __ballot(hit);
+                        // slots past the segment hold -inf; they pass only
+                        // when T is -inf and are dropped below
+                        uint64_t mask = __ballot(x[u][k] >= T);
                         while (mask != 0) {
                             const int l = __builtin_ctzll(mask);
                             mask &= mask - 1;
-                            const float v = readlane(x[u][k], l);
                             const int i = (wave_slot0 + l) * VEC + k;
-                            list_insert(L, I, v, i, K, lane, kmask);
+                            const float v = readlane(x[u][k], l);
+                            if ((wave_slot0 + l < v1) & (i < cols)) list_insert(L, I, v, i, K, lane, kmask);
                         }
                     }
                 }
@@ -659,7 +681,17 @@ __global__ void __launch_bounds__(W * 64)
                                                __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
             }
+        };
+
+        // Software pipeline over the segment's tiles: the loads of the next
+        // tile are in flight while one is folded.  Loads past the end of the
+        // segment touch no memory (buffer range check).
+        u32x4 raw[U];
+        if constexpr (ALIGNED) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(v0 + u * BLOCK + tid) * 16u);
         }
+        for (int base = v0; base < v1; base += STEP) tile(raw, base);
 
         const State st = group_merge<64>(State{ml, dl});
         if (lane < K) {

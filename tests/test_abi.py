@@ -137,6 +137,8 @@ def test_topk_split_validation(L, ons):
     assert ons.os_topk_plan(64, 128256, 8) == 4
     assert ons.os_topk_plan(4096, 128256, 8) == 1
     assert ons.os_topk_plan(16, 1000, 8) == 1
+    assert ons.os_topk_plan(64, 32000, 8) == 1
+    assert ons.os_topk_plan(16, 1 << 20, 8) == 8
 
 
 def test_copy_validation(L):
