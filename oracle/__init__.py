@@ -12,6 +12,9 @@ with the passages it follows:
   "OnlineSoftmax: Online normalizer calculation for softmax", section 2
   (safe softmax), and "CUDA算子优化(3)：Softmax", section "Softmax的cpu实现".
 * ``stats`` -- the per-row state (m, d) by the same plain definition.
+* ``logsumexp`` -- the per-row log(sum e^{x}) = m + log(d), the statistic that
+  "6.2 FlashAttention V2 chi tiết" keeps for the backward pass (sections 6.1,
+  7.1).
 * ``online_state`` -- the element-by-element recurrence of section 3.1 of the
   paper summary, starting from the identity (-inf, 0) ("第 7 课：Online Softmax
   与可结合状态", section 3).
@@ -67,6 +70,10 @@ class Oracle:
         for name in ("oracle_stats_f32", "oracle_stats_bf16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp, i64, i64, vp, vp]
+            fn.restype = ctypes.c_int
+        for name in ("oracle_logsumexp_f32", "oracle_logsumexp_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, i64, i64, vp]
             fn.restype = ctypes.c_int
         lib.oracle_online_state.argtypes = [vp, i64, _c_double_p, _c_double_p]
         lib.oracle_online_state.restype = None
@@ -142,6 +149,27 @@ class Oracle:
 
         self._run_rows(part, rows, threads)
         return m, d
+
+    def logsumexp(self, x: np.ndarray, threads: int = 1) -> np.ndarray:
+        """Per-row log(sum e^{x}) in double."""
+        x = np.ascontiguousarray(x)
+        rows, cols = x.shape
+        out = np.empty(rows, dtype=np.float64)
+        if rows == 0:
+            return out
+        if x.dtype == np.float32:
+            fn, esz = self.lib.oracle_logsumexp_f32, 4
+        elif x.dtype == np.uint16:
+            fn, esz = self.lib.oracle_logsumexp_bf16, 2
+        else:
+            raise TypeError("x must be float32 or uint16 (bf16 bit patterns)")
+        xb, ob = x.ctypes.data, out.ctypes.data
+
+        def part(r0, r1):
+            return fn(ctypes.c_void_p(xb + r0 * cols * esz), r1 - r0, cols, ctypes.c_void_p(ob + r0 * 8))
+
+        self._run_rows(part, rows, threads)
+        return out
 
     # -- the recurrence and the operator -------------------------------------
     def online_state(self, x) -> tuple[float, float]:

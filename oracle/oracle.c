@@ -19,6 +19,8 @@
  *   [TOPK]   same paper summary, section 4 "Softmax and top-k fusion"
  *            (probabilities of the K largest logits, relative to the whole
  *            row).  The oracle does not fuse anything: it sorts the whole row.
+ *   [LSE]    "6.2 FlashAttention V2 chi tiết", sections 6.1 and 7.1 (the
+ *            per-row logsumexp L = m + log(l) kept in place of m and l).
  *
  * Readings taken where the pages are silent:
  *   - An element equal to -inf contributes e^{-inf} = 0 and leaves the state
@@ -28,6 +30,9 @@
  *     propagation through exp and the sum).
  *   - Top-K order is the total order (value descending, index ascending); the
  *     probability of a selected logit u is e^{u - m}/d over the whole row.
+ *   - The logsumexp of a row is log(sum_j e^{x_j}), written as m + log(d)
+ *     (an exact identity that keeps the sum finite): -inf for an empty or
+ *     all -inf row, NaN for a row holding NaN or +inf, as for the softmax.
  *
  * Every floating-point step is IEEE double with no reassociation: build with
  * -ffp-contract=off and without -ffast-math.
@@ -143,6 +148,42 @@ int oracle_stats_bf16(const uint16_t *x, int64_t rows, int64_t cols, double *m, 
         widen_row_bf16(x + r * cols, cols, buf);
         m[r] = row_max(buf, cols);
         d[r] = row_sum_exp(buf, cols, m[r]);
+    }
+    free(buf);
+    return 0;
+}
+
+/* [LSE] per-row logsumexp log(sum_j e^{x_j}) = m + log(sum_j e^{x_j - m}),
+ * from the plain-definition m and d above; the empty and all -inf rows
+ * (d = 0) give -inf. */
+static double row_logsumexp(const double *x, int64_t n)
+{
+    const double m = row_max(x, n);
+    const double d = row_sum_exp(x, n, m);
+    return (d == 0.0) ? -INFINITY : m + log(d);
+}
+
+int oracle_logsumexp_f32(const float *x, int64_t rows, int64_t cols, double *lse)
+{
+    double *buf = (double *)malloc((size_t)(cols > 0 ? cols : 1) * sizeof(double));
+    if (!buf)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        widen_row_f32(x + r * cols, cols, buf);
+        lse[r] = row_logsumexp(buf, cols);
+    }
+    free(buf);
+    return 0;
+}
+
+int oracle_logsumexp_bf16(const uint16_t *x, int64_t rows, int64_t cols, double *lse)
+{
+    double *buf = (double *)malloc((size_t)(cols > 0 ? cols : 1) * sizeof(double));
+    if (!buf)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        widen_row_bf16(x + r * cols, cols, buf);
+        lse[r] = row_logsumexp(buf, cols);
     }
     free(buf);
     return 0;

@@ -265,6 +265,38 @@ def pin_topk_library(o):
     assert np.array_equal(i, ref)
 
 
+def pin_logsumexp(o):
+    """logsumexp = scipy.special.logsumexp; closed forms; special rows; exp(x - L) = softmax."""
+    from scipy.special import logsumexp, softmax
+    x = workloads.normal(24, 389, seed=61, scale=4.0)
+    x[0, :5] = 80.0
+    x[1, 7] = -np.inf
+    L = o.logsumexp(x)
+    ref = logsumexp(x.astype(np.float64), axis=1)
+    assert np.max(np.abs(L - ref)) <= 1e-13
+    # L near 80 carries ~1e-14 of rounding, which exp(x - L) passes on
+    assert np.max(np.abs(np.exp(x.astype(np.float64) - L[:, None]) - softmax(x.astype(np.float64), axis=1))) <= 1e-13
+    b = workloads.config(3, 0, 8)
+    f = b.view(np.int16).astype(np.int32) << 16
+    fb = f.astype(np.uint32).view(np.float32).astype(np.float64)
+    assert np.max(np.abs(o.logsumexp(b) - logsumexp(fb, axis=1))) <= 1e-13
+    # a + ln N for N equal entries; ln(e + e^2 + e^3); one element; two elements
+    for a, n in ((0.375, 1), (-7.5, 2), (3.0, 1000), (80.0, 4096)):
+        assert _rel(o.logsumexp(np.full((1, n), a, dtype=np.float32))[0], a + math.log(n)) <= 1e-15
+    assert _rel(o.logsumexp(np.array([[1.0, 2.0, 3.0]], dtype=np.float32))[0],
+                math.log(math.e + math.e ** 2 + math.e ** 3)) <= 1e-15
+    assert o.logsumexp(np.array([[-3e38]], dtype=np.float32))[0] == np.float64(np.float32(-3e38))
+    assert _rel(o.logsumexp(np.array([[0.5, -1.25]], dtype=np.float32))[0],
+                0.5 + math.log1p(math.exp(-1.75))) <= 1e-15
+    # -inf entries add nothing; all -inf gives -inf; empty rows give -inf
+    assert o.logsumexp(np.array([[2.0, -np.inf, 1.0]], dtype=np.float32))[0] == \
+        o.logsumexp(np.array([[2.0, 1.0]], dtype=np.float32))[0]
+    assert o.logsumexp(np.full((1, 3), -np.inf, dtype=np.float32))[0] == -np.inf
+    assert o.logsumexp(np.zeros((2, 0), dtype=np.float32)).tolist() == [-np.inf, -np.inf]
+    assert np.isnan(o.logsumexp(np.array([[1.0, np.nan]], dtype=np.float32))[0])
+    assert np.isnan(o.logsumexp(np.array([[1.0, np.inf]], dtype=np.float32))[0])
+
+
 PINS = [
     pin_two_shard_worked_example,
     pin_lesson_mock_vector,
@@ -279,6 +311,7 @@ PINS = [
     pin_shift_invariance,
     pin_bf16_widening,
     pin_topk_library,
+    pin_logsumexp,
 ]
 
 

@@ -39,6 +39,8 @@ MUTANTS = [
     ("topk_prob_unshifted", "probs[r * K + k] = exp(order[k].value - m) / d;",
      "probs[r * K + k] = exp(order[k].value) / d;"),
     ("bf16_wrong_shift", "((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
+    ("logsumexp_drops_max", "return (d == 0.0) ? -INFINITY : m + log(d);",
+     "return (d == 0.0) ? -INFINITY : log(d);"),
 ]
 
 
