@@ -293,6 +293,7 @@ def all_configs(ons, stream):
         entry = {"workload": n, "rows": rows, "cols": cols, "dtype": str(x.dtype).replace("torch.", ""),
                  "shape": list(ons.os_forward_plan(cols, x.dtype)), "algorithmic_bytes": nbytes}
         for name, fn in (("online", lambda: ons.os_softmax_forward(x, out=y)),
+                         ("online_lse", lambda: ons.os_softmax_forward_lse(x, out=y)),
                          ("safe_3pass", lambda: ons.safe_softmax_forward(x, out=y)),
                          ("copy", lambda: ons.os_device_copy(x, y))):
             t, te = measure(fn, reps)

@@ -123,6 +123,23 @@ int os_softmax_stats(const void *in, float *m, float *d, int64_t rows, int64_t c
                      void *stream);
 
 /*
+ * Forward with the per-row logsumexp L = m + ln d = ln(sum_j e^{x_j}), the
+ * statistic "6.2 FlashAttention V2 chi tiết" keeps in place of m and d for
+ * the backward pass (sections 6.1 and 7.1), written by the same launch as y.
+ *   in      [rows, cols] of `dtype`.
+ *   out     [rows, cols] of `dtype`, y as os_softmax_forward writes it, or
+ *           NULL to compute L alone (a logsumexp reduction).  in == out is
+ *           allowed.
+ *   lse     [rows] float, owned by the caller.  -inf for a row with no entry
+ *           above -inf (or cols == 0); NaN for a row holding NaN or +inf.
+ *           fp32: m + log2(d) * ln 2 rounded once (fused multiply-add).
+ *   Returns OS_OK, OS_EINVAL (lse NULL or misaligned, or as for the
+ *   forward), or OS_ELAUNCH.
+ */
+int os_softmax_forward_lse(const void *in, void *out, float *lse, int64_t rows, int64_t cols, int dtype,
+                           void *stream);
+
+/*
  * Fused softmax + top-K in one read of the input (paper summary, section 4):
  * the K largest logits of each row and their probabilities over the WHOLE row,
  * v = e^{u - m} / d (not renormalised over the K).  The full softmax is never

@@ -31,7 +31,7 @@ import torch  # loaded first: its HIP runtime is the one the library binds to
 
 __all__ = [
     "OS_F32", "OS_BF16", "OS_TOPK_KMAX", "OnlineSoftmaxError", "LIB_PATH", "lib",
-    "os_softmax_forward", "os_softmax_forward_tuned", "os_softmax_stats", "os_softmax_topk",
+    "os_softmax_forward", "os_softmax_forward_tuned", "os_softmax_stats", "os_softmax_forward_lse", "os_softmax_topk",
     "safe_softmax_forward", "os_device_copy", "os_forward_plan", "os_last_error", "os_version",
     "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan",
 ]
@@ -77,6 +77,7 @@ def _load() -> ctypes.CDLL:
         "os_softmax_forward_tuned": [vp, vp, i64, i64, i32, i32, i32, i32, vp],
         "os_forward_plan": [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
         "os_softmax_stats": [vp, vp, vp, i64, i64, i32, vp],
+        "os_softmax_forward_lse": [vp, vp, vp, i64, i64, i32, vp],
         "os_softmax_topk": [vp, vp, vp, i64, i64, i32, vp],
         "safe_softmax_forward": [vp, vp, i64, i64, i32, vp],
         "os_device_copy": [vp, vp, i64, vp],
@@ -188,6 +189,19 @@ def os_softmax_stats(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
            lib().os_softmax_stats(x.data_ptr(), m.data_ptr(), d.data_ptr(), rows, cols, _dtype_code(x),
                                   _stream(x)))
     return m, d
+
+
+def os_softmax_forward_lse(x: torch.Tensor, out: torch.Tensor | None = None,
+                           write_y: bool = True) -> tuple[torch.Tensor | None, torch.Tensor]:
+    """y = softmax(x) and L = logsumexp(x) over the last dim in one launch;
+    with write_y=False only L is computed (y is None)."""
+    rows, cols = _rows_cols(x)
+    y = _out_like(x, out) if write_y else None
+    lse = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check("os_softmax_forward_lse",
+           lib().os_softmax_forward_lse(x.data_ptr(), None if y is None else y.data_ptr(), lse.data_ptr(), rows,
+                                        cols, _dtype_code(x), _stream(x)))
+    return y, lse
 
 
 def os_topk_plan(rows: int, cols: int, K: int) -> int:

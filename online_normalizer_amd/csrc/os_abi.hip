@@ -72,7 +72,7 @@ int launched(const char* fn) {
 // ---------------------------------------------------------------------------
 // Register-resident shapes built into the library.
 // ---------------------------------------------------------------------------
-typedef void (*RowKernel)(const void*, void*, float*, float*, int64_t, int);
+typedef void (*RowKernel)(const void*, void*, RowStats, int64_t, int);
 typedef void (*SafeKernel)(const void*, void*, int64_t, int);
 
 struct ResidentShape {
@@ -206,7 +206,7 @@ int grid_for(int64_t groups, int block, int requested) {
     return static_cast<int>(g);
 }
 
-int run_rows(const char* fn, const void* in, void* out, float* st_m, float* st_d, int64_t rows,
+int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t rows,
              int64_t cols, int dtype, int lpr, int vpl, int grid_req, void* stream) {
     // Shape checks first: no HIP call happens before every argument is known good.
     const ResidentShape* shape = nullptr;
@@ -227,7 +227,7 @@ int run_rows(const char* fn, const void* in, void* out, float* st_m, float* st_d
         const int w = stream_waves(cols, dtype);
         const int block = w * 64;
         const int grid = grid_for(rows, block, grid_req);
-        hipLaunchKernelGGL(stream_kernel(w, dtype, al), dim3(grid), dim3(block), 0, st, in, out, st_m, st_d,
+        hipLaunchKernelGGL(stream_kernel(w, dtype, al), dim3(grid), dim3(block), 0, st, in, out, stats,
                            rows, static_cast<int>(cols));
         return launched(fn);
     }
@@ -235,7 +235,7 @@ int run_rows(const char* fn, const void* in, void* out, float* st_m, float* st_d
     const int rpb = block / lpr;
     const int64_t groups = (rows + rpb - 1) / rpb;
     const int grid = grid_for(groups, block, grid_req);
-    hipLaunchKernelGGL(shape->fn[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, st_m, st_d, rows,
+    hipLaunchKernelGGL(shape->fn[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, stats, rows,
                        static_cast<int>(cols));
     return launched(fn);
 }
@@ -264,7 +264,7 @@ int os_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, in
     if (rc != OS_OK) return rc;
     int lpr = 0, vpl = 0;
     auto_plan(cols, dtype, &lpr, &vpl);
-    return run_rows(fn, in, out, nullptr, nullptr, rows, cols, dtype, lpr, vpl, 0, stream);
+    return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, stream);
 }
 
 int os_softmax_forward_tuned(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int lanes_per_row,
@@ -278,7 +278,7 @@ int os_softmax_forward_tuned(const void* in, void* out, int64_t rows, int64_t co
         return fail(OS_EUNSUPPORTED, "%s: no kernel built for lanes_per_row=%d vecs_per_lane=%d", fn, lanes_per_row,
                     vecs_per_lane);
     if (rc == 1) return ok();
-    return run_rows(fn, in, out, nullptr, nullptr, rows, cols, dtype, lanes_per_row, vecs_per_lane, grid_blocks,
+    return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lanes_per_row, vecs_per_lane, grid_blocks,
                     stream);
 }
 
@@ -292,7 +292,23 @@ int os_softmax_stats(const void* in, float* m, float* d, int64_t rows, int64_t c
     // cols == 0: every row is empty and gets the identity state; the input is never read.
     int lpr = 0, vpl = 0;
     auto_plan(cols, dtype, &lpr, &vpl);
-    return run_rows(fn, cols == 0 ? nullptr : in, nullptr, m, d, rows, cols, dtype, lpr, vpl, 0, stream);
+    return run_rows(fn, cols == 0 ? nullptr : in, nullptr, RowStats{m, d, nullptr}, rows, cols, dtype, lpr, vpl, 0,
+                    stream);
+}
+
+int os_softmax_forward_lse(const void* in, void* out, float* lse, int64_t rows, int64_t cols, int dtype,
+                           void* stream) {
+    const char* fn = "os_softmax_forward_lse";
+    int rc = check_problem(fn, in, out, false, rows, cols, dtype);
+    if (rc != OS_OK && rc != 1) return rc;
+    if (rows == 0) return ok();
+    if (lse == nullptr) return fail(OS_EINVAL, "%s: lse must not be NULL", fn);
+    if (!aligned(lse, 4)) return fail(OS_EINVAL, "%s: lse must be 4-byte aligned", fn);
+    // cols == 0: every row is empty, L = -inf; neither x nor y is touched.
+    int lpr = 0, vpl = 0;
+    auto_plan(cols, dtype, &lpr, &vpl);
+    return run_rows(fn, cols == 0 ? nullptr : in, cols == 0 ? nullptr : out, RowStats{nullptr, nullptr, lse}, rows,
+                    cols, dtype, lpr, vpl, 0, stream);
 }
 
 int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {

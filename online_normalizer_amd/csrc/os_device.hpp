@@ -32,6 +32,11 @@ __device__ __forceinline__ float exp_e(float t) { return __builtin_amdgcn_exp2f(
 
 __device__ __forceinline__ float rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 
+constexpr float kLn2 = 0.693147180559945309417f;
+// m + ln(d) as one fused multiply-add on the hardware base-2 logarithm
+// (v_log_f32): ln d = log2(d) * ln 2.  Callers pass d >= 1 (a normal number).
+__device__ __forceinline__ float add_log_e(float m, float d) { return fmaf(__builtin_amdgcn_logf(d), kLn2, m); }
+
 // ---------------------------------------------------------------------------
 // The normaliser state and the merge (+).
 // ---------------------------------------------------------------------------

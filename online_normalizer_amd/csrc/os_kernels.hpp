@@ -100,6 +100,26 @@ __device__ __forceinline__ void store_slot(const Buf& b, uint32_t row_off, int v
     }
 }
 
+// Per-row statistics a forward launch may write besides y; each pointer may
+// be null.  m and d: the row's state ((-inf, 0) for an empty or all -inf
+// row).  lse: the logsumexp L = m + ln d, -inf for such rows.
+struct RowStats {
+    float* m;
+    float* d;
+    float* lse;
+};
+
+__device__ __forceinline__ bool any_stats(const RowStats& o) { return (o.m != nullptr) | (o.lse != nullptr); }
+
+__device__ __forceinline__ void put_stats(const RowStats& o, int64_t row, State s) {
+    const bool empty = s.d == 0.0f;
+    if (o.m != nullptr) {
+        o.m[row] = empty ? -INFINITY : s.m;
+        o.d[row] = s.d;
+    }
+    if (o.lse != nullptr) o.lse[row] = empty ? -INFINITY : add_log_e(s.m, s.d);
+}
+
 // ---------------------------------------------------------------------------
 // Register-resident forward: the row is read from HBM once.
 //
@@ -113,11 +133,11 @@ __device__ __forceinline__ void store_slot(const Buf& b, uint32_t row_off, int v
 // one tile): m_l = max of the slice, e_k = e^{x_k - m_l}, d_l = sum e_k; the
 // e_k stay in registers.  The lane states merge with (+).  Pass 2 writes
 // y_k = e_k * (e^{m_l - m} / d): one exponential per element in all.
-// Writes y when out != nullptr and (m, d) when st_m != nullptr.
+// Writes y when out != nullptr, and the statistics that `st` asks for.
 // ---------------------------------------------------------------------------
 template <bool BF16, int LPR, int VPL, bool ALIGNED>
 __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
-    k_resident(const void* in, void* out, float* st_m, float* st_d, int64_t rows, int cols) {
+    k_resident(const void* in, void* out, RowStats st, int64_t rows, int cols) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int BLOCK = LPR <= 64 ? 256 : LPR;
@@ -170,10 +190,7 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
             par ^= 1;
         }
 
-        if (st_m != nullptr && live && j == 0) {
-            st_m[row] = (s.d == 0.0f) ? -INFINITY : s.m;
-            st_d[row] = s.d;
-        }
+        if (any_stats(st) && live && j == 0) put_stats(st, row, s);
         if (out != nullptr) {
             const float scale = exp_e(ml - s.m) * rcp(s.d);
             const Buf bout(static_cast<char*>(out) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
@@ -197,7 +214,7 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
 // ---------------------------------------------------------------------------
 template <bool BF16, int W, int U, bool ALIGNED>
 __global__ void __launch_bounds__(W * 64)
-    k_stream(const void* in, void* out, float* st_m, float* st_d, int64_t rows, int cols) {
+    k_stream(const void* in, void* out, RowStats st, int64_t rows, int cols) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int BLOCK = W * 64;
@@ -237,10 +254,7 @@ __global__ void __launch_bounds__(W * 64)
             for (int w = 1; w < W; ++w) s = oplus(s, lds[par][w]);
             par ^= 1;
         }
-        if (st_m != nullptr && tid == 0) {
-            st_m[row] = (s.d == 0.0f) ? -INFINITY : s.m;
-            st_d[row] = s.d;
-        }
+        if (any_stats(st) && tid == 0) put_stats(st, row, s);
         if (out != nullptr) {
             const float inv_d = rcp(s.d);
             const Buf bout(static_cast<char*>(out) + row * row_bytes, row_bytes);

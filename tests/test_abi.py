@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["os_softmax_forward", "os_softmax_topk", "safe_softmax_forward", "os_softmax_stats",
-              "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
+              "os_softmax_forward_lse", "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
         assert n in names
 
 
@@ -100,6 +100,17 @@ def test_stats_validation(L):
     assert L.os_softmax_stats(FAKE, FAKE + 1, FAKE, 4, 4, F32, None) == EINVAL
     assert L.os_softmax_stats(None, FAKE, FAKE, 4, 4, F32, None) == EINVAL
     assert L.os_softmax_stats(None, None, None, 0, 4, F32, None) == 0
+
+
+def test_lse_validation(L):
+    f = L.os_softmax_forward_lse
+    assert f(FAKE, FAKE, None, 4, 4, F32, None) == EINVAL          # no lse
+    assert f(FAKE, FAKE, FAKE + 2, 4, 4, F32, None) == EINVAL      # misaligned lse
+    assert f(None, FAKE, FAKE, 4, 4, F32, None) == EINVAL          # no input
+    assert f(FAKE, FAKE + 2, FAKE, 4, 4, F32, None) == EINVAL      # misaligned output
+    assert f(FAKE, None, FAKE, 4, 4, 7, None) == EINVAL            # unknown dtype
+    assert f(FAKE, None, FAKE, -1, 4, F32, None) == EINVAL         # negative rows
+    assert f(None, None, None, 0, 4, F32, None) == 0               # no rows: nothing to do
 
 
 @pytest.mark.parametrize("args,code", [

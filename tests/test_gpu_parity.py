@@ -286,6 +286,106 @@ def test_stats_invariants(ons, orc):
     assert np.max(np.abs(to_host(d) - do) / do) <= 1e-5
 
 
+# -- logsumexp alongside the forward ------------------------------------------------
+
+def lse_tol(ref: np.ndarray) -> np.ndarray:
+    """Bound on |L - L_oracle| for L = m + ln d in fp32.  m is exact.  d's relative
+    error stays below about 4e-6: up to 64 sequential fp32 additions per lane
+    plus the merge tree (about 74 * 2^-24), with each e^{x-m} within a few ulp.
+    So ln d is off by about that much in absolute terms, plus about 1 ulp from
+    the base-2 logarithm.  The final fused m + log2(d) * ln 2 rounds once, by
+    at most 2^-24 |L|.  Allow 1e-5 absolute plus 2^-22 |L|."""
+    return 1e-5 + 2.0 ** -22 * np.abs(ref)
+
+
+def bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+def check_lse(ons, orc, x: np.ndarray, what: str, write_y: bool = True, rows=None):
+    say(f"lse {what} rows={x.shape[0]} cols={x.shape[1]} write_y={write_y}")
+    xd = to_device(np.ascontiguousarray(x))
+    y, L = ons.os_softmax_forward_lse(xd, write_y=write_y)
+    torch.cuda.synchronize()
+    L = to_host(L).astype(np.float64)
+    if rows is not None:
+        L, ref = L[rows], orc.logsumexp(np.ascontiguousarray(x[rows]), threads=16)
+    else:
+        ref = orc.logsumexp(x, threads=16)
+    assert np.array_equal(np.isnan(L), np.isnan(ref)), what
+    assert np.array_equal(np.isneginf(L), np.isneginf(ref)), what
+    fin = np.isfinite(ref)
+    err = np.abs(L[fin] - ref[fin])
+    assert np.all(err <= lse_tol(ref[fin])), f"{what}: max |L - ref| = {err.max()}"
+    if write_y:
+        y_plain = ons.os_softmax_forward(xd)  # same kernels: y must not change
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y), bits(y_plain)), what
+    else:
+        assert y is None
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_lse_every_plan_bucket(ons, orc, bf16):
+    for cols in [1, 3, 8, 33, 128, 129, 1000, 2048, 4097, 8193, 32000, 65536, 65537, 200001]:
+        rows = 13 if cols < 20000 else 4
+        x32 = workloads.normal(rows, cols, seed=7000 + cols, scale=4.0)
+        x32[0, cols // 2] = 80.0
+        x = bf16_bits(x32) if bf16 else x32
+        check_lse(ons, orc, x, f"bf16={bf16} cols={cols}")
+        check_lse(ons, orc, x, f"bf16={bf16} cols={cols}", write_y=False)
+
+
+def test_lse_special_rows(ons, orc):
+    """-inf rows give -inf, NaN / +inf rows NaN, one element gives x, N equal entries a + ln N."""
+    for cols in (6, 1024, 32000, 70000):
+        x = workloads.normal(8, cols, seed=cols + 1, scale=2.0)
+        x[0, ::3] = -np.inf
+        x[1, :] = -np.inf
+        x[2, cols // 3] = np.inf
+        x[3, cols - 1] = np.nan
+        x[4, :] = 0.375
+        x[5, :] = -np.inf
+        x[5, 1] = -3.0e38
+        x[6, :] = -80.0
+        check_lse(ons, orc, x, f"special cols={cols}")
+        _, L = ons.os_softmax_forward_lse(to_device(x), write_y=False)
+        torch.cuda.synchronize()
+        L = to_host(L)
+        assert L[1] == -np.inf and np.isnan(L[2]) and np.isnan(L[3])
+        assert L[5] == np.float32(-3.0e38)  # one finite entry: L = x exactly
+        assert abs(float(L[4]) - (0.375 + math.log(cols))) <= lse_tol(np.array(0.375 + math.log(cols)))
+    x = workloads.normal(5, 1, seed=2, scale=30.0)
+    _, L = ons.os_softmax_forward_lse(to_device(x), write_y=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(L), x[:, 0])  # cols = 1: L = x exactly
+    _, L = ons.os_softmax_forward_lse(torch.empty((3, 0), device="cuda"), write_y=False)
+    torch.cuda.synchronize()
+    assert to_host(L).tolist() == [-np.inf] * 3  # empty rows
+
+
+def test_lse_in_place(ons):
+    x = workloads.normal(37, 4096, seed=77, scale=3.0)
+    xd = to_device(x)
+    y_ref, L_ref = ons.os_softmax_forward_lse(to_device(x))
+    y, L = ons.os_softmax_forward_lse(xd, out=xd)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == xd.data_ptr()
+    assert torch.equal(bits(xd), bits(y_ref)) and torch.equal(bits(L), bits(L_ref))
+
+
+@pytest.mark.parametrize("n", [2, 3, 4])
+def test_lse_full_configs(ons, orc, n):
+    """Full-size workloads in the forward's launch configuration; all rows of
+    workload 2, sampled rows of the two largest."""
+    x = workloads.config(n)
+    rows = None
+    if n != 2:
+        rng = np.random.Generator(np.random.PCG64(100 + n))
+        rows = np.unique(np.concatenate([[0, x.shape[0] - 1], rng.choice(x.shape[0], 16384, replace=False)]))
+    check_lse(ons, orc, x, f"config{n}", rows=rows)
+
+
 # -- fused softmax + top-K ---------------------------------------------------------
 
 def check_topk(ons, orc, x: np.ndarray, K: int, what: str, splits=None):
