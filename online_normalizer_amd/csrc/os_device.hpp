@@ -66,6 +66,10 @@ enum : int {
     kDppHalfMirror = 0x141, // row_half_mirror: lane i <-> 7-i within 8
     kDppMirror = 0x140,     // row_mirror: lane i <-> 15-i within 16
     kDppWaveShr1 = 0x138,   // wave_shr:1, lane i reads lane i-1
+    kDppRev4 = 0x1B,        // quad_perm [3,2,1,0]: lane i <-> 3-i within 4
+    kDppRowShl4 = 0x104,    // row_shl:4, lane i reads lane i+4 within its row of 16
+    kDppRowShr4 = 0x114,    // row_shr:4, lane i reads lane i-4 within its row of 16
+    kDppRowRor8 = 0x128,    // row_ror:8, lane i reads lane i^8 within its row of 16
 };
 
 template <int CTRL>
@@ -77,6 +81,30 @@ __device__ __forceinline__ float dpp(float v) {
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
     return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+// The value held by lane (lane ^ MASK), for the masks the sorting networks
+// use: DPP where the partner sits in the same row of 16, ds_bpermute (the LDS
+// crossbar, no memory access) otherwise.
+template <int MASK>
+__device__ __forceinline__ int lane_xor(int v, int lane) {
+    if constexpr (MASK == 0) return v;
+    else if constexpr (MASK == 1) return dpp<kDppXor1>(v);
+    else if constexpr (MASK == 2) return dpp<kDppXor2>(v);
+    else if constexpr (MASK == 3) return dpp<kDppRev4>(v);
+    else if constexpr (MASK == 4) {
+        const int up = dpp<kDppRowShl4>(v);
+        const int down = dpp<kDppRowShr4>(v);
+        return (lane & 4) ? down : up;
+    } else if constexpr (MASK == 7) return dpp<kDppHalfMirror>(v);
+    else if constexpr (MASK == 8) return dpp<kDppRowRor8>(v);
+    else if constexpr (MASK == 15) return dpp<kDppMirror>(v);
+    else return __builtin_amdgcn_ds_bpermute((lane ^ MASK) << 2, v);
+}
+
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float v, int lane) {
+    return __int_as_float(lane_xor<MASK>(__float_as_int(v), lane));
 }
 
 // v_permlane16_swap: returns {own row's copy, partner row's copy} so that

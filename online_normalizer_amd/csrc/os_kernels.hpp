@@ -18,6 +18,7 @@
 namespace onorm {
 
 constexpr int kTopKMax = 32;
+constexpr int kTopKMaxSplits = 16;
 
 template <bool BF16, bool ALIGNED>
 __device__ __forceinline__ int vec_count(int cols) {
@@ -436,15 +437,14 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
 // row's K-th largest value:
 //   - first tile: the workgroup's tile is cut into 64 disjoint parts of W
 //     lanes; the K-th largest of the 64 part maxima is a tile element with
-//     at least K elements at or above it (one barrier, before any insert);
+//     at least K elements at or above it (two barriers, before any insert);
 //   - then: the K-th entry of the wave's own list, and the largest K-th entry
 //     published by any wave of the workgroup (an LDS atomic max).
 // Survivors (x >= T, so ties at T are kept) are inserted one at a time:
 // position p = number of entries ahead of the new pair, entries from p on
 // shift down one lane (DPP wave_shr:1).  Every true top-K element survives
-// every filter and stays in its wave's list, so the final K-way selection
-// over the W sorted lists (16-lane argmax rounds, lowest index on ties) is
-// exact.  Output: probs = e^{u - m} / d over the whole row, and indices.
+// every filter and stays in its wave's list, so the final merge of the W
+// sorted lists (a bitonic merge in one wave, lowest index on ties) is exact.  Output: probs = e^{u - m} / d over the whole row, and indices.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int ordered_bits(float f) {
     const int i = __float_as_int(f);
@@ -513,64 +513,98 @@ struct TopkEntry {
     int i;
 };
 
-// K rounds of a 16-lane argmax over up to 16 sorted lists whose heads sit in
-// lanes 0..n-1 (list `lane` read through get(lane, pos)); lane k ends with
-// the k-th best entry.  Lanes >= n hold the sentinel (-inf, INT_MAX), which
-// ranks after every real entry.  Each list lane also holds the entry after
-// its head, read one round early, so a round never waits on get().
-template <typename Get>
-__device__ __forceinline__ void merge_sorted_lists(int n, int K, int lane, Get get, float& out_v, int& out_i) {
-    int pos = 0;
-    float hv = -INFINITY, nv = -INFINITY;
-    int hi = 0x7FFFFFFF, ni = 0x7FFFFFFF;
-    if (lane < n) {
-        get(lane, 0, hv, hi);
-        if (K > 1) get(lane, 1, nv, ni);
+// Top-K of up to NL sorted lists, by a truncating bitonic merge inside one
+// wave.  Each list (value desc, index asc; K <= KP entries, KP a power of two
+// <= 32, read through get(list, pos, v, i)) is padded to KP entries with the
+// sentinel (-inf, INT_MAX), which ranks after every real entry, and lists are
+// packed 64 / KP to a register (register r, lane l: list (64 r + l) / KP,
+// position (64 r + l) % KP).
+//   - Two registers A and B merge lane by lane: A keeps the better of A[l] and
+//     B[l ^ (KP - 1)], B reversed within each KP-block.  Each block then holds
+//     the KP best of its two lists as a bitonic sequence.
+//   - Within a register, blocks merge in pairs at distance 1, 2, 4, ... blocks:
+//     lane l and lane l ^ (2^t KP - 1) both keep the better, so both blocks of
+//     a pair hold the KP best (one reversed), and the next level's mirror meets
+//     the right partner.
+//   - After every merge, half-cleaners at lane distances KP/2, ..., 1 (the
+//     lower lane keeps the better) sort every block.
+// Lane k < K ends with the k-th best entry of all lists.
+template <int S>
+__device__ __forceinline__ void keep_better(float& v, int& i, int lane) {  // both lanes keep the better
+    const float ov = lane_xor<S>(v, lane);
+    const int oi = lane_xor<S>(i, lane);
+    const bool t = ahead_of(ov, oi, v, i);
+    v = t ? ov : v;
+    i = t ? oi : i;
+}
+
+template <int S>
+__device__ __forceinline__ void half_clean(float& v, int& i, int lane) {  // lower lane keeps the better
+    const float ov = lane_xor<S>(v, lane);
+    const int oi = lane_xor<S>(i, lane);
+    const bool t = ahead_of(ov, oi, v, i) != ((lane & S) != 0);
+    v = t ? ov : v;
+    i = t ? oi : i;
+}
+
+template <int KP>
+__device__ __forceinline__ void sort_blocks(float& v, int& i, int lane) {
+    if constexpr (KP >= 32) half_clean<16>(v, i, lane);
+    if constexpr (KP >= 16) half_clean<8>(v, i, lane);
+    if constexpr (KP >= 8) half_clean<4>(v, i, lane);
+    if constexpr (KP >= 4) half_clean<2>(v, i, lane);
+    if constexpr (KP >= 2) half_clean<1>(v, i, lane);
+}
+
+template <int KP, int B, int SPAN>
+__device__ __forceinline__ void merge_blocks(float& v, int& i, int lane) {
+    if constexpr (B <= 64 && B / 2 < SPAN) {
+        keep_better<B - 1>(v, i, lane);
+        sort_blocks<KP>(v, i, lane);
+        merge_blocks<KP, 2 * B, SPAN>(v, i, lane);
     }
-    out_v = -INFINITY;
-    out_i = 0x7FFFFFFF;
-    for (int k = 0; k < K; ++k) {
-        float bv = hv;
-        int bi = hi;
-        float ov = dpp<kDppXor1>(bv);
-        int oi = dpp<kDppXor1>(bi);
-        bool t = ahead_of(ov, oi, bv, bi);
-        bv = t ? ov : bv;
-        bi = t ? oi : bi;
-        ov = dpp<kDppXor2>(bv);
-        oi = dpp<kDppXor2>(bi);
-        t = ahead_of(ov, oi, bv, bi);
-        bv = t ? ov : bv;
-        bi = t ? oi : bi;
-        ov = dpp<kDppHalfMirror>(bv);
-        oi = dpp<kDppHalfMirror>(bi);
-        t = ahead_of(ov, oi, bv, bi);
-        bv = t ? ov : bv;
-        bi = t ? oi : bi;
-        ov = dpp<kDppMirror>(bv);
-        oi = dpp<kDppMirror>(bi);
-        t = ahead_of(ov, oi, bv, bi);
-        bv = t ? ov : bv;
-        bi = t ? oi : bi;
-        bv = readlane(bv, 0);
-        bi = readlane(bi, 0);
-        if (lane == k) {
-            out_v = bv;
-            out_i = bi;
-        }
-        // the winning list (indices are distinct) advances
-        if (lane < n && hi == bi) {
-            ++pos;
-            hv = nv;
-            hi = ni;
-            if (pos + 1 < K) {
-                get(lane, pos + 1, nv, ni);
-            } else {
-                nv = -INFINITY;
-                ni = 0x7FFFFFFF;
-            }
+}
+
+template <int KP, int NL, typename Get>
+__device__ __forceinline__ void bitonic_topk(int n, int K, int lane, Get get, float& out_v, int& out_i) {
+    constexpr int NREG = NL * KP > 64 ? NL * KP / 64 : 1;
+    static_assert((NL & (NL - 1)) == 0 && NL * KP <= 64 * 8, "NL a power of two");
+    float v[NREG];
+    int ix[NREG];
+#pragma unroll
+    for (int r = 0; r < NREG; ++r) {
+        const int e = r * 64 + lane;
+        const int list = e / KP, pos = e % KP;
+        v[r] = -INFINITY;
+        ix[r] = 0x7FFFFFFF;
+        if ((list < n) & (pos < K)) get(list, pos, v[r], ix[r]);
+    }
+#pragma unroll
+    for (int half = NREG / 2; half >= 1; half /= 2) {
+#pragma unroll
+        for (int r = 0; r < half; ++r) {
+            const float bv = lane_xor<KP - 1>(v[r + half], lane);
+            const int bi = lane_xor<KP - 1>(ix[r + half], lane);
+            const bool t = ahead_of(bv, bi, v[r], ix[r]);
+            v[r] = t ? bv : v[r];
+            ix[r] = t ? bi : ix[r];
+            sort_blocks<KP>(v[r], ix[r], lane);
         }
     }
+    // lists still spread over blocks of register 0: NL * KP lanes, at most 64
+    merge_blocks<KP, 2 * KP, (NL * KP < 64 ? NL * KP : 64)>(v[0], ix[0], lane);
+    out_v = v[0];
+    out_i = ix[0];
+}
+
+template <int NL, typename Get>
+__device__ __forceinline__ void topk_of_lists(int n, int K, int lane, Get get, float& out_v, int& out_i) {
+    if (K <= 1) bitonic_topk<1, NL>(n, K, lane, get, out_v, out_i);
+    else if (K <= 2) bitonic_topk<2, NL>(n, K, lane, get, out_v, out_i);
+    else if (K <= 4) bitonic_topk<4, NL>(n, K, lane, get, out_v, out_i);
+    else if (K <= 8) bitonic_topk<8, NL>(n, K, lane, get, out_v, out_i);
+    else if (K <= 16) bitonic_topk<16, NL>(n, K, lane, get, out_v, out_i);
+    else bitonic_topk<32, NL>(n, K, lane, get, out_v, out_i);
 }
 
 // SPLIT = false: one workgroup per row, results written directly.
@@ -582,7 +616,7 @@ template <int W, int U, bool ALIGNED, bool SPLIT>
 __global__ void __launch_bounds__(W * 64)
     k_topk(const float* in, float* probs, int* idx, int64_t rows, int cols, int K, int S, State* ws_state,
            TopkEntry* ws_list) {
-    static_assert(W <= 16, "the final selection runs inside one 16-lane DPP row");
+    static_assert(W == 4 || W == 8 || W == 16, "the final merge packs W lists of up to 32 entries into 8 registers");
     constexpr int BLOCK = W * 64;
     constexpr int VEC = 4;
     constexpr int STEP = BLOCK * U;
@@ -721,7 +755,7 @@ __global__ void __launch_bounds__(W * 64)
             for (int ww = 1; ww < W; ++ww) t = oplus(t, s_md[ww]);
             float out_v;
             int out_i;
-            merge_sorted_lists(
+            topk_of_lists<W>(
                 W, K, lane, [&](int l, int p, float& v, int& i) { v = s_val[l][p]; i = s_idx[l][p]; }, out_v,
                 out_i);
             if constexpr (!SPLIT) {
@@ -738,8 +772,8 @@ __global__ void __launch_bounds__(W * 64)
 }
 
 // Second launch of the split top-K: one wavefront per row folds the S slice
-// states with (+) in slice order and merges the S sorted lists (16-lane
-// argmax rounds), then writes the K probabilities and indices.
+// states with (+) in slice order and merges the S sorted lists (bitonic, as
+// above), then writes the K probabilities and indices.
 __global__ void __launch_bounds__(256)
     k_topk_merge(float* probs, int* idx, int64_t rows, int K, int S, const State* ws_state,
                  const TopkEntry* ws_list) {
@@ -751,7 +785,7 @@ __global__ void __launch_bounds__(256)
     for (int q = 1; q < S; ++q) r = oplus(r, ws_state[u0 + q]);
     float out_v;
     int out_i;
-    merge_sorted_lists(
+    topk_of_lists<kTopKMaxSplits>(
         S, K, lane,
         [&](int l, int p, float& v, int& i) {
             const TopkEntry e = ws_list[(u0 + l) * K + p];
