@@ -69,6 +69,8 @@ extern "C" {
 
 /* most workgroups one row may be split over in os_softmax_topk_split */
 #define OS_TOPK_MAX_SPLITS 16
+/* most workgroups one row may be split over in os_softmax_forward_split */
+#define OS_FWD_MAX_SPLITS 256
 
 /* largest row length (columns) accepted by every entry point: 2^28 */
 #define OS_MAX_COLS (1LL << 28)
@@ -138,6 +140,34 @@ int os_softmax_stats(const void *in, float *m, float *d, int64_t rows, int64_t c
  */
 int os_softmax_forward_lse(const void *in, void *out, float *lse, int64_t rows, int64_t cols, int dtype,
                            void *stream);
+
+/*
+ * The forward with each row split over `splits` workgroups, for batches with
+ * too few rows to occupy the GPU (the paper summary, section 3.3: (+) lets any
+ * partition of a row be folded separately and merged; "5.2 Hiện thực và tối ưu
+ * CUDA Online Softmax", section 7.1, on several blocks per row).  Two launches
+ * on `stream`: each slice folds its (m, d) into the workspace, then each slice
+ * merges its row's states in a fixed order and writes its part of y.  The
+ * input is read twice and y written once.
+ *   in, out, rows, cols, dtype   as os_softmax_forward (in == out allowed).
+ *   splits      1..OS_FWD_MAX_SPLITS (1 = os_softmax_forward; workspace unused).
+ *   workspace   device memory of at least
+ *               os_softmax_forward_workspace_bytes(rows, splits) bytes, 8-byte
+ *               aligned, owned by the caller; no initialisation needed.  It is
+ *               in use until the second launch completes: calls that overlap
+ *               on other streams need workspaces of their own.
+ *   Returns OS_OK, OS_EINVAL (bad splits, missing, misaligned or short
+ *   workspace, or as for the forward), or OS_ELAUNCH.
+ */
+int os_softmax_forward_split(const void *in, void *out, int64_t rows, int64_t cols, int dtype, int splits,
+                             void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes os_softmax_forward_split needs (0 for splits == 1), or
+ * OS_EINVAL for rows < 0 or splits outside 1..OS_FWD_MAX_SPLITS.  Host only. */
+int64_t os_softmax_forward_workspace_bytes(int64_t rows, int splits);
+
+/* Suggested `splits` for a forward batch (1 = no split).  Host only. */
+int os_forward_split_plan(int64_t rows, int64_t cols, int dtype);
 
 /*
  * Fused softmax + top-K in one read of the input (paper summary, section 4):

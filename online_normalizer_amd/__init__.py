@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
   os_softmax_forward(x, out=None)              y = softmax(x) over the last dim
   os_softmax_forward_tuned(x, lanes_per_row, vecs_per_lane, grid_blocks=0, out=None)
   os_softmax_stats(x) -> (m, d)                per-row normaliser state
+  os_softmax_forward_lse(x, out=None, write_y=True) -> (y, lse)   y and the per-row logsumexp
+  os_softmax_forward_split(x, splits=None, out=None, workspace=None)   rows split over workgroups
+  os_softmax_forward_workspace_bytes(rows, splits), os_forward_split_plan(rows, cols, dtype)
   os_softmax_topk(x, K, splits=None) -> (probs, idx)   fused softmax + top-K
   os_softmax_topk_split(x, K, splits, workspace) -> (probs, idx)
   os_softmax_topk_workspace_bytes(rows, K, splits), os_topk_plan(rows, cols, K)
@@ -34,6 +37,7 @@ __all__ = [
     "os_softmax_forward", "os_softmax_forward_tuned", "os_softmax_stats", "os_softmax_forward_lse", "os_softmax_topk",
     "safe_softmax_forward", "os_device_copy", "os_forward_plan", "os_last_error", "os_version",
     "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan",
+    "os_softmax_forward_split", "os_softmax_forward_workspace_bytes", "os_forward_split_plan",
 ]
 
 OS_OK, OS_EINVAL, OS_EUNSUPPORTED, OS_ELAUNCH = 0, -1, -2, -3
@@ -78,6 +82,8 @@ def _load() -> ctypes.CDLL:
         "os_forward_plan": [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
         "os_softmax_stats": [vp, vp, vp, i64, i64, i32, vp],
         "os_softmax_forward_lse": [vp, vp, vp, i64, i64, i32, vp],
+        "os_softmax_forward_split": [vp, vp, i64, i64, i32, i32, vp, i64, vp],
+        "os_forward_split_plan": [i64, i64, i32],
         "os_softmax_topk": [vp, vp, vp, i64, i64, i32, vp],
         "safe_softmax_forward": [vp, vp, i64, i64, i32, vp],
         "os_device_copy": [vp, vp, i64, vp],
@@ -91,6 +97,8 @@ def _load() -> ctypes.CDLL:
         fn.restype = i32
     L.os_softmax_topk_workspace_bytes.argtypes = [i64, i32, i32]
     L.os_softmax_topk_workspace_bytes.restype = i64
+    L.os_softmax_forward_workspace_bytes.argtypes = [i64, i32]
+    L.os_softmax_forward_workspace_bytes.restype = i64
     L.os_last_error.argtypes = []
     L.os_last_error.restype = ctypes.c_char_p
     return L
@@ -215,17 +223,17 @@ def os_softmax_topk_workspace_bytes(rows: int, K: int, splits: int) -> int:
     return n
 
 
-# Split top-K workspaces, one per (device, stream) (calls on one stream run
-# in order, so they can share it).
-_TOPK_WS: dict[tuple[int, int], torch.Tensor] = {}
+# Workspaces of the split launches (top-K and forward), one per (device,
+# stream): calls on one stream run in order, so they can share it.
+_SPLIT_WS: dict[tuple[int, int], torch.Tensor] = {}
 
 
-def _topk_workspace(x: torch.Tensor, nbytes: int) -> torch.Tensor:
+def _split_workspace(x: torch.Tensor, nbytes: int) -> torch.Tensor:
     key = (x.device.index, _stream(x))
-    ws = _TOPK_WS.get(key)
+    ws = _SPLIT_WS.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
-        _TOPK_WS[key] = ws
+        _SPLIT_WS[key] = ws
     return ws
 
 
@@ -259,8 +267,37 @@ def os_softmax_topk(x: torch.Tensor, K: int, splits: int | None = None) -> tuple
         _check("os_softmax_topk",
                lib().os_softmax_topk(x.data_ptr(), probs.data_ptr(), idx.data_ptr(), rows, cols, K, _stream(x)))
         return probs, idx
-    ws = _topk_workspace(x, os_softmax_topk_workspace_bytes(rows, K, splits))
+    ws = _split_workspace(x, os_softmax_topk_workspace_bytes(rows, K, splits))
     return os_softmax_topk_split(x, K, splits, ws)
+
+
+def os_forward_split_plan(rows: int, cols: int, dtype: torch.dtype = torch.float32) -> int:
+    return lib().os_forward_split_plan(rows, cols, OS_BF16 if dtype == torch.bfloat16 else OS_F32)
+
+
+def os_softmax_forward_workspace_bytes(rows: int, splits: int) -> int:
+    n = lib().os_softmax_forward_workspace_bytes(rows, splits)
+    if n < 0:
+        raise OnlineSoftmaxError("os_softmax_forward_workspace_bytes", n, os_last_error())
+    return n
+
+
+def os_softmax_forward_split(x: torch.Tensor, splits: int | None = None, out: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The forward with each row split over several workgroups.  splits=None
+    asks the library's plan; without a workspace one cached per (device,
+    stream) is used."""
+    rows, cols = _rows_cols(x)
+    out = _out_like(x, out)
+    if splits is None:
+        splits = os_forward_split_plan(rows, cols, x.dtype)
+    if workspace is None:
+        workspace = _split_workspace(x, os_softmax_forward_workspace_bytes(rows, splits))
+    _check("os_softmax_forward_split",
+           lib().os_softmax_forward_split(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), splits,
+                                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                          _stream(x)))
+    return out
 
 
 def safe_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

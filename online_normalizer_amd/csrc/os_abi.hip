@@ -197,6 +197,31 @@ SafeKernel safe_kernel(int w, int dtype, bool al) {
     return safe_kernel_w<16>(dtype, al);
 }
 
+typedef void (*SplitFoldKernel)(const void*, State*, int64_t, int, int);
+typedef void (*SplitNormKernel)(const void*, void*, const State*, int64_t, int, int);
+
+template <int W>
+SplitFoldKernel split_fold_w(int dtype, bool al) {
+    if (dtype == OS_BF16) return al ? k_split_fold<true, W, kStreamU, true> : k_split_fold<true, W, kStreamU, false>;
+    return al ? k_split_fold<false, W, kStreamU, true> : k_split_fold<false, W, kStreamU, false>;
+}
+
+template <int W>
+SplitNormKernel split_norm_w(int dtype, bool al) {
+    if (dtype == OS_BF16) return al ? k_split_norm<true, W, kStreamU, true> : k_split_norm<true, W, kStreamU, false>;
+    return al ? k_split_norm<false, W, kStreamU, true> : k_split_norm<false, W, kStreamU, false>;
+}
+
+// Waves per workgroup for a slice of `vecs` 16-byte vectors: the most waves
+// whose one tile (waves * 64 lanes * kStreamU vectors) the slice fills, so no
+// lane idles through a partly filled tile.
+int slice_waves(int64_t vecs) {
+    if (vecs >= 16 * 64 * kStreamU) return 16;
+    if (vecs >= 8 * 64 * kStreamU) return 8;
+    if (vecs >= 4 * 64 * kStreamU) return 4;
+    return 1;
+}
+
 // A launch may hold at most 2^32 - 1 threads in total; stay below 2^31.
 int grid_for(int64_t groups, int block, int requested) {
     const int64_t max_grid = (int64_t(1) << 31) / block;
@@ -309,6 +334,75 @@ int os_softmax_forward_lse(const void* in, void* out, float* lse, int64_t rows, 
     auto_plan(cols, dtype, &lpr, &vpl);
     return run_rows(fn, cols == 0 ? nullptr : in, cols == 0 ? nullptr : out, RowStats{nullptr, nullptr, lse}, rows,
                     cols, dtype, lpr, vpl, 0, stream);
+}
+
+int64_t os_softmax_forward_workspace_bytes(int64_t rows, int splits) {
+    if (rows < 0 || splits < 1 || splits > OS_FWD_MAX_SPLITS) {
+        fail(OS_EINVAL, "os_softmax_forward_workspace_bytes: bad rows or splits");
+        return OS_EINVAL;
+    }
+    ok();
+    return splits == 1 ? 0 : rows * splits * static_cast<int64_t>(sizeof(State));
+}
+
+int os_forward_split_plan(int64_t rows, int64_t cols, int dtype) {
+    if (rows <= 0 || cols <= 0 || cols > OS_MAX_COLS || (dtype != OS_F32 && dtype != OS_BF16)) return 1;
+    // Rows that fit the register-resident kernels are read once and are not
+    // split (the second launch and read cost more than idle CUs on every
+    // batch measured).  Longer rows are split into the most slices that keep
+    // the batch at <= 256 workgroups (one per CU) and every slice >= 1024
+    // vectors (16 KB) (measured on MI355X over 1..256 rows of 128256 to 2^24
+    // columns, fp32 and bf16).
+    int lpr = 0, vpl = 0;
+    auto_plan(cols, dtype, &lpr, &vpl);
+    if (lpr != 0) return 1;
+    const int64_t vecs = vectors_needed(cols, dtype);
+    int S = 1;
+    while (S < OS_FWD_MAX_SPLITS && rows * S * 2 <= 256 && vecs / (S * 2) >= 1024) S *= 2;
+    return S;
+}
+
+int os_softmax_forward_split(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int splits,
+                             void* workspace, int64_t workspace_bytes, void* stream) {
+    const char* fn = "os_softmax_forward_split";
+    if (splits < 1 || splits > OS_FWD_MAX_SPLITS)
+        return fail(OS_EINVAL, "%s: splits=%d outside [1, %d]", fn, splits, OS_FWD_MAX_SPLITS);
+    int rc = check_problem(fn, in, out, true, rows, cols, dtype);
+    if (rc == 1) return ok();
+    if (rc != OS_OK) return rc;
+    if (splits == 1) {
+        int lpr = 0, vpl = 0;
+        auto_plan(cols, dtype, &lpr, &vpl);
+        return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, stream);
+    }
+    const int64_t need = rows * splits * static_cast<int64_t>(sizeof(State));
+    if (workspace == nullptr) return fail(OS_EINVAL, "%s: splits > 1 needs a workspace", fn);
+    if (!aligned(workspace, 8)) return fail(OS_EINVAL, "%s: workspace must be 8-byte aligned", fn);
+    if (workspace_bytes < need)
+        return fail(OS_EINVAL, "%s: workspace has %lld bytes, needs %lld", fn, (long long)workspace_bytes,
+                    (long long)need);
+    const bool al = vector_ok(in, out, cols, dtype);
+    const int64_t seg_vec = (vectors_needed(cols, dtype) + splits - 1) / splits;
+    const int w = slice_waves(seg_vec);
+    const int block = w * 64;
+    const int64_t units = rows * splits;
+    const int grid = grid_for(units, block, 0);
+    State* states = static_cast<State*>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const SplitFoldKernel kf = w == 1   ? split_fold_w<1>(dtype, al)
+                               : w == 4 ? split_fold_w<4>(dtype, al)
+                               : w == 8 ? split_fold_w<8>(dtype, al)
+                                        : split_fold_w<16>(dtype, al);
+    const SplitNormKernel kn = w == 1   ? split_norm_w<1>(dtype, al)
+                               : w == 4 ? split_norm_w<4>(dtype, al)
+                               : w == 8 ? split_norm_w<8>(dtype, al)
+                                        : split_norm_w<16>(dtype, al);
+    hipLaunchKernelGGL(kf, dim3(grid), dim3(block), 0, st, in, states, rows, static_cast<int>(cols), splits);
+    rc = launched(fn);
+    if (rc != OS_OK) return rc;
+    hipLaunchKernelGGL(kn, dim3(grid), dim3(block), 0, st, in, out, states, rows, static_cast<int>(cols), splits);
+    return launched(fn);
 }
 
 int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {

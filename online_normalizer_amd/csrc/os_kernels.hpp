@@ -427,6 +427,135 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
 }
 
 // ---------------------------------------------------------------------------
+// Split-row forward for batches with too few rows to fill the chip: S
+// workgroups per row, each over a contiguous slice of the row's vector slots,
+// in two launches (the launch boundary orders the phases):
+//   k_split_fold   workgroup (row, s) folds its slice into (m, d) (the tile form
+//                  of the recurrence, merged with (+) across lanes and waves)
+//                  and writes it to ws[row * S + s];
+//   k_split_norm   workgroup (row, s) merges the row's S states with (+) in a
+//                  fixed order (so every slice of a row uses the same bits),
+//                  re-reads its slice and writes y = e^{x - m} / d.
+// Each slice's buffer resource ends with the slice, so loads past its end
+// touch no memory and stores past it are dropped.
+// ---------------------------------------------------------------------------
+struct Slice {
+    int v0, v1;       // vector slots [v0, v1) of the row
+    uint32_t bytes;   // bytes of the row from its start to the end of the slice
+};
+
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ Slice slice_of(int seg, int S, int cols) {
+    using E = Elt<BF16>;
+    const int nvec = vec_count<BF16, ALIGNED>(cols);
+    const int seg_vec = (nvec + S - 1) / S;
+    const int v0 = seg * seg_vec < nvec ? seg * seg_vec : nvec;
+    const int v1 = v0 + seg_vec < nvec ? v0 + seg_vec : nvec;
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    const uint32_t end = static_cast<uint32_t>(v1) * static_cast<uint32_t>(E::kVec * E::kSize);
+    return Slice{v0, v1, end < row_bytes ? end : row_bytes};
+}
+
+// U slots per lane from slot `base`: lane tid reads slots base + u * BLOCK + tid;
+// slots at or past v1 become -inf.
+template <bool BF16, int BLOCK, int U, bool ALIGNED, bool STREAM>
+__device__ __forceinline__ void load_tile(const Buf& b, int base, int tid, int v1, int cols,
+                                          float (&x)[U][Elt<BF16>::kVec]) {
+    if constexpr (ALIGNED) {
+        load_slots<BF16, U, true, STREAM>(b, 0u, base + tid, BLOCK, v1, cols, true, x);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int slot = base + u * BLOCK + tid;
+            load_slot<BF16, false, STREAM>(b, 0u, slot, v1, cols, slot < v1, x[u]);
+        }
+    }
+}
+
+template <bool BF16, int W, int U, bool ALIGNED>
+__global__ void __launch_bounds__(W * 64)
+    k_split_fold(const void* in, State* ws, int64_t rows, int cols, int S) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    constexpr int BLOCK = W * 64;
+    __shared__ State lds[2][W];
+    const int tid = threadIdx.x;
+    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
+    const int64_t units = rows * S;
+    int par = 0;
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t row = unit / S;
+        const Slice sl = slice_of<BF16, ALIGNED>(static_cast<int>(unit - row * S), S, cols);
+        const Buf bin(static_cast<const char*>(in) + row * row_bytes, sl.bytes);
+        float ml = kFloor, dl = 0.0f;
+        for (int base = sl.v0; base < sl.v1; base += BLOCK * U) {
+            float x[U][VEC];
+            load_tile<BF16, BLOCK, U, ALIGNED, false>(bin, base, tid, sl.v1, cols, x);
+            float mc = kFloor;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) mc = fmaxf(mc, x[u][k]);
+            const float mn = fmaxf(ml, mc);
+            float acc = dl * exp_e(ml - mn);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc += exp_e(x[u][k] - mn);
+            dl = acc;
+            ml = mn;
+        }
+        State st = group_merge<64>(State{ml, dl});
+        if constexpr (W > 1) {
+            if ((tid & (kWave - 1)) == 0) lds[par][tid / kWave] = st;
+            __syncthreads();
+            st = lds[par][0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) st = oplus(st, lds[par][w]);
+            par ^= 1;
+        }
+        if (tid == 0) ws[unit] = st;
+    }
+}
+
+template <bool BF16, int W, int U, bool ALIGNED>
+__global__ void __launch_bounds__(W * 64)
+    k_split_norm(const void* in, void* out, const State* ws, int64_t rows, int cols, int S) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    constexpr int BLOCK = W * 64;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
+    const int64_t units = rows * S;
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t row = unit / S;
+        const Slice sl = slice_of<BF16, ALIGNED>(static_cast<int>(unit - row * S), S, cols);
+        // the row's S slice states: lane l folds states l, l + 64, ... in
+        // order, then the wave merges the 64 lane states (same bits in every
+        // lane, and in every workgroup of the row)
+        State t{kFloor, 0.0f};
+        for (int q = lane; q < S; q += kWave) t = oplus(t, ws[row * S + q]);
+        t = group_merge<64>(t);
+        const float m = t.m;
+        const float inv_d = rcp(t.d);
+        const Buf bin(static_cast<const char*>(in) + row * row_bytes, sl.bytes);
+        const Buf bout(static_cast<char*>(out) + row * row_bytes, sl.bytes);
+        for (int base = sl.v0; base < sl.v1; base += BLOCK * U) {
+            float x[U][VEC];
+            load_tile<BF16, BLOCK, U, ALIGNED, true>(bin, base, tid, sl.v1, cols, x);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int slot = base + u * BLOCK + tid;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - m) * inv_d;
+                store_slot<BF16, ALIGNED>(bout, 0u, slot, sl.v1, cols, slot < sl.v1, x[u]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fused softmax + top-K (paper summary, section 4), one read of the input.
 //
 // One W-wave workgroup per row.  Every lane folds (m, d) over its slots as in

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["os_softmax_forward", "os_softmax_topk", "safe_softmax_forward", "os_softmax_stats",
-              "os_softmax_forward_lse", "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
+              "os_softmax_forward_lse", "os_softmax_forward_split", "os_softmax_forward_workspace_bytes",
+              "os_forward_split_plan", "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
         assert n in names
 
 
@@ -150,6 +151,35 @@ def test_topk_split_validation(L, ons):
     assert ons.os_topk_plan(16, 1000, 8) == 1
     assert ons.os_topk_plan(64, 32000, 8) == 1
     assert ons.os_topk_plan(16, 1 << 20, 8) == 8
+
+
+def test_forward_split_validation(L, ons):
+    assert ons.os_softmax_forward_workspace_bytes(10, 1) == 0
+    need = ons.os_softmax_forward_workspace_bytes(10, 4)
+    assert need == 10 * 4 * 8
+    with pytest.raises(ons.OnlineSoftmaxError):
+        ons.os_softmax_forward_workspace_bytes(10, 257)
+    with pytest.raises(ons.OnlineSoftmaxError):
+        ons.os_softmax_forward_workspace_bytes(-1, 2)
+    f = L.os_softmax_forward_split
+    assert f(FAKE, FAKE, 10, 1000, F32, 0, FAKE, need, None) == EINVAL       # splits < 1
+    assert f(FAKE, FAKE, 10, 1000, F32, 257, FAKE, need, None) == EINVAL     # splits > 256
+    assert f(FAKE, FAKE, 10, 1000, F32, 4, None, need, None) == EINVAL       # no workspace
+    assert f(FAKE, FAKE, 10, 1000, F32, 4, FAKE, need - 1, None) == EINVAL   # short workspace
+    assert f(FAKE, FAKE, 10, 1000, F32, 4, FAKE + 4, need, None) == EINVAL   # misaligned workspace
+    assert f(FAKE, None, 10, 1000, F32, 4, FAKE, need, None) == EINVAL       # no output
+    assert f(FAKE, FAKE, 10, 1000, 5, 4, FAKE, need, None) == EINVAL         # unknown dtype
+    assert f(None, None, 0, 1000, F32, 4, None, 0, None) == 0                # empty
+    assert ons.os_forward_split_plan(4096, 32000) == 1
+    assert ons.os_forward_split_plan(16, 32000) == 1      # register-resident rows are never split
+    assert ons.os_forward_split_plan(64, 1000) == 1
+    assert ons.os_forward_split_plan(0, 1000) == 1
+    assert ons.os_forward_split_plan(16, 1 << 20) == 16   # <= 256 workgroups
+    assert ons.os_forward_split_plan(1, 1 << 24) == 256
+    assert ons.os_forward_split_plan(1, 1 << 20) == 256   # slices of 1024 vectors
+    assert ons.os_forward_split_plan(16, 128256) == 16
+    assert ons.os_forward_split_plan(64, 128256) == 4
+    assert ons.os_forward_split_plan(256, 128256) == 1
 
 
 def test_copy_validation(L):

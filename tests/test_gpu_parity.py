@@ -232,7 +232,7 @@ def test_deterministic(ons):
 
 
 def test_graph_replays_match_eager(ons):
-    """The forward, the baseline and the top-K captured in a HIP graph: every
+    """The forward, the baseline, the top-K and the split forward captured in a HIP graph: every
     replay, with eager work and synchronisations between replays, equals the
     eager result bit for bit."""
     x = to_device(workloads.config(2, 0, 512))
@@ -241,19 +241,25 @@ def test_graph_replays_match_eager(ons):
     y_ref = ons.os_softmax_forward(x)
     s_ref = ons.safe_softmax_forward(x)
     p_ref, i_ref = ons.os_softmax_topk(xt, 8)
+    xs = to_device(workloads.normal(4, 100003, seed=9, scale=3.0))
+    ws = torch.empty(ons.os_softmax_forward_workspace_bytes(4, 8), dtype=torch.uint8, device="cuda")
+    sp_ref = ons.os_softmax_forward_split(xs, splits=8, workspace=ws)
     torch.cuda.synchronize()
     y = torch.empty_like(x)
     s3 = torch.empty_like(x)
+    sp = torch.empty_like(xs)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         ons.os_softmax_forward(x, out=y)
         ons.safe_softmax_forward(x, out=s3)
         p, i = ons.os_softmax_topk(xt, 8)
+        ons.os_softmax_forward_split(xs, splits=8, out=sp, workspace=ws)
     for rep in range(4):
         y.zero_()
         s3.zero_()
         p.zero_()
         i.zero_()
+        sp.zero_()
         junk = ons.os_softmax_forward(torch.randn(64, 1000, device="cuda"))  # eager work between replays
         torch.cuda.synchronize()
         say(f"graph replay {rep}")
@@ -262,6 +268,7 @@ def test_graph_replays_match_eager(ons):
         assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), rep
         assert torch.equal(s3.view(torch.int32), s_ref.view(torch.int32)), rep
         assert torch.equal(p, p_ref) and torch.equal(i, i_ref), rep
+        assert torch.equal(sp.view(torch.int32), sp_ref.view(torch.int32)), rep
         del junk
 
 
@@ -284,6 +291,66 @@ def test_stats_invariants(ons, orc):
     mo, do = orc.stats(xb)
     assert np.array_equal(to_host(m).astype(np.float64), mo)
     assert np.max(np.abs(to_host(d) - do) / do) <= 1e-5
+
+
+# -- split-row forward ---------------------------------------------------------------
+
+def run_split(ons, x: np.ndarray, splits, ws=None):
+    xd = to_device(x)
+    y = ons.os_softmax_forward_split(xd, splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_split_forward(ons, orc, bf16):
+    """Slices of every size class, ragged last slices, more slices than vectors
+    (empty trailing slices), unaligned rows, and splits 1..256."""
+    cases = [(3, 1, 4), (5, 7, 16), (4, 100, 3), (7, 4096, 2), (3, 4097, 5), (2, 32000, 16), (5, 32003, 7),
+             (3, 65536, 8), (2, 200001, 16), (2, 1 << 20, 16), (1, 1 << 20, 3), (2, 300007, 100),
+             (1, 1 << 20, 256), (2, 5000, 256)]
+    for rows, cols, S in cases:
+        say(f"split forward bf16={bf16} rows={rows} cols={cols} S={S}")
+        x32 = workloads.normal(rows, cols, seed=cols + S, scale=3.0)
+        x32[0, cols - 1] = 60.0
+        x = bf16_bits(x32) if bf16 else x32
+        assert_parity(run_split(ons, x, S), orc.softmax(x), bf16, f"split rows={rows} cols={cols} S={S}")
+
+
+def test_split_forward_plan_and_specials(ons, orc):
+    """The planned split on a small batch of long rows; special-value rows; in place; determinism."""
+    x = workloads.normal(8, 70000, seed=5, scale=2.0)
+    x[0, ::3] = -np.inf
+    x[1, :] = -np.inf
+    x[2, 50000] = np.inf
+    x[3, 69999] = np.nan
+    x[4, 0] = 80.0
+    x[4, 69999] = 80.0
+    x[5, :] = -np.inf
+    x[5, 12345] = -3.0e38
+    S = ons.os_forward_split_plan(8, 70000)
+    say(f"split specials S={S}")
+    assert S > 1
+    ref = orc.softmax(x)
+    assert_fp32_parity(run_split(ons, x, None), ref, "split specials (plan)")
+    for S in (2, 16):
+        assert_fp32_parity(run_split(ons, x, S), ref, f"split specials S={S}")
+    xd = to_device(x)
+    y1 = ons.os_softmax_forward_split(xd, splits=8)
+    y2 = ons.os_softmax_forward_split(xd, splits=8)
+    y3 = ons.os_softmax_forward_split(xd, splits=8, out=xd)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    assert y3.data_ptr() == xd.data_ptr() and torch.equal(xd.view(torch.int32), y1.view(torch.int32))
+
+
+def test_split_forward_reuses_workspace(ons, orc):
+    """A caller workspace filled with junk needs no initialisation; back-to-back calls reuse it."""
+    ws = torch.full((ons.os_softmax_forward_workspace_bytes(4, 64),), 0x7F, dtype=torch.uint8, device="cuda")
+    for cols, S in ((70001, 16), (300000, 64), (90000, 3)):
+        x = workloads.normal(4, cols, seed=cols, scale=2.0)
+        say(f"split workspace reuse cols={cols} S={S}")
+        assert_fp32_parity(run_split(ons, x, S, ws), orc.softmax(x), f"split ws cols={cols}")
 
 
 # -- logsumexp alongside the forward ------------------------------------------------
