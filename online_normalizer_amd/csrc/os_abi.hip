@@ -37,6 +37,11 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int elt_size(int dtype) { return dtype == OS_BF16 ? 2 : 4; }
 
+// Workspaces hold a fixed number of bytes per (row, slice); refuse row counts
+// whose workspace size would not fit in int64 (with room for alignment).
+constexpr int64_t kMaxWorkspaceBytes = int64_t(1) << 60;
+bool workspace_fits(int64_t rows, int64_t bytes_per_row) { return rows <= kMaxWorkspaceBytes / bytes_per_row; }
+
 // Common checks of a [rows, cols] problem.  Returns OS_OK, an error, or 1 for
 // "empty: nothing to do".
 int check_problem(const char* fn, const void* in, const void* out, bool need_out, int64_t rows,
@@ -337,7 +342,8 @@ int os_softmax_forward_lse(const void* in, void* out, float* lse, int64_t rows, 
 }
 
 int64_t os_softmax_forward_workspace_bytes(int64_t rows, int splits) {
-    if (rows < 0 || splits < 1 || splits > OS_FWD_MAX_SPLITS) {
+    if (rows < 0 || splits < 1 || splits > OS_FWD_MAX_SPLITS ||
+        !workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State)))) {
         fail(OS_EINVAL, "os_softmax_forward_workspace_bytes: bad rows or splits");
         return OS_EINVAL;
     }
@@ -375,6 +381,8 @@ int os_softmax_forward_split(const void* in, void* out, int64_t rows, int64_t co
         auto_plan(cols, dtype, &lpr, &vpl);
         return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, stream);
     }
+    if (!workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State))))
+        return fail(OS_EINVAL, "%s: rows * splits overflows the workspace size", fn);
     const int64_t need = rows * splits * static_cast<int64_t>(sizeof(State));
     if (workspace == nullptr) return fail(OS_EINVAL, "%s: splits > 1 needs a workspace", fn);
     if (!aligned(workspace, 8)) return fail(OS_EINVAL, "%s: workspace must be 8-byte aligned", fn);
@@ -523,7 +531,8 @@ int os_softmax_topk(const float* in, float* probs, int32_t* idx, int64_t rows, i
 }
 
 int64_t os_softmax_topk_workspace_bytes(int64_t rows, int K, int splits) {
-    if (rows < 0 || K < 1 || K > OS_TOPK_KMAX || splits < 1 || splits > OS_TOPK_MAX_SPLITS) {
+    if (rows < 0 || K < 1 || K > OS_TOPK_KMAX || splits < 1 || splits > OS_TOPK_MAX_SPLITS ||
+        !workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State) + K * sizeof(TopkEntry)) + 512)) {
         fail(OS_EINVAL, "os_softmax_topk_workspace_bytes: bad rows, K or splits");
         return OS_EINVAL;
     }
@@ -554,6 +563,8 @@ int os_softmax_topk_split(const float* in, float* probs, int32_t* idx, int64_t r
     if (rc == 1) return ok();
     if (rc != OS_OK) return rc;
     if (splits > 1) {
+        if (!workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State) + K * sizeof(TopkEntry)) + 512))
+            return fail(OS_EINVAL, "%s: rows * splits overflows the workspace size", fn);
         if (workspace == nullptr) return fail(OS_EINVAL, "%s: workspace is NULL", fn);
         if (!aligned(workspace, 256)) return fail(OS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
         const int64_t need = topk_workspace(rows, K, splits).bytes;

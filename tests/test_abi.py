@@ -136,6 +136,8 @@ def test_topk_split_validation(L, ons):
     assert need >= 10 * 4 * 8 + 10 * 4 * 8 * 8
     with pytest.raises(ons.OnlineSoftmaxError):
         ons.os_softmax_topk_workspace_bytes(10, 8, 17)
+    with pytest.raises(ons.OnlineSoftmaxError):
+        ons.os_softmax_topk_workspace_bytes(1 << 58, 32, 16)                # size would overflow
     f = L.os_softmax_topk_split
     assert f(FAKE, FAKE, FAKE, 10, 1000, 8, 0, FAKE, need, None) == EINVAL      # splits < 1
     assert f(FAKE, FAKE, FAKE, 10, 1000, 8, 17, FAKE, need, None) == EINVAL     # splits > 16
@@ -161,6 +163,9 @@ def test_forward_split_validation(L, ons):
         ons.os_softmax_forward_workspace_bytes(10, 257)
     with pytest.raises(ons.OnlineSoftmaxError):
         ons.os_softmax_forward_workspace_bytes(-1, 2)
+    with pytest.raises(ons.OnlineSoftmaxError):
+        ons.os_softmax_forward_workspace_bytes(1 << 58, 256)                # size would overflow
+    assert L.os_softmax_forward_split(FAKE, FAKE, 1 << 58, 1, F32, 256, FAKE, 1 << 62, None) == EINVAL
     f = L.os_softmax_forward_split
     assert f(FAKE, FAKE, 10, 1000, F32, 0, FAKE, need, None) == EINVAL       # splits < 1
     assert f(FAKE, FAKE, 10, 1000, F32, 257, FAKE, need, None) == EINVAL     # splits > 256
