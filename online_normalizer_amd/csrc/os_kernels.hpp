@@ -567,6 +567,9 @@ __global__ void __launch_bounds__(W * 64)
 //   - first tile: the workgroup's tile is cut into 64 disjoint parts of W
 //     lanes; the K-th largest of the 64 part maxima is a tile element with
 //     at least K elements at or above it (two barriers, before any insert);
+//   - a quarter of the way through a segment of >= 4 tiles: the same bound
+//     over everything seen so far (each part is then W lanes' slots of every
+//     tile so far, and its maximum the lanes' running maxima);
 //   - then: the K-th entry of the wave's own list, and the largest K-th entry
 //     published by any wave of the workgroup (an LDS atomic max).
 // Survivors (x >= T, so ties at T are kept) are inserted one at a time:
@@ -633,7 +636,8 @@ __device__ __forceinline__ float tile_bound(float mx, int K, int w, int lane, fl
     if (r != 0) __hip_atomic_fetch_add(&s_rank[lane], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __syncthreads();
     const int rank = __hip_atomic_load(&s_rank[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return readlane(a, __builtin_ctzll(__ballot(rank == K - 1)));
+    const uint64_t sel = __ballot(rank == K - 1);
+    return sel != 0 ? readlane(a, __builtin_ctzll(sel)) : -INFINITY;  // sel has one bit (ranks are a permutation)
 }
 
 // One (value, index) entry of a segment's partial top-K list.
@@ -753,7 +757,7 @@ __global__ void __launch_bounds__(W * 64)
     __shared__ int s_idx[W][kTopKMax];
     __shared__ State s_md[W];
     __shared__ float s_sub[64];
-    __shared__ int s_rank[64];
+    __shared__ int s_rank[2][64];  // one per bound: the first tile's, the refresh
     __shared__ int s_thr;
 
     const int tid = threadIdx.x;
@@ -775,14 +779,16 @@ __global__ void __launch_bounds__(W * 64)
         const uint32_t seg_end = static_cast<uint32_t>(v1) * 16u;
         const Buf bin(in + row * static_cast<int64_t>(cols), seg_end < row_bytes ? seg_end : row_bytes);
         if (tid == 0) s_thr = ordered_bits(-INFINITY);
-        if (tid < 64) s_rank[tid] = 0;
+        if (tid < 128) s_rank[tid / 64][tid % 64] = 0;
         __syncthreads();
 
         float ml = kFloor, dl = 0.0f;
         float L = -INFINITY;
         int I = 0x7FFFFFFF;
         float T = -INFINITY;
-        bool first = true;
+        const int ntiles = (v1 - v0 + STEP - 1) / STEP;
+        const int refresh = ntiles >= 4 ? ntiles / 4 : -1;  // tile index of the refreshed bound
+        int t = 0;
 
         // One tile: unpack the raw loads (slots past the segment become
         // -inf), issue the next tile's loads into the same registers, fold
@@ -824,12 +830,16 @@ __global__ void __launch_bounds__(W * 64)
             dl = acc;
             ml = mn;
             // candidates
-            if (first) {
-                // every wave of the workgroup runs the segment's first tile
-                // (v0 < v1 is uniform), so all reach the barriers inside
-                T = tile_bound<W>(mx, K, w, lane, s_sub, s_rank);
-                first = false;
+            // every wave of the workgroup runs every tile of the segment (v0,
+            // v1 and the tile count are uniform), so all reach the barriers
+            // inside tile_bound
+            if (t == 0) {
+                T = tile_bound<W>(mx, K, w, lane, s_sub, s_rank[0]);
+            } else if (t == refresh) {
+                // a lane that has seen no element yet holds kFloor: not an element
+                T = fmaxf(T, tile_bound<W>(ml > kFloor ? ml : -INFINITY, K, w, lane, s_sub, s_rank[1]));
             }
+            ++t;
             T = fmaxf(T, from_ordered_bits(__hip_atomic_load(&s_thr, __ATOMIC_RELAXED,
                                                              __HIP_MEMORY_SCOPE_WORKGROUP)));
             if (__ballot(mx >= T) != 0) {
