@@ -345,6 +345,26 @@ def all_configs(ons, stream):
         entry[name] = {"us": round(tu * 1e6, 2), "fused_speedup": round(tu / t, 2), "us_eager": round(tue * 1e6, 2),
                        "us_flushed": round(tuf * 1e6, 2), "fused_speedup_flushed": round(tuf / tf, 2)}
     table.append(entry)
+    del xt, yt
+
+    # few long rows: one workgroup per row against the planned split (not one
+    # of the five workloads; it shows what the split-row forward is for)
+    for rows, cols in ((16, 1 << 20), (1, 1 << 24)):
+        x = torch.randn(rows, cols, device="cuda", generator=torch.Generator("cuda").manual_seed(rows)) * 3
+        y = torch.empty_like(x)
+        nbytes = rows * cols * 8
+        S = ons.os_forward_split_plan(rows, cols, x.dtype)
+        ws = torch.empty(ons.os_softmax_forward_workspace_bytes(rows, S), dtype=torch.uint8, device="cuda")
+        tu, _ = measure(lambda: ons.os_softmax_forward(x, out=y), 10)
+        ts, _ = measure(lambda: ons.os_softmax_forward_split(x, splits=S, out=y, workspace=ws), 30)
+        tsf = flushed(lambda: ons.os_softmax_forward_split(x, splits=S, out=y, workspace=ws))
+        table.append({"case": "split_forward", "rows": rows, "cols": cols, "dtype": "float32", "splits": S,
+                      "algorithmic_bytes": nbytes,
+                      "unsplit": {"us": round(tu * 1e6, 2), "pct_peak": round(100 * nbytes / tu / 1e9 / PEAK_HBM_GBS, 1)},
+                      "split": {"us": round(ts * 1e6, 2), "pct_peak": round(100 * nbytes / ts / 1e9 / PEAK_HBM_GBS, 1),
+                                "us_flushed": round(tsf * 1e6, 2)},
+                      "speedup": round(tu / ts, 2)})
+        del x, y, ws
     return table
 
 
