@@ -234,6 +234,11 @@ def main(argv=None) -> int:
         _, perc = time_launches(lambda: ons.os_device_copy(x, y), 20, 3, stream)
         ac = sum(perc) / len(perc)
         legs["copy"] = {"kernel_us": round(ac * 1e6, 2), "GBs": round(bytes_alg / ac / 1e9, 2)}
+        # the same copy with the forward's own access pattern (one 1024-lane
+        # workgroup per 128 KB row, all loads before the stores)
+        _, perr = time_launches(lambda: ons.os_device_copy_rows(x, y), 20, 3, stream)
+        ar = sum(perr) / len(perr)
+        legs["copy_row_pattern"] = {"kernel_us": round(ar * 1e6, 2), "GBs": round(bytes_alg / ar / 1e9, 2)}
         # the headline kernel with L2 / Infinity Cache flushed before each launch
         scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         times = []
@@ -250,6 +255,7 @@ def main(argv=None) -> int:
         legs["online_flushed"] = {"kernel_us": round(af * 1e6, 2), "effective_GBs": round(bytes_alg / af / 1e9, 2)}
         legs["speedup_vs_safe_3pass"] = round(a3 / avg, 3)
         legs["pct_of_copy"] = round(100.0 * ac / avg, 2)
+        legs["pct_of_row_pattern_copy"] = round(100.0 * ar / avg, 2)
         out["compare"] = legs
 
     if not args.no_cpu_baseline:

@@ -232,6 +232,17 @@ int safe_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, 
  */
 int os_device_copy(const void *src, void *dst, int64_t bytes, void *stream);
 
+/*
+ * Device copy of `rows` rows of `row_bytes` bytes each with the access pattern
+ * of the register-resident forward on rows up to 128 KiB: one 1024-lane
+ * workgroup per row, eight 16-byte vectors per lane, every load of a row
+ * issued before any of its stores.  A bandwidth reference: the ceiling of that
+ * pattern, next to os_device_copy's (4 KiB tiles, one vector per lane).
+ * row_bytes a multiple of 16 and at most 131072; src and dst 16-byte aligned,
+ * no overlap.  Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_device_copy_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes, void *stream);
+
 /* Message for the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call on the same thread. */
 const char *os_last_error(void);

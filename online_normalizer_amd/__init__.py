@@ -19,6 +19,7 @@ Entry points (same names as the C ABI):
   os_softmax_topk_workspace_bytes(rows, K, splits), os_topk_plan(rows, cols, K)
   safe_softmax_forward(x, out=None)            three-pass baseline
   os_device_copy(src, dst)                     plain copy (bandwidth reference)
+  os_device_copy_rows(src, dst)                copy with the row-per-workgroup pattern (reference)
   os_forward_plan(cols, dtype) -> (lanes_per_row, vecs_per_lane)
   os_last_error(), os_version()
 
@@ -35,7 +36,7 @@ import torch  # loaded first: its HIP runtime is the one the library binds to
 __all__ = [
     "OS_F32", "OS_BF16", "OS_TOPK_KMAX", "OnlineSoftmaxError", "LIB_PATH", "lib",
     "os_softmax_forward", "os_softmax_forward_tuned", "os_softmax_stats", "os_softmax_forward_lse", "os_softmax_topk",
-    "safe_softmax_forward", "os_device_copy", "os_forward_plan", "os_last_error", "os_version",
+    "safe_softmax_forward", "os_device_copy", "os_device_copy_rows", "os_forward_plan", "os_last_error", "os_version",
     "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan",
     "os_softmax_forward_split", "os_softmax_forward_workspace_bytes", "os_forward_split_plan",
 ]
@@ -87,6 +88,7 @@ def _load() -> ctypes.CDLL:
         "os_softmax_topk": [vp, vp, vp, i64, i64, i32, vp],
         "safe_softmax_forward": [vp, vp, i64, i64, i32, vp],
         "os_device_copy": [vp, vp, i64, vp],
+        "os_device_copy_rows": [vp, vp, i64, i64, vp],
         "os_version": [],
         "os_softmax_topk_split": [vp, vp, vp, i64, i64, i32, i32, vp, i64, vp],
         "os_topk_plan": [i64, i64, i32],
@@ -269,6 +271,17 @@ def os_softmax_topk(x: torch.Tensor, K: int, splits: int | None = None) -> tuple
         return probs, idx
     ws = _split_workspace(x, os_softmax_topk_workspace_bytes(rows, K, splits))
     return os_softmax_topk_split(x, K, splits, ws)
+
+
+def os_device_copy_rows(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Copy src (rows x row_bytes, row_bytes <= 128 KiB) with the register-resident
+    forward's access pattern (a bandwidth reference)."""
+    rows, cols = _rows_cols(src)
+    if dst.shape != src.shape or dst.dtype != src.dtype or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous tensor like src")
+    _check("os_device_copy_rows", lib().os_device_copy_rows(src.data_ptr(), dst.data_ptr(), rows,
+                                                            cols * src.element_size(), _stream(src)))
+    return dst
 
 
 def os_forward_split_plan(rows: int, cols: int, dtype: torch.dtype = torch.float32) -> int:

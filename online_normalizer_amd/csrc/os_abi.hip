@@ -592,4 +592,22 @@ int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     return launched(fn);
 }
 
+int os_device_copy_rows(const void* src, void* dst, int64_t rows, int64_t row_bytes, void* stream) {
+    const char* fn = "os_device_copy_rows";
+    if (rows < 0 || row_bytes < 0 || row_bytes % 16 != 0 || row_bytes > 131072)
+        return fail(OS_EINVAL, "%s: row_bytes must be a multiple of 16 in [0, 131072]", fn);
+    if (rows == 0 || row_bytes == 0) return ok();
+    if (rows > INT64_MAX / row_bytes) return fail(OS_EINVAL, "%s: rows * row_bytes overflows", fn);
+    if (src == nullptr || dst == nullptr) return fail(OS_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(OS_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    const int64_t bytes = rows * row_bytes;
+    const char* s = static_cast<const char*>(src);
+    const char* d = static_cast<const char*>(dst);
+    if (s < d + bytes && d < s + bytes) return fail(OS_EINVAL, "%s: source and destination overlap", fn);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_copy_rows, dim3(grid_for(rows, 1024, 0)), dim3(1024), 0, static_cast<hipStream_t>(stream), s,
+                       static_cast<char*>(dst), rows, static_cast<uint32_t>(row_bytes));
+    return launched(fn);
+}
+
 }  // extern "C"

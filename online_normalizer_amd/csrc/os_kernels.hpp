@@ -951,4 +951,24 @@ __global__ void __launch_bounds__(256) k_copy(const char* src, char* dst, int64_
     bd.store16(off, bs.load16<true>(off));
 }
 
+// ---------------------------------------------------------------------------
+// Copy with the register-resident forward's access pattern on rows of up to
+// 128 KiB: one 1024-lane workgroup per row, 8 vectors per lane (slot
+// v * 1024 + lane), every load issued before any store.  It is the bandwidth
+// ceiling of that pattern, the one k_resident<*, 1024, 8> runs at.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) k_copy_rows(const char* src, char* dst, int64_t rows, uint32_t row_bytes) {
+    constexpr int VPL = 8;
+    const uint32_t tid = threadIdx.x;
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const Buf bs(src + row * row_bytes, row_bytes), bd(dst + row * row_bytes, row_bytes);
+        u32x4 v[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) v[i] = bs.load16<true>((i * 1024u + tid) * 16u);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) bd.store16((i * 1024u + tid) * 16u, v[i]);
+    }
+}
+
 }  // namespace onorm

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["os_softmax_forward", "os_softmax_topk", "safe_softmax_forward", "os_softmax_stats",
               "os_softmax_forward_lse", "os_softmax_forward_split", "os_softmax_forward_workspace_bytes",
-              "os_forward_split_plan", "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
+              "os_forward_split_plan", "os_device_copy_rows", "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
         assert n in names
 
 
@@ -192,6 +192,17 @@ def test_copy_validation(L):
     assert L.os_device_copy(FAKE + 4, FAKE + 4096, 32, None) == EINVAL  # misaligned
     assert L.os_device_copy(FAKE, FAKE + 16, 64, None) == EINVAL        # overlap
     assert L.os_device_copy(None, None, 0, None) == 0
+
+
+def test_copy_rows_validation(L):
+    f = L.os_device_copy_rows
+    assert f(FAKE, FAKE + (1 << 20), 4, 20, None) == EINVAL          # row_bytes not a multiple of 16
+    assert f(FAKE, FAKE + (1 << 20), 4, 131088, None) == EINVAL      # row longer than 128 KiB
+    assert f(None, FAKE, 4, 64, None) == EINVAL                      # NULL
+    assert f(FAKE + 8, FAKE + (1 << 20), 4, 64, None) == EINVAL      # misaligned
+    assert f(FAKE, FAKE + 64, 4, 64, None) == EINVAL                 # overlap
+    assert f(FAKE, FAKE, -1, 64, None) == EINVAL
+    assert f(None, None, 0, 64, None) == 0                           # nothing to copy
 
 
 def test_forward_plan(ons):

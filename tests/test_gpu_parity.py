@@ -552,6 +552,19 @@ def test_topk_matches_forward(ons):
     assert float((yi - p).abs().max()) <= 2e-6
 
 
+def test_copy_references(ons):
+    """Both bandwidth references copy exactly, including ragged rows."""
+    for rows, cols in ((4096, 32000), (3, 4), (17, 32768), (5, 1000)):
+        say(f"copy references {rows}x{cols}")
+        x = torch.randn(rows, cols, device="cuda")
+        y = torch.zeros_like(x)
+        ons.os_device_copy_rows(x, y)
+        y2 = torch.zeros_like(x)
+        ons.os_device_copy(x, y2)
+        torch.cuda.synchronize()
+        assert torch.equal(x, y) and torch.equal(x, y2)
+
+
 # -- full-size configurations, in the launch configuration the benchmark times -------
 
 def test_config2_full(ons, orc):
