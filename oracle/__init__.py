@@ -20,7 +20,8 @@ with the passages it follows:
   与可结合状态", section 3).
 * ``combine`` -- the binary operator of section 3.3 of the paper summary.
 * ``topk`` -- brute-force sort of the whole row under (value desc, index asc),
-  probabilities e^{u-m}/d over the whole row (section 4 of the paper summary).
+  probabilities e^{u-m}/d over the whole row (section 4 of the paper summary),
+  for fp32 rows or bf16 rows (widened exactly).
 
 Rows are independent, so the wrappers may split a batch of rows over host
 threads (each thread runs the same sequential C code on its own rows).
@@ -79,8 +80,10 @@ class Oracle:
         lib.oracle_online_state.restype = None
         lib.oracle_combine.argtypes = [ctypes.c_double] * 4 + [_c_double_p, _c_double_p]
         lib.oracle_combine.restype = None
-        lib.oracle_topk_f32.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
-        lib.oracle_topk_f32.restype = ctypes.c_int
+        for name in ("oracle_topk_f32", "oracle_topk_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
+            fn.restype = ctypes.c_int
         self.lib = lib
 
     # -- helpers -----------------------------------------------------------
@@ -188,17 +191,24 @@ class Oracle:
 
     # -- fused-softmax top-K, by brute force ----------------------------------
     def topk(self, x: np.ndarray, K: int, threads: int = 1):
-        x = np.ascontiguousarray(x, dtype=np.float32)
+        """K best entries per row (value desc, index asc) of a float32 array, or
+        of a uint16 array of bf16 bit patterns; probabilities over the whole row."""
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.float32:
+            fn, esz = self.lib.oracle_topk_f32, 4
+        elif x.dtype == np.uint16:
+            fn, esz = self.lib.oracle_topk_bf16, 2
+        else:
+            raise TypeError("x must be float32 or uint16 (bf16 bit patterns)")
         rows, cols = x.shape
         probs = np.empty((rows, K), dtype=np.float64)
         idx = np.empty((rows, K), dtype=np.int32)
         if rows == 0:
             return probs, idx
         xb, pb, ib = x.ctypes.data, probs.ctypes.data, idx.ctypes.data
-        fn = self.lib.oracle_topk_f32
 
         def part(r0, r1):
-            return fn(ctypes.c_void_p(xb + r0 * cols * 4), r1 - r0, cols, K,
+            return fn(ctypes.c_void_p(xb + r0 * cols * esz), r1 - r0, cols, K,
                       ctypes.c_void_p(pb + r0 * K * 8), ctypes.c_void_p(ib + r0 * K * 4))
 
         self._run_rows(part, rows, threads)

@@ -255,7 +255,24 @@ static int rank_order(const void *pa, const void *pb)
     return 0;
 }
 
-/* probs[r*K + k], idx[r*K + k] for k = 0..K-1, best first.
+/* One widened row: its K best entries under (value desc, index asc), with
+ * probabilities e^{u - m}/d over the whole row, into probs[0..K), idx[0..K). */
+static void topk_row(const double *buf, int64_t cols, int K, ranked_t *order, double *probs, int32_t *idx)
+{
+    double m = row_max(buf, cols);
+    double d = row_sum_exp(buf, cols, m);
+    for (int64_t j = 0; j < cols; ++j) {
+        order[j].value = buf[j];
+        order[j].index = j;
+    }
+    qsort(order, (size_t)cols, sizeof(ranked_t), rank_order);
+    for (int k = 0; k < K; ++k) {
+        probs[k] = exp(order[k].value - m) / d;
+        idx[k] = (int32_t)order[k].index;
+    }
+}
+
+/* probs[r*K + k], idx[r*K + k] for k = 0..K-1, best first, for an fp32 input.
  * Returns 0, -1 on allocation failure, -2 if K is out of [1, cols]. */
 int oracle_topk_f32(const float *x, int64_t rows, int64_t cols, int K, double *probs, int32_t *idx)
 {
@@ -270,17 +287,28 @@ int oracle_topk_f32(const float *x, int64_t rows, int64_t cols, int K, double *p
     }
     for (int64_t r = 0; r < rows; ++r) {
         widen_row_f32(x + r * cols, cols, buf);
-        double m = row_max(buf, cols);
-        double d = row_sum_exp(buf, cols, m);
-        for (int64_t j = 0; j < cols; ++j) {
-            order[j].value = buf[j];
-            order[j].index = j;
-        }
-        qsort(order, (size_t)cols, sizeof(ranked_t), rank_order);
-        for (int k = 0; k < K; ++k) {
-            probs[r * K + k] = exp(order[k].value - m) / d;
-            idx[r * K + k] = (int32_t)order[k].index;
-        }
+        topk_row(buf, cols, K, order, probs + r * K, idx + r * K);
+    }
+    free(buf);
+    free(order);
+    return 0;
+}
+
+/* The same for bf16 input given as raw 16-bit patterns (widened exactly). */
+int oracle_topk_bf16(const uint16_t *x, int64_t rows, int64_t cols, int K, double *probs, int32_t *idx)
+{
+    if (K < 1 || (int64_t)K > cols)
+        return -2;
+    double *buf = (double *)malloc((size_t)cols * sizeof(double));
+    ranked_t *order = (ranked_t *)malloc((size_t)cols * sizeof(ranked_t));
+    if (!buf || !order) {
+        free(buf);
+        free(order);
+        return -1;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        widen_row_bf16(x + r * cols, cols, buf);
+        topk_row(buf, cols, K, order, probs + r * K, idx + r * K);
     }
     free(buf);
     free(order);

@@ -263,6 +263,15 @@ def pin_topk_library(o):
     p, i = o.topk(w, 8)
     ref = np.argsort(-w.astype(np.float64), axis=1, kind="stable")[:, :8]
     assert np.array_equal(i, ref)
+    # bf16 rows (many exact ties after rounding): the same order on the widened values
+    b = workloads.f32_to_bf16_bits(rng.standard_normal((12, 301)).astype(np.float32) * np.float32(0.05))
+    b[2, :] = workloads.f32_to_bf16_bits(np.full((1, 301), 1.5, dtype=np.float32))[0]
+    wide = workloads.bf16_bits_to_f32(b).astype(np.float64)
+    for K in (1, 8, 32, 301):
+        p, i = o.topk(b, K)
+        ref = np.argsort(-wide, axis=1, kind="stable")[:, :K]
+        assert np.array_equal(i, ref)
+        assert np.max(np.abs(p - np.take_along_axis(softmax(wide, axis=1), ref, axis=1))) <= 1e-15
 
 
 def pin_logsumexp(o):

@@ -36,8 +36,8 @@ MUTANTS = [
      "if (a->index < b->index)\n        return 1;"),
     ("topk_ascending", "if (a->value > b->value)\n        return -1;",
      "if (a->value > b->value)\n        return 1;"),
-    ("topk_prob_unshifted", "probs[r * K + k] = exp(order[k].value - m) / d;",
-     "probs[r * K + k] = exp(order[k].value) / d;"),
+    ("topk_prob_unshifted", "probs[k] = exp(order[k].value - m) / d;",
+     "probs[k] = exp(order[k].value) / d;"),
     ("bf16_wrong_shift", "((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
     ("logsumexp_drops_max", "return (d == 0.0) ? -INFINITY : m + log(d);",
      "return (d == 0.0) ? -INFINITY : log(d);"),
