@@ -339,6 +339,15 @@ def all_configs(ons, stream):
     tf = flushed(lambda: ons.os_softmax_topk(xt, workloads.TOPK_K))
     entry["topk"]["us_flushed"] = round(tf * 1e6, 2)
     entry["topk"]["pct_peak_flushed"] = round(100 * nbytes / tf / 1e9 / PEAK_HBM_GBS, 1)
+    # the same logits rounded to bf16 (half the bytes to read)
+    xb = xt.to(torch.bfloat16)
+    nb16 = rows * cols * 2 + rows * workloads.TOPK_K * 8
+    tb, _ = measure(lambda: ons.os_softmax_topk(xb, workloads.TOPK_K), 200)
+    tbf = flushed(lambda: ons.os_softmax_topk(xb, workloads.TOPK_K))
+    entry["topk_bf16"] = {"us": round(tb * 1e6, 2), "GBs": round(nb16 / tb / 1e9, 1),
+                          "pct_peak": round(100 * nb16 / tb / 1e9 / PEAK_HBM_GBS, 1),
+                          "us_flushed": round(tbf * 1e6, 2), "algorithmic_bytes": nb16}
+    del xb
     # the unfused pipelines of the fusion comparison: softmax written out, then
     # top-K over the probabilities (online: 2R+1W then 1R; safe: 3R+1W then 1R)
     yt = torch.empty_like(xt)

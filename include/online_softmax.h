@@ -213,6 +213,22 @@ int64_t os_softmax_topk_workspace_bytes(int64_t rows, int K, int splits);
 int os_topk_plan(int64_t rows, int64_t cols, int K);
 
 /*
+ * The fused softmax + top-K for fp32 or bf16 logits (the paper summary,
+ * section 4), with an optional split as in os_softmax_topk_split.  bf16
+ * inputs widen exactly to fp32; the arithmetic, the ranking (value desc,
+ * index asc; bf16 rows tie far more often) and the outputs are those of
+ * os_softmax_topk.
+ *   in      [rows, cols] of `dtype`, aligned to its element size.
+ *   dtype   OS_F32 or OS_BF16.
+ *   probs, idx, rows, cols, K, splits, workspace, workspace_bytes, stream
+ *           as os_softmax_topk_split (the workspace does not depend on dtype).
+ *   Returns OS_OK, OS_EINVAL (as os_softmax_topk_split, or an unknown dtype),
+ *   or OS_ELAUNCH.
+ */
+int os_softmax_topk_ex(const void *in, int dtype, float *probs, int32_t *idx, int64_t rows, int64_t cols, int K,
+                       int splits, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * Baseline: safe softmax in three passes over the input in global memory
  * (maximum, sum of e^{x-m}, normalise and store), as in the paper summary,
  * section 2, and "5.2 Hiện thực và tối ưu CUDA Online Softmax", section 1.1.

@@ -14,7 +14,8 @@ Entry points (same names as the C ABI):
   os_softmax_forward_lse(x, out=None, write_y=True) -> (y, lse)   y and the per-row logsumexp
   os_softmax_forward_split(x, splits=None, out=None, workspace=None)   rows split over workgroups
   os_softmax_forward_workspace_bytes(rows, splits), os_forward_split_plan(rows, cols, dtype)
-  os_softmax_topk(x, K, splits=None) -> (probs, idx)   fused softmax + top-K
+  os_softmax_topk(x, K, splits=None) -> (probs, idx)   fused softmax + top-K (fp32 or bf16 x)
+  os_softmax_topk_ex(x, K, splits, workspace) -> (probs, idx)   the same with the dtype passed through
   os_softmax_topk_split(x, K, splits, workspace) -> (probs, idx)
   os_softmax_topk_workspace_bytes(rows, K, splits), os_topk_plan(rows, cols, K)
   safe_softmax_forward(x, out=None)            three-pass baseline
@@ -37,7 +38,7 @@ __all__ = [
     "OS_F32", "OS_BF16", "OS_TOPK_KMAX", "OnlineSoftmaxError", "LIB_PATH", "lib",
     "os_softmax_forward", "os_softmax_forward_tuned", "os_softmax_stats", "os_softmax_forward_lse", "os_softmax_topk",
     "safe_softmax_forward", "os_device_copy", "os_device_copy_rows", "os_forward_plan", "os_last_error", "os_version",
-    "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan",
+    "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan", "os_softmax_topk_ex",
     "os_softmax_forward_split", "os_softmax_forward_workspace_bytes", "os_forward_split_plan",
 ]
 
@@ -92,6 +93,7 @@ def _load() -> ctypes.CDLL:
         "os_version": [],
         "os_softmax_topk_split": [vp, vp, vp, i64, i64, i32, i32, vp, i64, vp],
         "os_topk_plan": [i64, i64, i32],
+        "os_softmax_topk_ex": [vp, i32, vp, vp, i64, i64, i32, i32, vp, i64, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -241,8 +243,8 @@ def _split_workspace(x: torch.Tensor, nbytes: int) -> torch.Tensor:
 
 def _topk_out(x, K):
     rows, cols = _rows_cols(x)
-    if x.dtype != torch.float32:
-        raise TypeError("top-K takes float32 input")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("top-K takes float32 or bfloat16 input")
     shape = (*x.shape[:-1], K)
     probs = torch.empty(shape, dtype=torch.float32, device=x.device)
     idx = torch.empty(shape, dtype=torch.int32, device=x.device)
@@ -265,6 +267,9 @@ def os_softmax_topk(x: torch.Tensor, K: int, splits: int | None = None) -> tuple
     rows, cols, probs, idx = _topk_out(x, K)
     if splits is None:
         splits = os_topk_plan(rows, cols, K)
+    if x.dtype == torch.bfloat16:
+        ws = _split_workspace(x, os_softmax_topk_workspace_bytes(rows, K, splits))
+        return os_softmax_topk_ex(x, K, splits, ws, probs, idx)
     if splits == 1:
         _check("os_softmax_topk",
                lib().os_softmax_topk(x.data_ptr(), probs.data_ptr(), idx.data_ptr(), rows, cols, K, _stream(x)))
@@ -311,6 +316,20 @@ def os_softmax_forward_split(x: torch.Tensor, splits: int | None = None, out: to
                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                           _stream(x)))
     return out
+
+
+def os_softmax_topk_ex(x: torch.Tensor, K: int, splits: int, workspace: torch.Tensor,
+                       probs: torch.Tensor | None = None,
+                       idx: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Fused softmax + top-K for float32 or bfloat16 input (dtype from the tensor)."""
+    rows, cols, p_new, i_new = _topk_out(x, K)
+    probs = p_new if probs is None else probs
+    idx = i_new if idx is None else idx
+    _check("os_softmax_topk_ex",
+           lib().os_softmax_topk_ex(x.data_ptr(), _dtype_code(x), probs.data_ptr(), idx.data_ptr(), rows, cols, K,
+                                    splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream(x)))
+    return probs, idx
 
 
 def safe_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -463,8 +463,9 @@ TopkWorkspace topk_workspace(int64_t rows, int K, int S) {
     return w;
 }
 
-int check_topk(const char* fn, const float* in, const float* probs, const int32_t* idx, int64_t rows,
+int check_topk(const char* fn, const void* in, int dtype, const float* probs, const int32_t* idx, int64_t rows,
                int64_t cols, int K) {
+    if (dtype != OS_F32 && dtype != OS_BF16) return fail(OS_EINVAL, "%s: unknown dtype %d", fn, dtype);
     if (rows < 0 || cols < 0) return fail(OS_EINVAL, "%s: rows and cols must be >= 0", fn);
     if (cols > OS_MAX_COLS) return fail(OS_EINVAL, "%s: cols %lld exceeds OS_MAX_COLS", fn, (long long)cols);
     if (K < 1 || K > OS_TOPK_KMAX) return fail(OS_EINVAL, "%s: K=%d outside [1, %d]", fn, K, OS_TOPK_KMAX);
@@ -472,31 +473,40 @@ int check_topk(const char* fn, const float* in, const float* probs, const int32_
     if (static_cast<int64_t>(K) > cols) return fail(OS_EINVAL, "%s: K=%d exceeds cols=%lld", fn, K, (long long)cols);
     if (rows > INT64_MAX / cols / 4) return fail(OS_EINVAL, "%s: rows * cols overflows", fn);
     if (in == nullptr || probs == nullptr || idx == nullptr) return fail(OS_EINVAL, "%s: NULL pointer", fn);
-    if (!aligned(in, 4) || !aligned(probs, 4) || !aligned(idx, 4))
-        return fail(OS_EINVAL, "%s: pointers must be 4-byte aligned", fn);
+    if (!aligned(in, elt_size(dtype)) || !aligned(probs, 4) || !aligned(idx, 4))
+        return fail(OS_EINVAL, "%s: input must be aligned to its element size, probs and idx to 4 bytes", fn);
     return OS_OK;
 }
 
-typedef void (*TopkKernel)(const float*, float*, int*, int64_t, int, int, int, State*, TopkEntry*);
+typedef void (*TopkKernel)(const void*, float*, int*, int64_t, int, int, int, State*, TopkEntry*);
 
-template <int W>
-TopkKernel topk_kernel(bool al, bool split) {
-    if (split) return al ? k_topk<W, 4, true, true> : k_topk<W, 4, false, true>;
-    return al ? k_topk<W, 4, true, false> : k_topk<W, 4, false, false>;
+// Vectors per lane per tile: 4 for fp32, 2 for bf16 (16 elements either way).
+template <int W, bool BF16>
+TopkKernel topk_kernel_t(bool al, bool split) {
+    constexpr int U = BF16 ? 2 : 4;
+    if (split) return al ? k_topk<BF16, W, U, true, true> : k_topk<BF16, W, U, false, true>;
+    return al ? k_topk<BF16, W, U, true, false> : k_topk<BF16, W, U, false, false>;
 }
 
-int launch_topk(const char* fn, const float* in, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K,
-                int S, void* workspace, void* stream) {
-    const bool al = aligned(in, 16) && (cols % 4) == 0;
+template <int W>
+TopkKernel topk_kernel(int dtype, bool al, bool split) {
+    return dtype == OS_BF16 ? topk_kernel_t<W, true>(al, split) : topk_kernel_t<W, false>(al, split);
+}
+
+int launch_topk(const char* fn, const void* in, int dtype, float* probs, int32_t* idx, int64_t rows, int64_t cols,
+                int K, int S, void* workspace, void* stream) {
+    const bool al = aligned(in, 16) && ((cols * elt_size(dtype)) % 16) == 0;
     const int64_t units = rows * S;
-    // 8-wave workgroups, except for K > 8 on at most 256 workgroups, where a
-    // row's candidate inserts spread over 16 waves pay off (measured on MI355X
-    // over 16..4096 rows of 32000 and 128256 columns, K = 1..32: this choice
-    // is within 2% of the faster width everywhere).
-    const bool wide = units <= 256 && K > 8;
+    // 8-wave workgroups, except on at most 256 workgroups for K > 8 (fp32) or
+    // any K (bf16), where 16 waves per row hide more of the per-element
+    // arithmetic and spread the candidate inserts (measured on MI355X over
+    // 16..4096 rows of 32000 and 128256 columns, K = 1..32: this choice is
+    // within 2% of the faster width everywhere for fp32; for bf16 16 waves
+    // are 10-25% faster on 256 rows and 15-40% slower on >= 1024).
+    const bool wide = units <= 256 && (K > 8 || dtype == OS_BF16);
     const int block = wide ? 1024 : 512;
     const int grid = grid_for(units, block, 0);
-    const TopkKernel k = wide ? topk_kernel<16>(al, S > 1) : topk_kernel<8>(al, S > 1);
+    const TopkKernel k = wide ? topk_kernel<16>(dtype, al, S > 1) : topk_kernel<8>(dtype, al, S > 1);
     State* states = nullptr;
     TopkEntry* lists = nullptr;
     if (S > 1) {
@@ -518,16 +528,36 @@ int launch_topk(const char* fn, const float* in, float* probs, int32_t* idx, int
     return launched(fn);
 }
 
+int topk_split_common(const char* fn, const void* in, int dtype, float* probs, int32_t* idx, int64_t rows,
+                      int64_t cols, int K, int splits, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (splits < 1 || splits > OS_TOPK_MAX_SPLITS)
+        return fail(OS_EINVAL, "%s: splits=%d outside [1, %d]", fn, splits, OS_TOPK_MAX_SPLITS);
+    const int rc = check_topk(fn, in, dtype, probs, idx, rows, cols, K);
+    if (rc == 1) return ok();
+    if (rc != OS_OK) return rc;
+    if (splits > 1) {
+        if (!workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State) + K * sizeof(TopkEntry)) + 512))
+            return fail(OS_EINVAL, "%s: rows * splits overflows the workspace size", fn);
+        if (workspace == nullptr) return fail(OS_EINVAL, "%s: workspace is NULL", fn);
+        if (!aligned(workspace, 256)) return fail(OS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+        const int64_t need = topk_workspace(rows, K, splits).bytes;
+        if (workspace_bytes < need)
+            return fail(OS_EINVAL, "%s: workspace has %lld bytes, needs %lld", fn, (long long)workspace_bytes,
+                        (long long)need);
+    }
+    return launch_topk(fn, in, dtype, probs, idx, rows, cols, K, splits, workspace, stream);
+}
+
 }  // namespace
 
 extern "C" {
 
 int os_softmax_topk(const float* in, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K, void* stream) {
     const char* fn = "os_softmax_topk";
-    const int rc = check_topk(fn, in, probs, idx, rows, cols, K);
+    const int rc = check_topk(fn, in, OS_F32, probs, idx, rows, cols, K);
     if (rc == 1) return ok();
     if (rc != OS_OK) return rc;
-    return launch_topk(fn, in, probs, idx, rows, cols, K, 1, nullptr, stream);
+    return launch_topk(fn, in, OS_F32, probs, idx, rows, cols, K, 1, nullptr, stream);
 }
 
 int64_t os_softmax_topk_workspace_bytes(int64_t rows, int K, int splits) {
@@ -556,23 +586,14 @@ int os_topk_plan(int64_t rows, int64_t cols, int K) {
 
 int os_softmax_topk_split(const float* in, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K, int splits,
                           void* workspace, int64_t workspace_bytes, void* stream) {
-    const char* fn = "os_softmax_topk_split";
-    if (splits < 1 || splits > OS_TOPK_MAX_SPLITS)
-        return fail(OS_EINVAL, "%s: splits=%d outside [1, %d]", fn, splits, OS_TOPK_MAX_SPLITS);
-    const int rc = check_topk(fn, in, probs, idx, rows, cols, K);
-    if (rc == 1) return ok();
-    if (rc != OS_OK) return rc;
-    if (splits > 1) {
-        if (!workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State) + K * sizeof(TopkEntry)) + 512))
-            return fail(OS_EINVAL, "%s: rows * splits overflows the workspace size", fn);
-        if (workspace == nullptr) return fail(OS_EINVAL, "%s: workspace is NULL", fn);
-        if (!aligned(workspace, 256)) return fail(OS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
-        const int64_t need = topk_workspace(rows, K, splits).bytes;
-        if (workspace_bytes < need)
-            return fail(OS_EINVAL, "%s: workspace has %lld bytes, needs %lld", fn, (long long)workspace_bytes,
-                        (long long)need);
-    }
-    return launch_topk(fn, in, probs, idx, rows, cols, K, splits, workspace, stream);
+    return topk_split_common("os_softmax_topk_split", in, OS_F32, probs, idx, rows, cols, K, splits, workspace,
+                             workspace_bytes, stream);
+}
+
+int os_softmax_topk_ex(const void* in, int dtype, float* probs, int32_t* idx, int64_t rows, int64_t cols, int K,
+                       int splits, void* workspace, int64_t workspace_bytes, void* stream) {
+    return topk_split_common("os_softmax_topk_ex", in, dtype, probs, idx, rows, cols, K, splits, workspace,
+                             workspace_bytes, stream);
 }
 
 int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {

@@ -745,13 +745,14 @@ __device__ __forceinline__ void topk_of_lists(int n, int K, int lane, Get get, f
 // row's vector slots, each writing its state (m, d) and its sorted K-list to
 // the workspace; k_topk_merge (the next launch on the stream, so every
 // partial is visible) combines them.
-template <int W, int U, bool ALIGNED, bool SPLIT>
+template <bool BF16, int W, int U, bool ALIGNED, bool SPLIT>
 __global__ void __launch_bounds__(W * 64)
-    k_topk(const float* in, float* probs, int* idx, int64_t rows, int cols, int K, int S, State* ws_state,
+    k_topk(const void* in, float* probs, int* idx, int64_t rows, int cols, int K, int S, State* ws_state,
            TopkEntry* ws_list) {
+    using E = Elt<BF16>;
     static_assert(W == 4 || W == 8 || W == 16, "the final merge packs W lists of up to 32 entries into 8 registers");
     constexpr int BLOCK = W * 64;
-    constexpr int VEC = 4;
+    constexpr int VEC = E::kVec;
     constexpr int STEP = BLOCK * U;
     __shared__ float s_val[W][kTopKMax];
     __shared__ int s_idx[W][kTopKMax];
@@ -764,10 +765,10 @@ __global__ void __launch_bounds__(W * 64)
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
     const uint64_t kmask = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
-    const int nvec = vec_count<false, ALIGNED>(cols);
+    const int nvec = vec_count<BF16, ALIGNED>(cols);
     const int seg_vec = SPLIT ? (nvec + S - 1) / S : nvec;
     const int64_t units = SPLIT ? rows * S : rows;
-    const uint32_t row_bytes = static_cast<uint32_t>(cols) * 4u;
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
 
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t row = SPLIT ? unit / S : unit;
@@ -777,7 +778,8 @@ __global__ void __launch_bounds__(W * 64)
         // The resource ends with the segment, so loads issued ahead past its
         // end (into the next segment or past the row) touch no memory.
         const uint32_t seg_end = static_cast<uint32_t>(v1) * 16u;
-        const Buf bin(in + row * static_cast<int64_t>(cols), seg_end < row_bytes ? seg_end : row_bytes);
+        const Buf bin(static_cast<const char*>(in) + row * static_cast<int64_t>(row_bytes),
+                      seg_end < row_bytes ? seg_end : row_bytes);
         if (tid == 0) s_thr = ordered_bits(-INFINITY);
         if (tid < 128) s_rank[tid / 64][tid % 64] = 0;
         __syncthreads();
@@ -798,7 +800,7 @@ __global__ void __launch_bounds__(W * 64)
             if constexpr (ALIGNED) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    Elt<false>::unpack(raw[u], x[u]);
+                    E::unpack(raw[u], x[u]);
                     const bool ok = base + u * BLOCK + tid < v1;
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) x[u][k] = ok ? x[u][k] : -INFINITY;
@@ -811,7 +813,7 @@ __global__ void __launch_bounds__(W * 64)
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int slot = base + u * BLOCK + tid;
-                    load_slot<false, false, true>(bin, 0u, slot, v1, cols, slot < v1, x[u]);
+                    load_slot<BF16, false, true>(bin, 0u, slot, v1, cols, slot < v1, x[u]);
                 }
             }
 

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["os_softmax_forward", "os_softmax_topk", "safe_softmax_forward", "os_softmax_stats",
               "os_softmax_forward_lse", "os_softmax_forward_split", "os_softmax_forward_workspace_bytes",
-              "os_forward_split_plan", "os_device_copy_rows", "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
+              "os_forward_split_plan", "os_device_copy_rows", "os_softmax_topk_ex", "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
         assert n in names
 
 
@@ -192,6 +192,19 @@ def test_copy_validation(L):
     assert L.os_device_copy(FAKE + 4, FAKE + 4096, 32, None) == EINVAL  # misaligned
     assert L.os_device_copy(FAKE, FAKE + 16, 64, None) == EINVAL        # overlap
     assert L.os_device_copy(None, None, 0, None) == 0
+
+
+def test_topk_ex_validation(L, ons):
+    f = L.os_softmax_topk_ex
+    need = ons.os_softmax_topk_workspace_bytes(10, 8, 4)
+    assert f(FAKE, 5, FAKE, FAKE, 10, 1000, 8, 1, None, 0, None) == EINVAL          # unknown dtype
+    assert f(FAKE + 1, BF16, FAKE, FAKE, 10, 1000, 8, 1, None, 0, None) == EINVAL   # odd bf16 address
+    assert f(FAKE + 2, F32, FAKE, FAKE, 10, 1000, 8, 1, None, 0, None) == EINVAL    # fp32 needs 4 bytes
+    assert f(FAKE, BF16, FAKE, FAKE, 10, 1000, 0, 1, None, 0, None) == EINVAL       # K < 1
+    assert f(FAKE, BF16, FAKE, FAKE, 10, 4, 8, 1, None, 0, None) == EINVAL          # K > cols
+    assert f(FAKE, BF16, FAKE, FAKE, 10, 1000, 8, 4, None, need, None) == EINVAL    # no workspace
+    assert f(FAKE, BF16, FAKE, FAKE, 10, 1000, 8, 17, FAKE, need, None) == EINVAL   # splits > 16
+    assert f(None, BF16, None, None, 0, 1000, 8, 1, None, 0, None) == 0             # empty
 
 
 def test_copy_rows_validation(L):

@@ -540,6 +540,50 @@ def test_topk_split_reuses_workspace(ons):
     assert float((a[0] - c[0]).abs().max()) <= 1e-6
 
 
+def test_topk_bf16(ons, orc):
+    """bf16 logits (many exact ties after rounding): ragged rows, every K class, splits, an
+    element-aligned base, all-equal and mostly -inf rows."""
+    rng = np.random.Generator(np.random.PCG64(88))
+    for rows, cols in ((7, 1000), (5, 4093), (3, 65536 + 8), (2, 200003)):
+        x32 = (rng.standard_normal((rows, cols)) * 0.05).astype(np.float32)
+        x32[0, :] = 1.25
+        if rows > 2:
+            x32[2, :] = -np.inf
+            x32[2, rng.integers(cols, size=3)] = 0.5
+        x = bf16_bits(x32)
+        for K in (1, 8, 13, 32):
+            for splits in (1, 3):
+                say(f"topk bf16 rows={rows} cols={cols} K={K} splits={splits}")
+                p, i = ons.os_softmax_topk(to_device(x), K, splits=splits)
+                torch.cuda.synchronize()
+                pr, ir = orc.topk(x, K, threads=8)
+                assert np.array_equal(to_host(i), ir), f"bf16 cols={cols} K={K} S={splits}"
+                p = to_host(p).astype(np.float64)
+                assert np.array_equal(np.isnan(p), np.isnan(pr))
+                ok = ~np.isnan(pr)
+                assert np.max(np.abs(p[ok] - pr[ok]), initial=0.0) <= TOPK_PROB_ABS
+    # an element-aligned (not 16-byte aligned) base
+    x = bf16_bits((rng.standard_normal((4, 3001)) * 0.1).astype(np.float32))
+    buf = torch.empty(x.size + 1, dtype=torch.bfloat16, device="cuda")
+    xd = buf[1:].view(4, 3001)
+    xd.copy_(to_device(x))
+    say("topk bf16 misaligned base")
+    p, i = ons.os_softmax_topk(xd, 8)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(i), orc.topk(x, 8)[1])
+
+
+def test_topk_bf16_full_size(ons, orc):
+    """Workload 5's logits rounded to bf16, in the launch the plan picks."""
+    x = bf16_bits(workloads.config(5))
+    say("topk bf16 full 256x128256")
+    p, i = ons.os_softmax_topk(to_device(x), workloads.TOPK_K)
+    torch.cuda.synchronize()
+    pr, ir = orc.topk(x, workloads.TOPK_K, threads=16)
+    assert np.array_equal(to_host(i), ir)
+    assert np.max(np.abs(to_host(p).astype(np.float64) - pr)) <= TOPK_PROB_ABS
+
+
 def test_topk_matches_forward(ons):
     """The fused probabilities equal the full softmax at the selected indices."""
     x = workloads.config(5, 0, 16)
