@@ -72,7 +72,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-            "(or python -m online_normalizer_amd.build); there is no fallback")
+            "(or python online_normalizer_amd/build.py); there is no fallback")
     L = ctypes.CDLL(LIB_PATH)
     runtimes = _hip_runtimes_mapped()
     if len(runtimes) > 1:

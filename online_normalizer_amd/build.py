@@ -1,6 +1,7 @@
 """Build the HIP library ``libonline_softmax.so`` for gfx950 with hipcc.
 
-``python -m online_normalizer_amd.build`` compiles in place.  Packed fp32 VALU
+``python online_normalizer_amd/build.py`` compiles in place (run it as a
+script: importing it through the package would load the library first).  Packed fp32 VALU
 instructions are disabled for all device code (``-packed-fp32-ops``).
 """
 from __future__ import annotations

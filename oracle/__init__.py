@@ -38,12 +38,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
 
 
-def build(*args, **kwargs) -> str:
-    """Compile ``oracle.c`` (see ``oracle/build.py``)."""
-    from .build import build as _build
-    return _build(*args, **kwargs)
-
-__all__ = ["Oracle", "load", "build", "DEFAULT_LIB"]
+# Compiling the library lives in the ``oracle.build`` module
+# (``from oracle.build import build``; ``python -m oracle.build``).
+__all__ = ["Oracle", "load", "DEFAULT_LIB"]
 
 _c_double_p = ctypes.POINTER(ctypes.c_double)
 

@@ -258,3 +258,21 @@ def test_error_message_is_thread_local(L, ons):
     t.join()
     assert seen == [""]
     assert "NULL" in ons.os_last_error()
+
+
+def test_build_scripts_load_without_the_package():
+    """__graft_entry__.build() must work on a fresh checkout, before any library
+    exists: its build scripts load by path, without importing the packages
+    whose __init__ needs the library."""
+    import subprocess
+    import sys
+    code = (
+        "import os, sys, __graft_entry__ as g\n"
+        "h = g._script(os.path.join(g.ROOT, 'online_normalizer_amd', 'build.py'), '_h')\n"
+        "o = g._script(os.path.join(g.ROOT, 'oracle', 'build.py'), '_o')\n"
+        "assert callable(h.build) and callable(o.build)\n"
+        "assert 'online_normalizer_amd' not in sys.modules and 'oracle' not in sys.modules\n"
+        "print('ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr
