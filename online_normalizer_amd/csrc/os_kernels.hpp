@@ -799,11 +799,16 @@ __global__ void __launch_bounds__(W * 64)
             float x[U][VEC];
             if constexpr (ALIGNED) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    E::unpack(raw[u], x[u]);
-                    const bool ok = base + u * BLOCK + tid < v1;
+                for (int u = 0; u < U; ++u) E::unpack(raw[u], x[u]);
+                // only a segment's last tile can hold slots past its end (read
+                // as 0 by the range check); the test is uniform
+                if (base + STEP > v1) {
 #pragma unroll
-                    for (int k = 0; k < VEC; ++k) x[u][k] = ok ? x[u][k] : -INFINITY;
+                    for (int u = 0; u < U; ++u) {
+                        const bool ok = base + u * BLOCK + tid < v1;
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) x[u][k] = ok ? x[u][k] : -INFINITY;
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u)
