@@ -16,7 +16,7 @@ using namespace onorm;
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: logsumexp, split-row forward, bf16 top-K, row-pattern copy
 
 thread_local char g_error[512] = "";
 

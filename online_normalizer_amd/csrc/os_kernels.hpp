@@ -1,16 +1,18 @@
 // os_kernels.hpp -- gfx950 kernels for row-wise softmax with the online
 // normalizer ("OnlineSoftmax: Online normalizer calculation for softmax",
-// paper summary, sections 3.1-3.3 and 4), the three-pass safe-softmax
-// baseline (same page, section 2), and a plain copy used as a bandwidth
-// reference.
+// paper summary, sections 3.1-3.3 and 4): the register-resident and streaming
+// forwards (optionally writing (m, d) or the logsumexp), the split-row
+// forward, the fused softmax + top-K; the three-pass safe-softmax baseline
+// (same page, section 2); and two plain copies used as bandwidth references.
 //
 // Row layout: row-major, stride == cols.  Lanes address a row in 16-byte
 // vectors: vector slot vi covers elements [vi*VEC, vi*VEC + VEC).  ALIGNED
 // kernels move whole vectors with 128-bit buffer accesses (row starts 16-byte
 // aligned, cols a multiple of VEC); the others move the same slots element by
-// element.  Every row is read and written through a buffer resource that
-// covers that row only; elements past the end read as -inf (e^{-inf} adds 0
-// to any state) and stores past the end are dropped by the hardware.
+// element.  Rows are read and written through buffer resources that cover
+// only the rows, or the row slice, a workgroup works on; elements past the end
+// read as -inf (e^{-inf} adds 0 to any state) and stores past the end are
+// dropped by the hardware.
 #pragma once
 
 #include "os_device.hpp"
@@ -558,8 +560,8 @@ __global__ void __launch_bounds__(W * 64)
 // ---------------------------------------------------------------------------
 // Fused softmax + top-K (paper summary, section 4), one read of the input.
 //
-// One W-wave workgroup per row.  Every lane folds (m, d) over its slots as in
-// k_stream.  Candidates: each wave keeps ONE sorted list of the best K
+// One W-wave workgroup per row (per row slice with SPLIT), fp32 or bf16
+// logits.  Every lane folds (m, d) over its slots as in k_stream.  Candidates: each wave keeps ONE sorted list of the best K
 // (value, index) pairs it has seen, spread over lanes 0..K-1 (lane k holds
 // rank k) under the total order (value desc, index asc).  Most elements are
 // rejected by a compare with a wave-uniform threshold T, a lower bound on the
@@ -576,7 +578,8 @@ __global__ void __launch_bounds__(W * 64)
 // position p = number of entries ahead of the new pair, entries from p on
 // shift down one lane (DPP wave_shr:1).  Every true top-K element survives
 // every filter and stays in its wave's list, so the final merge of the W
-// sorted lists (a bitonic merge in one wave, lowest index on ties) is exact.  Output: probs = e^{u - m} / d over the whole row, and indices.
+// sorted lists (a bitonic merge in one wave, lowest index on ties) is exact.
+// Output: probs = e^{u - m} / d over the whole row, and indices.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int ordered_bits(float f) {
     const int i = __float_as_int(f);

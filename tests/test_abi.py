@@ -52,7 +52,7 @@ def test_exported_symbols_are_c_linkage():
 
 
 def test_version(ons):
-    assert ons.os_version() == 100
+    assert ons.os_version() == 200
 
 
 EINVAL, EUNSUP = -1, -2
