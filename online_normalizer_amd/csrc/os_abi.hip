@@ -236,8 +236,15 @@ int grid_for(int64_t groups, int block, int requested) {
     return static_cast<int>(g);
 }
 
+// Rows past the register-resident limit: on aligned rows of up to this many
+// columns the hybrid kernel keeps the first 65536 elements in registers and
+// streams the rest (measured 15-20% faster than streaming the whole row twice
+// up to 262144 columns; no better on longer rows, where the resident share is
+// small).
+constexpr int64_t kHybridMaxCols = 4 * 65536;
+
 int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t rows,
-             int64_t cols, int dtype, int lpr, int vpl, int grid_req, void* stream) {
+             int64_t cols, int dtype, int lpr, int vpl, int grid_req, bool allow_hybrid, void* stream) {
     // Shape checks first: no HIP call happens before every argument is known good.
     const ResidentShape* shape = nullptr;
     if (lpr != 0) {
@@ -254,6 +261,12 @@ int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t 
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape == nullptr) {
+        if (allow_hybrid && al && cols <= kHybridMaxCols) {
+            const RowKernel k = dtype == OS_BF16 ? k_hybrid<true, 8, 2, true> : k_hybrid<false, 16, 2, true>;
+            hipLaunchKernelGGL(k, dim3(grid_for(rows, 1024, grid_req)), dim3(1024), 0, st, in, out, stats, rows,
+                               static_cast<int>(cols));
+            return launched(fn);
+        }
         const int w = stream_waves(cols, dtype);
         const int block = w * 64;
         const int grid = grid_for(rows, block, grid_req);
@@ -294,7 +307,7 @@ int os_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, in
     if (rc != OS_OK) return rc;
     int lpr = 0, vpl = 0;
     auto_plan(cols, dtype, &lpr, &vpl);
-    return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, stream);
+    return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, true, stream);
 }
 
 int os_softmax_forward_tuned(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int lanes_per_row,
@@ -308,7 +321,7 @@ int os_softmax_forward_tuned(const void* in, void* out, int64_t rows, int64_t co
         return fail(OS_EUNSUPPORTED, "%s: no kernel built for lanes_per_row=%d vecs_per_lane=%d", fn, lanes_per_row,
                     vecs_per_lane);
     if (rc == 1) return ok();
-    return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lanes_per_row, vecs_per_lane, grid_blocks,
+    return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lanes_per_row, vecs_per_lane, grid_blocks, false,
                     stream);
 }
 
@@ -323,7 +336,7 @@ int os_softmax_stats(const void* in, float* m, float* d, int64_t rows, int64_t c
     int lpr = 0, vpl = 0;
     auto_plan(cols, dtype, &lpr, &vpl);
     return run_rows(fn, cols == 0 ? nullptr : in, nullptr, RowStats{m, d, nullptr}, rows, cols, dtype, lpr, vpl, 0,
-                    stream);
+                    true, stream);
 }
 
 int os_softmax_forward_lse(const void* in, void* out, float* lse, int64_t rows, int64_t cols, int dtype,
@@ -338,7 +351,7 @@ int os_softmax_forward_lse(const void* in, void* out, float* lse, int64_t rows, 
     int lpr = 0, vpl = 0;
     auto_plan(cols, dtype, &lpr, &vpl);
     return run_rows(fn, cols == 0 ? nullptr : in, cols == 0 ? nullptr : out, RowStats{nullptr, nullptr, lse}, rows,
-                    cols, dtype, lpr, vpl, 0, stream);
+                    cols, dtype, lpr, vpl, 0, true, stream);
 }
 
 int64_t os_softmax_forward_workspace_bytes(int64_t rows, int splits) {
@@ -379,7 +392,7 @@ int os_softmax_forward_split(const void* in, void* out, int64_t rows, int64_t co
     if (splits == 1) {
         int lpr = 0, vpl = 0;
         auto_plan(cols, dtype, &lpr, &vpl);
-        return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, stream);
+        return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, true, stream);
     }
     if (!workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State))))
         return fail(OS_EINVAL, "%s: rows * splits overflows the workspace size", fn);

@@ -276,6 +276,98 @@ __global__ void __launch_bounds__(W * 64)
 }
 
 // ---------------------------------------------------------------------------
+// Hybrid forward for rows longer than the register-resident kernels hold: one
+// 1024-lane workgroup per row keeps the row's first 1024 * VPL vectors in
+// registers (read once, as in k_resident) and streams the rest twice (as in
+// k_stream).  Pass 1: e_k = e^{x_k - m_r} over the resident slots (m_r the
+// lane's resident maximum), then the streamed tiles fold into the same lane
+// state by the tile form of the recurrence; lanes and waves merge with (+).
+// Pass 2 writes the resident slots as e_k * (e^{m_r - m} / d) and re-reads
+// the streamed ones.  HBM traffic per row: in + out + the streamed part again.
+// ---------------------------------------------------------------------------
+template <bool BF16, int VPL, int U, bool ALIGNED>
+__global__ void __launch_bounds__(1024)
+    k_hybrid(const void* in, void* out, RowStats st, int64_t rows, int cols) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    constexpr int W = 16;
+    constexpr int BLOCK = W * 64;
+    constexpr int RES = BLOCK * VPL;  // resident vector slots per row
+    __shared__ State lds[2][W];
+
+    const int tid = threadIdx.x;
+    const int nvec = vec_count<BF16, ALIGNED>(cols);
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    int par = 0;
+
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const Buf bin(static_cast<const char*>(in) + row * row_bytes, row_bytes);
+        float xr[VPL][VEC];
+        load_slots<BF16, VPL, ALIGNED, true>(bin, 0u, tid, BLOCK, nvec, cols, true, xr);
+        float mr = kFloor;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) mr = fmaxf(mr, xr[v][k]);
+        float dl = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                xr[v][k] = exp_e(xr[v][k] - mr);
+                dl += xr[v][k];
+            }
+        float ml = mr;
+        for (int base = RES; base < nvec; base += BLOCK * U) {
+            float x[U][VEC];
+            load_slots<BF16, U, ALIGNED, false>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+            float mc = kFloor;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) mc = fmaxf(mc, x[u][k]);
+            const float mn = fmaxf(ml, mc);
+            float acc = dl * exp_e(ml - mn);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc += exp_e(x[u][k] - mn);
+            dl = acc;
+            ml = mn;
+        }
+        State s = group_merge<64>(State{ml, dl});
+        if ((tid & (kWave - 1)) == 0) lds[par][tid / kWave] = s;
+        __syncthreads();
+        s = lds[par][0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) s = oplus(s, lds[par][w]);
+        par ^= 1;
+        if (any_stats(st) && tid == 0) put_stats(st, row, s);
+        if (out != nullptr) {
+            const float inv_d = rcp(s.d);
+            const float scale = exp_e(mr - s.m) * inv_d;
+            const Buf bout(static_cast<char*>(out) + row * row_bytes, row_bytes);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) xr[v][k] *= scale;
+                store_slot<BF16, ALIGNED>(bout, 0u, v * BLOCK + tid, nvec, cols, true, xr[v]);
+            }
+            for (int base = RES; base < nvec; base += BLOCK * U) {
+                float x[U][VEC];
+                load_slots<BF16, U, ALIGNED, true>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - s.m) * inv_d;
+                    store_slot<BF16, ALIGNED>(bout, 0u, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Baseline: safe softmax in three streaming passes over global memory
 // (maximum; sum of e^{x - m}; normalise and store), same geometry and loads
 // as k_stream so that the two differ only in the passes.

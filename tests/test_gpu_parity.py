@@ -126,6 +126,44 @@ def test_streaming_two_pass(ons, orc, bf16):
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_hybrid_long_rows(ons, orc, bf16):
+    """Aligned rows past the register-resident limit (up to 262144 columns) take the
+    hybrid kernel: the first 65536 elements stay in registers, the rest stream.
+    Rows put the maximum in the streamed part only, make the resident part all
+    -inf, or hold NaN / +inf / only -inf."""
+    for rows, cols in ((3, 65544), (17, 100000), (5, 128256), (2, 200000), (2, 262144)):
+        x32 = workloads.normal(rows, cols, seed=cols + 3, scale=3.0)
+        x32[0, cols - 5] = 90.0                 # the row maximum, in the streamed part
+        if rows > 2:
+            x32[1, :65536] = -np.inf            # nothing in the resident part
+            x32[2, 70000 % cols] = np.nan
+        if rows > 4:
+            x32[3, :] = -np.inf
+            x32[4, 100] = np.inf
+        x = bf16_bits(x32) if bf16 else x32
+        ref = orc.softmax(x, threads=8)
+        say(f"hybrid bf16={bf16} rows={rows} cols={cols}")
+        assert_parity(run_forward(ons, x), ref, bf16, f"hybrid cols={cols}")
+        assert_parity(run_forward(ons, x, lanes=0), ref, bf16, f"stream cols={cols}")
+        xd = to_device(x)
+        m, d = ons.os_softmax_stats(xd)
+        _, lse = ons.os_softmax_forward_lse(xd, write_y=False)
+        y = ons.os_softmax_forward(xd)
+        yi = ons.os_softmax_forward(xd, out=xd)  # in place
+        torch.cuda.synchronize()
+        assert torch.equal(bits(yi), bits(y))
+        mo, do = orc.stats(x, threads=8)
+        m, d = to_host(m).astype(np.float64), to_host(d).astype(np.float64)
+        fin = np.isfinite(do) & (do > 0)
+        assert np.array_equal(m[fin], mo[fin]) and np.max(np.abs(d[fin] - do[fin]) / do[fin], initial=0.0) <= 1e-5
+        lo = orc.logsumexp(x, threads=8)
+        lse = to_host(lse).astype(np.float64)
+        assert np.array_equal(np.isnan(lse), np.isnan(lo)) and np.array_equal(np.isneginf(lse), np.isneginf(lo))
+        f = np.isfinite(lo)
+        assert np.all(np.abs(lse[f] - lo[f]) <= lse_tol(lo[f]))
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_safe_three_pass(ons, orc, bf16):
     for rows, cols in [(3, 1), (11, 33), (7, 4096), (9, 32000), (3, 200001)]:
         say(f"safe3 bf16={bf16} rows={rows} cols={cols}")
