@@ -382,6 +382,22 @@ def test_split_forward_plan_and_specials(ons, orc):
     assert y3.data_ptr() == xd.data_ptr() and torch.equal(xd.view(torch.int32), y1.view(torch.int32))
 
 
+def test_split_launches_past_the_grid_cap(ons, orc):
+    """More (row, slice) units than one launch's 2^31 threads hold: the split
+    kernels stride over the rest (forward: 35.8M one-wave units; top-K: 4.8M
+    512-thread units)."""
+    x = workloads.normal(140000, 4, seed=140, scale=3.0)
+    say("split forward past the grid cap: 140000 rows x 256 slices")
+    assert_fp32_parity(run_split(ons, x, 256), orc.softmax(x, threads=8), "split forward, grid stride")
+    xt = workloads.normal(300000, 32, seed=300, scale=3.0)
+    say("split top-K past the grid cap: 300000 rows x 16 slices")
+    p, i = ons.os_softmax_topk(to_device(xt), 1, splits=16)
+    torch.cuda.synchronize()
+    pr, ir = orc.topk(xt, 1, threads=8)
+    assert np.array_equal(to_host(i), ir)
+    assert np.max(np.abs(to_host(p).astype(np.float64) - pr)) <= TOPK_PROB_ABS
+
+
 def test_split_forward_reuses_workspace(ons, orc):
     """A caller workspace filled with junk needs no initialisation; back-to-back calls reuse it."""
     ws = torch.full((ons.os_softmax_forward_workspace_bytes(4, 64),), 0x7F, dtype=torch.uint8, device="cuda")
