@@ -17,6 +17,8 @@
  *   - The paper summary, section 2, and "5.2 Hiện thực và tối ưu CUDA Online
  *     Softmax", section 1.1: safe softmax in three passes (max, sum, divide),
  *     the baseline.
+ *   - "6.2 FlashAttention V2 chi tiết", sections 6.1 and 7.1: the per-row
+ *     logsumexp L = m + log(d) kept in place of m and d.
  *
  * Conventions shared by every entry point
  *   Layout     row-major, contiguous, row stride == cols elements.
@@ -29,8 +31,9 @@
  *   dtype      OS_F32: float in, float out.  OS_BF16: bfloat16 in and out
  *              (raw 16-bit patterns), fp32 arithmetic inside, output rounded to
  *              nearest-even.
- *   Aliasing   `in == out` (exact alias) is allowed for the forward and safe
- *              entry points; any other overlap is undefined.
+ *   Aliasing   `in == out` (exact alias) is allowed for every forward entry
+ *              point (plain, tuned, logsumexp, split) and the safe baseline;
+ *              any other overlap is undefined.
  *   Sizes      0 <= cols <= OS_MAX_COLS; rows * cols * element size must fit in
  *              int64.
  *   Empty      rows == 0, or cols == 0 for the forward/safe entry points, is a
