@@ -1019,24 +1019,27 @@ __global__ void __launch_bounds__(256)
     k_topk_merge(float* probs, int* idx, int64_t rows, int K, int S, const State* ws_state,
                  const TopkEntry* ws_list) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
-    if (row >= rows) return;  // whole wavefronts leave together
-    const int64_t u0 = row * S;
-    State r = ws_state[u0];
-    for (int q = 1; q < S; ++q) r = oplus(r, ws_state[u0 + q]);
-    float out_v;
-    int out_i;
-    topk_of_lists<kTopKMaxSplits>(
-        S, K, lane,
-        [&](int l, int p, float& v, int& i) {
-            const TopkEntry e = ws_list[(u0 + l) * K + p];
-            v = e.v;
-            i = e.i;
-        },
-        out_v, out_i);
-    if (lane < K) {
-        probs[row * K + lane] = exp_e(out_v - r.m) * rcp(r.d);
-        idx[row * K + lane] = out_i;
+    // one row per wavefront; rows past the grid stride (no barrier here, so
+    // wavefronts may leave independently)
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; row < rows;
+         row += static_cast<int64_t>(gridDim.x) * 4) {
+        const int64_t u0 = row * S;
+        State r = ws_state[u0];
+        for (int q = 1; q < S; ++q) r = oplus(r, ws_state[u0 + q]);
+        float out_v;
+        int out_i;
+        topk_of_lists<kTopKMaxSplits>(
+            S, K, lane,
+            [&](int l, int p, float& v, int& i) {
+                const TopkEntry e = ws_list[(u0 + l) * K + p];
+                v = e.v;
+                i = e.i;
+            },
+            out_v, out_i);
+        if (lane < K) {
+            probs[row * K + lane] = exp_e(out_v - r.m) * rcp(r.d);
+            idx[row * K + lane] = out_i;
+        }
     }
 }
 

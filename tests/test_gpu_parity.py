@@ -385,7 +385,7 @@ def test_split_forward_plan_and_specials(ons, orc):
 def test_split_launches_past_the_grid_cap(ons, orc):
     """More (row, slice) units than one launch's 2^31 threads hold: the split
     kernels stride over the rest (forward: 35.8M one-wave units; top-K: 4.8M
-    512-thread units)."""
+    512-thread units; top-K merge: 34M rows at one per wavefront)."""
     x = workloads.normal(140000, 4, seed=140, scale=3.0)
     say("split forward past the grid cap: 140000 rows x 256 slices")
     assert_fp32_parity(run_split(ons, x, 256), orc.softmax(x, threads=8), "split forward, grid stride")
@@ -394,6 +394,15 @@ def test_split_launches_past_the_grid_cap(ons, orc):
     p, i = ons.os_softmax_topk(to_device(xt), 1, splits=16)
     torch.cuda.synchronize()
     pr, ir = orc.topk(xt, 1, threads=8)
+    assert np.array_equal(to_host(i), ir)
+    assert np.max(np.abs(to_host(p).astype(np.float64) - pr)) <= TOPK_PROB_ABS
+    # the split top-K's merge launch (one row per wavefront) past its own cap:
+    # more than 4 x 2^31 / 256 rows
+    xm = workloads.normal(34_000_000, 2, seed=34, scale=3.0)
+    say("split top-K merge past the grid cap: 34M rows x 2 slices")
+    p, i = ons.os_softmax_topk(to_device(xm), 1, splits=2)
+    torch.cuda.synchronize()
+    pr, ir = orc.topk(xm, 1, threads=16)
     assert np.array_equal(to_host(i), ir)
     assert np.max(np.abs(to_host(p).astype(np.float64) - pr)) <= TOPK_PROB_ABS
 
