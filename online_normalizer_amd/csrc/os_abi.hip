@@ -619,9 +619,8 @@ int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     const char* d = static_cast<const char*>(dst);
     if (s < d + bytes && d < s + bytes) return fail(OS_EINVAL, "%s: source and destination overlap", fn);
     const int64_t tiles = (bytes + 4095) / 4096;
-    if (tiles > INT32_MAX) return fail(OS_EINVAL, "%s: copy too large", fn);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_copy, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, static_cast<hipStream_t>(stream),
+    hipLaunchKernelGGL(k_copy, dim3(grid_for(tiles, 256, 0)), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const char*>(src), static_cast<char*>(dst), bytes);
     return launched(fn);
 }

@@ -1045,15 +1045,17 @@ __global__ void __launch_bounds__(256)
 
 // ---------------------------------------------------------------------------
 // Plain 128-bit copy (bandwidth reference and counter calibration): each
-// thread moves one 16-byte vector, 256-thread workgroups, one tile each.
+// thread moves one 16-byte vector, 256-thread workgroups, one 4 KiB tile each
+// (striding over further tiles past the grid cap).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_copy(const char* src, char* dst, int64_t bytes) {
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 4096;
-    const int64_t left = bytes - t0;
-    const uint32_t tile = static_cast<uint32_t>(left < 4096 ? left : 4096);
-    const Buf bs(src + t0, tile), bd(dst + t0, tile);
     const uint32_t off = threadIdx.x * 16u;
-    bd.store16(off, bs.load16<true>(off));
+    for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * 4096; t0 < bytes; t0 += static_cast<int64_t>(gridDim.x) * 4096) {
+        const int64_t left = bytes - t0;
+        const uint32_t tile = static_cast<uint32_t>(left < 4096 ? left : 4096);
+        const Buf bs(src + t0, tile), bd(dst + t0, tile);
+        bd.store16(off, bs.load16<true>(off));
+    }
 }
 
 // ---------------------------------------------------------------------------

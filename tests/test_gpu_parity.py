@@ -670,6 +670,18 @@ def test_copy_references(ons):
         ons.os_device_copy(x, y2)
         torch.cuda.synchronize()
         assert torch.equal(x, y) and torch.equal(x, y2)
+    # past the tiled copy's grid cap (2^31 threads = 2^23 tiles of 4 KiB): 32 GiB + 3 tiles
+    n = ((1 << 35) + 3 * 4096) // 4
+    say("tiled copy past the grid cap: 32 GiB + 12 KiB")
+    a = torch.empty(n, dtype=torch.int32, device="cuda")
+    a[: 1 << 20].random_()
+    a[-(1 << 20):].random_()
+    b = torch.zeros_like(a)
+    ons.os_device_copy(a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a[: 1 << 20], b[: 1 << 20]) and torch.equal(a[-(1 << 20):], b[-(1 << 20):])
+    del a, b
+    torch.cuda.empty_cache()
 
 
 # -- full-size configurations, in the launch configuration the benchmark times -------
