@@ -27,7 +27,9 @@
  *     unchanged; a row (or prefix) made only of -inf has the identity state
  *     (-inf, 0).  Its softmax is 0/0 = NaN.
  *   - NaN or +inf in a row makes every output of that row NaN (plain IEEE
- *     propagation through exp and the sum).
+ *     propagation through exp and the sum), d and the logsumexp included, also
+ *     when every other entry is -inf; m stays the maximum of the non-NaN
+ *     entries (-inf if there are none).
  *   - Top-K order is the total order (value descending, index ascending); the
  *     probability of a selected logit u is e^{u - m}/d over the whole row.
  *   - The logsumexp of a row is log(sum_j e^{x_j}), written as m + log(d)
@@ -66,8 +68,14 @@ static double row_max(const double *x, int64_t n)
 
 static double row_sum_exp(const double *x, int64_t n, double m)
 {
-    if (m == -INFINITY)
-        return 0.0; /* empty or all -inf: the identity state */
+    if (m == -INFINITY) {
+        /* No entry above -inf: the -inf entries contribute nothing (the
+         * identity state), but a NaN entry still makes the sum NaN. */
+        for (int64_t j = 0; j < n; ++j)
+            if (x[j] != x[j])
+                return NAN;
+        return 0.0;
+    }
     double d = 0.0;
     for (int64_t j = 0; j < n; ++j)
         d += exp(x[j] - m);

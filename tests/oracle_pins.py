@@ -304,6 +304,12 @@ def pin_logsumexp(o):
     assert o.logsumexp(np.zeros((2, 0), dtype=np.float32)).tolist() == [-np.inf, -np.inf]
     assert np.isnan(o.logsumexp(np.array([[1.0, np.nan]], dtype=np.float32))[0])
     assert np.isnan(o.logsumexp(np.array([[1.0, np.inf]], dtype=np.float32))[0])
+    # NaN next to nothing but -inf is still NaN (not the empty row's -inf)
+    z = np.array([[-np.inf, np.nan, -np.inf], [np.nan, np.nan, np.nan]], dtype=np.float32)
+    assert np.all(np.isnan(o.logsumexp(z)))
+    m, d = o.stats(z)
+    assert np.all(m == -np.inf) and np.all(np.isnan(d))
+    assert np.all(np.isnan(o.softmax(z)))
 
 
 PINS = [
