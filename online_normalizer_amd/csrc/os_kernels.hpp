@@ -105,7 +105,8 @@ __device__ __forceinline__ void store_slot(const Buf& b, uint32_t row_off, int v
 
 // Per-row statistics a forward launch may write besides y; each pointer may
 // be null.  m and d: the row's state ((-inf, 0) for an empty or all -inf
-// row).  lse: the logsumexp L = m + ln d, -inf for such rows.
+// row; m = -inf and d = NaN when the only entries above -inf are NaN).  lse:
+// the logsumexp L = m + ln d, -inf for an empty or all -inf row, NaN when d is.
 struct RowStats {
     float* m;
     float* d;
@@ -115,12 +116,15 @@ struct RowStats {
 __device__ __forceinline__ bool any_stats(const RowStats& o) { return (o.m != nullptr) | (o.lse != nullptr); }
 
 __device__ __forceinline__ void put_stats(const RowStats& o, int64_t row, State s) {
-    const bool empty = s.d == 0.0f;
+    // d >= 1 exactly whenever an entry above -inf was folded (the maximum
+    // contributes e^0), so a start-value maximum with d below 1 (0, or NaN
+    // from a NaN entry) means the row had no such entry
+    const bool no_entry = (s.m == kFloor) & !(s.d >= 1.0f);
     if (o.m != nullptr) {
-        o.m[row] = empty ? -INFINITY : s.m;
+        o.m[row] = no_entry ? -INFINITY : s.m;
         o.d[row] = s.d;
     }
-    if (o.lse != nullptr) o.lse[row] = empty ? -INFINITY : add_log_e(s.m, s.d);
+    if (o.lse != nullptr) o.lse[row] = s.d == 0.0f ? -INFINITY : add_log_e(s.m, s.d);
 }
 
 // ---------------------------------------------------------------------------

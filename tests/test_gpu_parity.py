@@ -478,11 +478,17 @@ def test_lse_special_rows(ons, orc):
         x[5, :] = -np.inf
         x[5, 1] = -3.0e38
         x[6, :] = -80.0
+        x[7, :] = -np.inf
+        x[7, cols // 2] = np.nan                # NaN beside nothing but -inf
         check_lse(ons, orc, x, f"special cols={cols}")
         _, L = ons.os_softmax_forward_lse(to_device(x), write_y=False)
         torch.cuda.synchronize()
         L = to_host(L)
-        assert L[1] == -np.inf and np.isnan(L[2]) and np.isnan(L[3])
+        assert L[1] == -np.inf and np.isnan(L[2]) and np.isnan(L[3]) and np.isnan(L[7])
+        m, d = ons.os_softmax_stats(to_device(x))
+        torch.cuda.synchronize()
+        m, d = to_host(m), to_host(d)
+        assert m[7] == -np.inf and np.isnan(d[7]) and m[1] == -np.inf and d[1] == 0.0
         assert L[5] == np.float32(-3.0e38)  # one finite entry: L = x exactly
         assert abs(float(L[4]) - (0.375 + math.log(cols))) <= lse_tol(np.array(0.375 + math.log(cols)))
     x = workloads.normal(5, 1, seed=2, scale=30.0)
