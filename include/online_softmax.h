@@ -44,9 +44,15 @@
  *   Errors     a negative status; nothing is launched on an error found while
  *              checking arguments, which happens before any HIP call.
  *              os_last_error() describes the last failure on the calling thread.
- *              Pointers must be aligned to their element size; 16-byte
- *              alignment of the row starts selects 128-bit accesses, anything
- *              else a slower per-element path (not an error).
+ *   Alignment  pointers must be aligned to their element size.  Every row is
+ *              moved with 128-bit accesses: rows whose starts are not 16-byte
+ *              aligned are read as the 16-byte blocks they overlap, so a read
+ *              may touch up to 15 bytes before a row range's first element or
+ *              after its last, never outside those blocks (and so never
+ *              outside a mapped page).  Writes touch only output elements:
+ *              whole blocks where out has in's offset within its 16-byte
+ *              block, single elements at the ends of rows and when the offsets
+ *              differ.
  */
 #ifndef ONLINE_SOFTMAX_H
 #define ONLINE_SOFTMAX_H
@@ -83,10 +89,12 @@ extern "C" {
  * sections 3.1 and 3.3; the normalising pass as in "5.2 Hiện thực và tối ưu
  * CUDA Online Softmax", section 2.2).
  *   in, out   [rows, cols] of `dtype`.
- *   The kernel is chosen from `cols` and `dtype`: rows short enough to stay in
- *   registers are read from HBM once (several rows per wavefront, one
- *   wavefront per row, or one workgroup per row); longer rows are streamed in
- *   two passes (fold, then normalise), reading the row twice.
+ *   The kernel is chosen from `cols`, `dtype` and the row alignment: rows of
+ *   up to 65536 elements stay in registers and are read from HBM once
+ *   (several rows per wavefront, one wavefront per row, or one workgroup per
+ *   row); rows of up to 262144 elements keep their first 65536 in registers
+ *   and read the rest twice; longer rows are streamed in two passes (fold,
+ *   then normalise), reading the row twice.
  *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
  */
 int os_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
@@ -98,10 +106,13 @@ int os_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, in
  *   lanes_per_row   lanes that share one row: 4, 8, 16, 32, 64, 128, 256, 512
  *                   or 1024 (register-resident kernels), or 0 for the
  *                   streaming two-pass kernel.
- *   vecs_per_lane   16-byte vectors held per lane (2, 4, 8 or 16; only the
+ *   vecs_per_lane   16-byte vectors held per lane (1, 2, 4, 8 or 16; only the
  *                   combinations built into the library are accepted).  The
  *                   shape must hold the row: lanes_per_row * vecs_per_lane *
- *                   (16 / element size) >= cols.  Ignored when lanes_per_row == 0.
+ *                   VEC >= cols, VEC = 16 / element size, and >= cols + VEC - 1
+ *                   when the row starts are not all 16-byte aligned (such a
+ *                   row may span one more 16-byte block).  Ignored when
+ *                   lanes_per_row == 0.
  *   grid_blocks     workgroups to launch (grid-stride over rows); 0 = automatic.
  *   Returns OS_OK, OS_EINVAL (shape too small or grid_blocks < 0),
  *   OS_EUNSUPPORTED (shape not built), or OS_ELAUNCH.
@@ -110,8 +121,12 @@ int os_softmax_forward_tuned(const void *in, void *out, int64_t rows, int64_t co
                              int lanes_per_row, int vecs_per_lane, int grid_blocks, void *stream);
 
 /*
- * The shape os_softmax_forward uses for (cols, dtype).  Host only: no HIP call.
- *   *lanes_per_row, *vecs_per_lane receive the shape (0, 0 for streaming).
+ * The shape os_softmax_forward uses for rows of `cols` elements of `dtype` in
+ * an array whose base is 16-byte aligned (the shape depends on whether the row
+ * starts are all 16-byte aligned, i.e. on cols * element size % 16 here).
+ * Host only: no HIP call.
+ *   *lanes_per_row, *vecs_per_lane receive the shape (0, 0 for rows longer
+ *   than the register-resident kernels hold).
  *   Returns OS_OK or OS_EINVAL.
  */
 int os_forward_plan(int64_t cols, int dtype, int *lanes_per_row, int *vecs_per_lane);
@@ -121,7 +136,10 @@ int os_forward_plan(int64_t cols, int dtype, int *lanes_per_row, int *vecs_per_l
  * output pass (paper summary, sections 3.1-3.3).
  *   in      [rows, cols] of `dtype`.
  *   m, d    [rows] float each.  A row with no entry above -inf (or cols == 0)
- *           gets the identity (-inf, 0).
+ *           gets the identity (-inf, 0).  A row holding NaN or +inf gets d NaN;
+ *           its m is the largest entry other than NaN, or -inf if there is
+ *           none above -inf (so also when that entry is -FLT_MAX and the row
+ *           holds a NaN).
  *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
  */
 int os_softmax_stats(const void *in, float *m, float *d, int64_t rows, int64_t cols, int dtype,

@@ -113,7 +113,7 @@ struct ResidentShape {
         }                                                                            \
     }
 
-const ResidentShape kResident[] = {
+constexpr ResidentShape kResident[] = {
     ONORM_RESIDENT(4, 1),     ONORM_RESIDENT(4, 2),     ONORM_RESIDENT(4, 4),
     ONORM_RESIDENT(8, 1),     ONORM_RESIDENT(8, 2),     ONORM_RESIDENT(8, 4),
     ONORM_RESIDENT(16, 1),    ONORM_RESIDENT(16, 2),    ONORM_RESIDENT(16, 4),
@@ -127,17 +127,33 @@ const ResidentShape kResident[] = {
 };
 constexpr int kNumResident = sizeof(kResident) / sizeof(kResident[0]);
 
-// Automatic choice, by the row's 16-byte vector count (next power of two),
-// from a sweep of every built shape on MI355X at ~0.5 GiB per launch: one
-// vector per lane up to 128 vectors (several rows per wavefront up to 64),
-// then two vectors per lane on up to 1024 lanes, then 1024 lanes with 4, 8
-// or 16 vectors.  Entry i covers rows of up to 4 << i vectors.
-const int kAutoF32[][2] = {{4, 1},   {8, 1},   {16, 1},    {32, 1},    {64, 1},    {128, 1},   {128, 2},
-                           {256, 2}, {512, 2}, {1024, 2},  {1024, 4},  {1024, 8},  {1024, 16}};
-const int kAutoBF16[][2] = {{4, 1},   {8, 1},   {16, 1},    {32, 1},    {64, 1},    {64, 2},    {128, 2},
-                            {256, 2}, {512, 2}, {1024, 2},  {1024, 4},  {1024, 8}};
-constexpr int kNumAutoF32 = sizeof(kAutoF32) / sizeof(kAutoF32[0]);
-constexpr int kNumAutoBF16 = sizeof(kAutoBF16) / sizeof(kAutoBF16[0]);
+// Automatic choice, by the number of 16-byte slots a row spans, from sweeps
+// of every built shape on MI355X at ~0.5 GiB per launch, with rows at both
+// ends and in the middle of every power-of-two bucket of slots, aligned and
+// not.  Entry {n, l, v} serves rows of up to n slots with l lanes of v
+// vectors.  A row just past a power of two runs fastest on half the lanes
+// with twice the vectors (its workgroups are smaller, or its wavefronts carry
+// more rows); unaligned rows (rows whose starts are not all 16-byte aligned)
+// favour shapes whose partial first and last slots fall in fewer vector steps.
+struct PlanEntry {
+    int max_slots, lpr, vpl;
+};
+constexpr PlanEntry kPlanF32[] = {
+    {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {24, 16, 2},      {32, 32, 1},      {48, 32, 2},
+    {64, 64, 1},     {128, 64, 2},     {256, 128, 2},    {512, 256, 2},    {640, 256, 4},    {1024, 512, 2},
+    {1536, 512, 4},  {2560, 512, 8},   {4096, 1024, 4},  {8192, 1024, 8},  {16384, 1024, 16}};
+constexpr PlanEntry kPlanF32Unaligned[] = {
+    {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {32, 32, 1},      {40, 32, 2},      {64, 64, 1},
+    {128, 64, 2},    {256, 64, 4},     {320, 128, 4},    {512, 256, 2},    {640, 256, 4},    {1024, 512, 2},
+    {2048, 512, 4},  {4096, 1024, 4},  {8192, 1024, 8},  {16384, 1024, 16}};
+constexpr PlanEntry kPlanBF16[] = {
+    {4, 4, 1},       {8, 8, 1},        {10, 8, 2},       {16, 16, 1},      {32, 16, 2},      {64, 32, 2},
+    {128, 64, 2},    {192, 64, 4},     {256, 128, 2},    {384, 64, 8},     {512, 256, 2},    {1024, 256, 4},
+    {2048, 256, 8},  {4096, 1024, 4},  {8192, 1024, 8}};
+constexpr PlanEntry kPlanBF16Unaligned[] = {
+    {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {32, 32, 1},      {48, 32, 2},      {64, 64, 1},
+    {80, 32, 4},     {128, 64, 2},     {256, 64, 4},     {320, 128, 4},    {512, 256, 2},    {640, 256, 4},
+    {1024, 512, 2},  {2048, 256, 8},   {4096, 512, 8},   {8192, 1024, 8}};
 
 const ResidentShape* find_shape(int lpr, int vpl, int dtype) {
     const int bf = dtype == OS_BF16 ? 1 : 0;
@@ -152,14 +168,53 @@ int64_t vectors_needed(int64_t cols, int dtype) {
     return (cols + vec - 1) / vec;
 }
 
-void auto_plan(int64_t cols, int dtype, int* lpr, int* vpl) {
-    const int64_t need = vectors_needed(cols, dtype);
-    const int(*table)[2] = dtype == OS_BF16 ? kAutoBF16 : kAutoF32;
-    const int n = dtype == OS_BF16 ? kNumAutoBF16 : kNumAutoF32;
+// 16-byte slots a row may span: its vectors, or, when row starts are not
+// 16-byte aligned, the 16-byte blocks it overlaps (up to VEC - 1 elements
+// more at its front).
+int64_t slots_needed(int64_t cols, int dtype, bool al) {
+    return vectors_needed(al ? cols : cols + 16 / elt_size(dtype) - 1, dtype);
+}
+
+// Every plan entry names a built shape (for bf16: one built for bf16) that
+// holds its slots, and the entries grow.
+template <size_t N>
+constexpr bool plan_ok(const PlanEntry (&t)[N], bool bf16) {
+    for (size_t i = 0; i < N; ++i) {
+        if (static_cast<int64_t>(t[i].lpr) * t[i].vpl < t[i].max_slots) return false;
+        if (i > 0 && t[i].max_slots <= t[i - 1].max_slots) return false;
+        bool built = false;
+        for (int k = 0; k < kNumResident; ++k)
+            built = built || (kResident[k].lpr == t[i].lpr && kResident[k].vpl == t[i].vpl &&
+                              kResident[k].fn[bf16 ? 1 : 0][0] != nullptr);
+        if (!built) return false;
+    }
+    return true;
+}
+static_assert(plan_ok(kPlanF32, false) && plan_ok(kPlanF32Unaligned, false), "fp32 plan names an unbuilt shape");
+static_assert(plan_ok(kPlanBF16, true) && plan_ok(kPlanBF16Unaligned, true), "bf16 plan names an unbuilt shape");
+template <size_t N>
+constexpr int last_slots(const PlanEntry (&t)[N]) {
+    return t[N - 1].max_slots;
+}
+static_assert(last_slots(kPlanF32) == 16384 && last_slots(kPlanF32Unaligned) == 16384 &&
+                  last_slots(kPlanBF16) == 8192 && last_slots(kPlanBF16Unaligned) == 8192,
+              "plans end at the register-resident limit (65536 elements)");
+
+void auto_plan(int64_t cols, int dtype, bool al, int* lpr, int* vpl) {
+    const int64_t need = slots_needed(cols, dtype, al);
+    const PlanEntry* t;
+    int n;
+    if (dtype == OS_BF16) {
+        t = al ? kPlanBF16 : kPlanBF16Unaligned;
+        n = al ? sizeof(kPlanBF16) / sizeof(PlanEntry) : sizeof(kPlanBF16Unaligned) / sizeof(PlanEntry);
+    } else {
+        t = al ? kPlanF32 : kPlanF32Unaligned;
+        n = al ? sizeof(kPlanF32) / sizeof(PlanEntry) : sizeof(kPlanF32Unaligned) / sizeof(PlanEntry);
+    }
     for (int i = 0; i < n; ++i) {
-        if (static_cast<int64_t>(table[i][0]) * table[i][1] >= need) {
-            *lpr = table[i][0];
-            *vpl = table[i][1];
+        if (need <= t[i].max_slots) {
+            *lpr = t[i].lpr;
+            *vpl = t[i].vpl;
             return;
         }
     }
@@ -243,26 +298,38 @@ int grid_for(int64_t groups, int block, int requested) {
 // small).
 constexpr int64_t kHybridMaxCols = 4 * 65536;
 
+// The register-resident shape os_softmax_forward takes for these rows
+// (lpr = 0: longer rows, hybrid or streaming).
+void plan_rows(const void* in, const void* out, int64_t cols, int dtype, int* lpr, int* vpl) {
+    auto_plan(cols, dtype, vector_ok(in, out, cols, dtype), lpr, vpl);
+}
+
+RowKernel hybrid_kernel(int dtype, bool al) {
+    if (dtype == OS_BF16) return al ? k_hybrid<true, 8, 2, true> : k_hybrid<true, 8, 2, false>;
+    return al ? k_hybrid<false, 16, 2, true> : k_hybrid<false, 16, 2, false>;
+}
+
 int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t rows,
              int64_t cols, int dtype, int lpr, int vpl, int grid_req, bool allow_hybrid, void* stream) {
     // Shape checks first: no HIP call happens before every argument is known good.
+    const bool al = vector_ok(in, out, cols, dtype);
     const ResidentShape* shape = nullptr;
     if (lpr != 0) {
         shape = find_shape(lpr, vpl, dtype);
         if (shape == nullptr)
             return fail(OS_EUNSUPPORTED, "%s: no kernel built for lanes_per_row=%d vecs_per_lane=%d", fn, lpr,
                         vpl);
-        if (static_cast<int64_t>(lpr) * vpl < vectors_needed(cols, dtype))
-            return fail(OS_EINVAL, "%s: lanes_per_row=%d x vecs_per_lane=%d cannot hold %lld columns", fn, lpr,
-                        vpl, (long long)cols);
+        if (static_cast<int64_t>(lpr) * vpl < slots_needed(cols, dtype, al))
+            return fail(OS_EINVAL,
+                        "%s: lanes_per_row=%d x vecs_per_lane=%d cannot hold %lld columns%s", fn, lpr, vpl,
+                        (long long)cols, al ? "" : " (rows not 16-byte aligned span one more 16-byte block)");
     }
-    const bool al = vector_ok(in, out, cols, dtype);
     const int bf = dtype == OS_BF16 ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape == nullptr) {
-        if (allow_hybrid && al && cols <= kHybridMaxCols) {
-            const RowKernel k = dtype == OS_BF16 ? k_hybrid<true, 8, 2, true> : k_hybrid<false, 16, 2, true>;
+        if (allow_hybrid && cols <= kHybridMaxCols) {
+            const RowKernel k = hybrid_kernel(dtype, al);
             hipLaunchKernelGGL(k, dim3(grid_for(rows, 1024, grid_req)), dim3(1024), 0, st, in, out, stats, rows,
                                static_cast<int>(cols));
             return launched(fn);
@@ -296,7 +363,8 @@ int os_forward_plan(int64_t cols, int dtype, int* lanes_per_row, int* vecs_per_l
     if (cols < 0 || cols > OS_MAX_COLS) return fail(OS_EINVAL, "os_forward_plan: cols %lld out of range", (long long)cols);
     if (lanes_per_row == nullptr || vecs_per_lane == nullptr)
         return fail(OS_EINVAL, "os_forward_plan: NULL output pointer");
-    auto_plan(cols, dtype, lanes_per_row, vecs_per_lane);
+    // rows of a 16-byte aligned array: aligned when the row bytes are a multiple of 16
+    auto_plan(cols, dtype, (cols * elt_size(dtype)) % 16 == 0, lanes_per_row, vecs_per_lane);
     return ok();
 }
 
@@ -306,7 +374,7 @@ int os_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, in
     if (rc == 1) return ok();
     if (rc != OS_OK) return rc;
     int lpr = 0, vpl = 0;
-    auto_plan(cols, dtype, &lpr, &vpl);
+    plan_rows(in, out, cols, dtype, &lpr, &vpl);
     return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, true, stream);
 }
 
@@ -334,7 +402,7 @@ int os_softmax_stats(const void* in, float* m, float* d, int64_t rows, int64_t c
     if (!aligned(m, 4) || !aligned(d, 4)) return fail(OS_EINVAL, "%s: m and d must be 4-byte aligned", fn);
     // cols == 0: every row is empty and gets the identity state; the input is never read.
     int lpr = 0, vpl = 0;
-    auto_plan(cols, dtype, &lpr, &vpl);
+    plan_rows(in, nullptr, cols, dtype, &lpr, &vpl);
     return run_rows(fn, cols == 0 ? nullptr : in, nullptr, RowStats{m, d, nullptr}, rows, cols, dtype, lpr, vpl, 0,
                     true, stream);
 }
@@ -349,7 +417,7 @@ int os_softmax_forward_lse(const void* in, void* out, float* lse, int64_t rows, 
     if (!aligned(lse, 4)) return fail(OS_EINVAL, "%s: lse must be 4-byte aligned", fn);
     // cols == 0: every row is empty, L = -inf; neither x nor y is touched.
     int lpr = 0, vpl = 0;
-    auto_plan(cols, dtype, &lpr, &vpl);
+    plan_rows(in, out, cols, dtype, &lpr, &vpl);
     return run_rows(fn, cols == 0 ? nullptr : in, cols == 0 ? nullptr : out, RowStats{nullptr, nullptr, lse}, rows,
                     cols, dtype, lpr, vpl, 0, true, stream);
 }
@@ -373,7 +441,7 @@ int os_forward_split_plan(int64_t rows, int64_t cols, int dtype) {
     // vectors (16 KB) (measured on MI355X over 1..256 rows of 128256 to 2^24
     // columns, fp32 and bf16).
     int lpr = 0, vpl = 0;
-    auto_plan(cols, dtype, &lpr, &vpl);
+    auto_plan(cols, dtype, true, &lpr, &vpl);
     if (lpr != 0) return 1;
     const int64_t vecs = vectors_needed(cols, dtype);
     int S = 1;
@@ -391,7 +459,7 @@ int os_softmax_forward_split(const void* in, void* out, int64_t rows, int64_t co
     if (rc != OS_OK) return rc;
     if (splits == 1) {
         int lpr = 0, vpl = 0;
-        auto_plan(cols, dtype, &lpr, &vpl);
+        plan_rows(in, out, cols, dtype, &lpr, &vpl);
         return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, true, stream);
     }
     if (!workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State))))
@@ -403,7 +471,7 @@ int os_softmax_forward_split(const void* in, void* out, int64_t rows, int64_t co
         return fail(OS_EINVAL, "%s: workspace has %lld bytes, needs %lld", fn, (long long)workspace_bytes,
                     (long long)need);
     const bool al = vector_ok(in, out, cols, dtype);
-    const int64_t seg_vec = (vectors_needed(cols, dtype) + splits - 1) / splits;
+    const int64_t seg_vec = (slots_needed(cols, dtype, al) + splits - 1) / splits;
     const int w = slice_waves(seg_vec);
     const int block = w * 64;
     const int64_t units = rows * splits;
@@ -435,7 +503,7 @@ int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, 
     const int bf = dtype == OS_BF16 ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     int lpr = 0, vpl = 0;
-    auto_plan(cols, dtype, &lpr, &vpl);
+    auto_plan(cols, dtype, al, &lpr, &vpl);
     (void)hipGetLastError();
     if (lpr != 0) {
         // rows that fit the register-resident geometry: same lanes and

@@ -5,14 +5,20 @@
 // forward, the fused softmax + top-K; the three-pass safe-softmax baseline
 // (same page, section 2); and two plain copies used as bandwidth references.
 //
-// Row layout: row-major, stride == cols.  Lanes address a row in 16-byte
-// vectors: vector slot vi covers elements [vi*VEC, vi*VEC + VEC).  ALIGNED
-// kernels move whole vectors with 128-bit buffer accesses (row starts 16-byte
-// aligned, cols a multiple of VEC); the others move the same slots element by
-// element.  Rows are read and written through buffer resources that cover
-// only the rows, or the row slice, a workgroup works on; elements past the end
-// read as -inf (e^{-inf} adds 0 to any state) and stores past the end are
-// dropped by the hardware.
+// Row layout: row-major, stride == cols.  Every kernel moves rows in 16-byte
+// vector slots with 128-bit buffer accesses.  ALIGNED kernels serve rows whose
+// starts are all 16-byte aligned (an aligned base, row bytes a multiple of 16):
+// slot vi of a row holds its elements [vi*VEC, vi*VEC + VEC).  The others take
+// the 16-byte blocks of memory a row overlaps as its slots: a row whose first
+// element lies `ph` elements into its block has slot vi = elements
+// [vi*VEC - ph, vi*VEC - ph + VEC), and slot entries outside the row are
+// masked by their index.  Rows are read and written through buffer resources
+// that cover only the rows, or the row slice, a workgroup works on, widened to
+// whole 16-byte blocks: every block such a resource covers holds an element of
+// the row range, so no access leaves the array's pages (memory is mapped in
+// pages, which 16-byte blocks never straddle).  Masked entries read as -inf
+// (e^{-inf} adds 0 to any state); stores outside the resource are dropped by
+// the hardware, and stores never touch an element outside the row.
 #pragma once
 
 #include "os_device.hpp"
@@ -22,83 +28,138 @@ namespace onorm {
 constexpr int kTopKMax = 32;
 constexpr int kTopKMaxSplits = 16;
 
-template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ int vec_count(int cols) {
-    constexpr int VEC = Elt<BF16>::kVec;
-    return ALIGNED ? cols / VEC : (cols + VEC - 1) / VEC;
-}
-
 // An offset no buffer resource here reaches: accesses there are dropped.
 constexpr uint32_t kOutside = 0x80000000u;
 
-// Load vector slot vi of a row into v[VEC]; -inf where the slot or element is
-// outside the row (or the row is not live).  `row_off` is the byte offset of
-// the row inside the buffer resource.
-template <bool BF16, bool ALIGNED, bool STREAM>
-__device__ __forceinline__ void load_slot(const Buf& b, uint32_t row_off, int vi, int nvec, int cols, bool live,
-                                          float* v) {
-    using E = Elt<BF16>;
-    constexpr int VEC = E::kVec;
-    if constexpr (ALIGNED) {
-        E::unpack(b.load16<STREAM>(row_off + static_cast<uint32_t>(vi) * 16u), v);
-        const bool ok = live && vi < nvec;
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) v[k] = ok ? v[k] : -INFINITY;
-    } else {
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            const int e = vi * VEC + k;
-            const bool ok = live && e < cols;
-            const float t = E::load1(b, ok ? row_off + static_cast<uint32_t>(e) * E::kSize : kOutside);
-            v[k] = ok ? t : -INFINITY;
-        }
-    }
+// Where a row sits in its buffer resource: its first element lies `ph`
+// elements into the 16-byte block at byte `blk` (ph = 0 when ALIGNED).  Slot
+// vi is the block at blk + 16 vi; element e of the row is at byte
+// blk + (e + ph) * element size.
+struct RowAt {
+    uint32_t blk;
+    int ph;
+};
+
+// A buffer resource's base and size over n elements from element e0 of the
+// array at p, widened to whole 16-byte blocks unless ALIGNED; `lead` is the
+// byte offset of element e0 in it (0 when ALIGNED).
+struct Span {
+    const char* base;
+    uint32_t bytes;
+    uint32_t lead;
+};
+
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ Span span_of(const void* p, int64_t e0, int64_t n) {
+    constexpr int SZ = Elt<BF16>::kSize;
+    const char* a = static_cast<const char*>(p) + e0 * SZ;
+    const uint32_t bytes = static_cast<uint32_t>(n * SZ);
+    if constexpr (ALIGNED) return Span{a, bytes, 0u};
+    const uint32_t lead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a) & 15u);
+    return Span{a - lead, (lead + bytes + 15u) & ~15u, lead};
 }
 
-// Two-phase form used by the register-resident kernels: issue the raw 128-bit
-// loads of all VPL slots, fence the scheduler, then unpack.  Without the
-// fence the scheduler may sink each load next to its unpack code, and every
-// load then waits for the previous one to return.
+// The row whose first element is at byte `start` of a resource.
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ RowAt row_at(uint32_t start) {
+    if constexpr (ALIGNED) return RowAt{start, 0};
+    return RowAt{start & ~15u, static_cast<int>((start & 15u) / Elt<BF16>::kSize)};
+}
+
+// Slots a row of `cols` elements spans.
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ int slot_count(int cols, int ph) {
+    constexpr int VEC = Elt<BF16>::kVec;
+    return ALIGNED ? cols / VEC : (cols + ph + VEC - 1) / VEC;
+}
+
+// True when in and out rows lie at the same offset within their 16-byte
+// blocks (then a slot of the input is a whole block of the output too).
+__device__ __forceinline__ bool same_phase(const void* a, const void* b) {
+    return ((reinterpret_cast<uintptr_t>(a) ^ reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
+}
+
+// Load VPL slots first, first + stride, ... of row r into x: issue the raw
+// 128-bit loads of all of them, fence the scheduler, then unpack.  Without
+// the fence the scheduler may sink each load next to its unpack code, and
+// every load then waits for the previous one to return.  Slots at or past
+// `lim` and rows that are not live are not fetched (their loads go outside
+// the resource); their entries, and (unaligned rows) entries outside the
+// row's elements, become -inf.
 template <bool BF16, int VPL, bool ALIGNED, bool STREAM>
-__device__ __forceinline__ void load_slots(const Buf& b, uint32_t row_off, int first, int stride, int nvec,
-                                           int cols, bool live, float (&x)[VPL][Elt<BF16>::kVec]) {
+__device__ __forceinline__ void load_slots(const Buf& b, RowAt r, int first, int stride, int lim, int cols,
+                                           bool live, float (&x)[VPL][Elt<BF16>::kVec]) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
-    if constexpr (ALIGNED) {
-        u32x4 raw[VPL];
+    u32x4 raw[VPL];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            raw[v] = b.load16<STREAM>(row_off + static_cast<uint32_t>(first + v * stride) * 16u);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int v = 0; v < VPL; ++v) {
+        const int slot = first + v * stride;
+        raw[v] = b.load16<STREAM>(live && slot < lim ? r.blk + static_cast<uint32_t>(slot) * 16u : kOutside);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-            E::unpack(raw[v], x[v]);
-            const bool ok = live && (first + v * stride) < nvec;
+    for (int v = 0; v < VPL; ++v) {
+        E::unpack(raw[v], x[v]);
+        const int slot = first + v * stride;
+        const bool ok = live && slot < lim;
+        if constexpr (ALIGNED) {
 #pragma unroll
             for (int k = 0; k < VEC; ++k) x[v][k] = ok ? x[v][k] : -INFINITY;
-        }
-    } else {
+        } else {
+            // only a row's first and last slots are partial: mask entry by
+            // entry in a branch the other lanes skip
+            const int e0 = slot * VEC - r.ph;  // row index of the slot's first entry
+            if (!(ok && e0 >= 0 && e0 + VEC <= cols)) {
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) load_slot<BF16, false, STREAM>(b, row_off, first + v * stride, nvec, cols, live, x[v]);
+                for (int k = 0; k < VEC; ++k)
+                    x[v][k] =
+                        (ok && static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols)) ? x[v][k] : -INFINITY;
+            }
+        }
     }
 }
 
-// Store slot vi of a row; slots / elements outside the row are sent to an
-// offset outside the resource, which the hardware drops.
+// Store slot vi of an input row with phase `ph` (values v[VEC]) to output row
+// ro.  Only the row's own elements are written: a slot wholly inside the row
+// goes out as one 128-bit store when the output has the input's phase
+// (`same`), entries at the row's ends, and every entry when the phases differ,
+// element by element.  Slots at or past `lim` and rows that are not live
+// store nothing.
 template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ void store_slot(const Buf& b, uint32_t row_off, int vi, int nvec, int cols, bool live,
-                                           const float* v) {
+__device__ __forceinline__ void store_slot(const Buf& b, RowAt ro, int ph, bool same, int vi, int lim, int cols,
+                                           bool live, const float* v) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
+    const bool ok = live && vi < lim;
     if constexpr (ALIGNED) {
-        const bool ok = live && vi < nvec;
-        b.store16(ok ? row_off + static_cast<uint32_t>(vi) * 16u : kOutside, E::pack(v));
+        b.store16(ok ? ro.blk + static_cast<uint32_t>(vi) * 16u : kOutside, E::pack(v));
     } else {
+        const int e0 = vi * VEC - ph;
+        if (same) {
+            const bool whole = ok && e0 >= 0 && e0 + VEC <= cols;
+            b.store16(whole ? ro.blk + static_cast<uint32_t>(vi) * 16u : kOutside, E::pack(v));
+            if (ok && !whole) {
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            const int e = vi * VEC + k;
-            const bool ok = live && e < cols;
-            E::store1(b, ok ? row_off + static_cast<uint32_t>(e) * E::kSize : kOutside, v[k]);
+                for (int k = 0; k < VEC; ++k) {
+                    const int e = e0 + k;
+                    E::store1(b,
+                              static_cast<uint32_t>(e) < static_cast<uint32_t>(cols)
+                                  ? ro.blk + static_cast<uint32_t>(e + ro.ph) * E::kSize
+                                  : kOutside,
+                              v[k]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const int e = e0 + k;
+                E::store1(b,
+                          (ok && static_cast<uint32_t>(e) < static_cast<uint32_t>(cols))
+                              ? ro.blk + static_cast<uint32_t>(e + ro.ph) * E::kSize
+                              : kOutside,
+                          v[k]);
+            }
         }
     }
 }
@@ -156,8 +217,8 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
     const int tid = threadIdx.x;
     const int j = tid % LPR;
     const int g = tid / LPR;
-    const int nvec = vec_count<BF16, ALIGNED>(cols);
     const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    const bool same = same_phase(in, out);
     int par = 0;
 
     for (int64_t rb = blockIdx.x; rb * RPB < rows; rb += gridDim.x) {
@@ -167,11 +228,13 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         const int64_t nrows = (rows - row0) < RPB ? (rows - row0) : RPB;
         const int64_t row = row0 + g;
         const bool live = g < nrows;
-        const uint32_t row_off = static_cast<uint32_t>(g) * row_bytes;
-        const Buf bin(static_cast<const char*>(in) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
+        const Span si = span_of<BF16, ALIGNED>(in, row0 * cols, nrows * cols);
+        const Buf bin(si.base, si.bytes);
+        const RowAt ri = row_at<BF16, ALIGNED>(si.lead + static_cast<uint32_t>(g) * row_bytes);
+        const int ns = slot_count<BF16, ALIGNED>(cols, ri.ph);
 
         float x[VPL][VEC];
-        load_slots<BF16, VPL, ALIGNED, true>(bin, row_off, j, LPR, nvec, cols, live, x);
+        load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, ns, cols, live, x);
 
         float ml = kFloor;
 #pragma unroll
@@ -200,12 +263,14 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         if (any_stats(st) && live && j == 0) put_stats(st, row, s);
         if (out != nullptr) {
             const float scale = exp_e(ml - s.m) * rcp(s.d);
-            const Buf bout(static_cast<char*>(out) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
+            const Span so = span_of<BF16, ALIGNED>(out, row0 * cols, nrows * cols);
+            const Buf bout(so.base, so.bytes);
+            const RowAt ro = row_at<BF16, ALIGNED>(so.lead + static_cast<uint32_t>(g) * row_bytes);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) x[v][k] *= scale;
-                store_slot<BF16, ALIGNED>(bout, row_off, v * LPR + j, nvec, cols, live, x[v]);
+                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, ns, cols, live, x[v]);
             }
         }
     }
@@ -228,16 +293,18 @@ __global__ void __launch_bounds__(W * 64)
     __shared__ State lds[2][W];
 
     const int tid = threadIdx.x;
-    const int nvec = vec_count<BF16, ALIGNED>(cols);
-    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    const bool same = same_phase(in, out);
     int par = 0;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const Buf bin(static_cast<const char*>(in) + row * row_bytes, row_bytes);
+        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const Buf bin(si.base, si.bytes);
+        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
+        const int nvec = slot_count<BF16, ALIGNED>(cols, ri.ph);
         float ml = kFloor, dl = 0.0f;
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-            load_slots<BF16, U, ALIGNED, false>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+            load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
             float mc = kFloor;
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -264,15 +331,17 @@ __global__ void __launch_bounds__(W * 64)
         if (any_stats(st) && tid == 0) put_stats(st, row, s);
         if (out != nullptr) {
             const float inv_d = rcp(s.d);
-            const Buf bout(static_cast<char*>(out) + row * row_bytes, row_bytes);
+            const Span so = span_of<BF16, ALIGNED>(out, row * cols, cols);
+            const Buf bout(so.base, so.bytes);
+            const RowAt ro = row_at<BF16, ALIGNED>(so.lead);
             for (int base = 0; base < nvec; base += BLOCK * U) {
                 float x[U][VEC];
-                load_slots<BF16, U, ALIGNED, true>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+                load_slots<BF16, U, ALIGNED, true>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - s.m) * inv_d;
-                    store_slot<BF16, ALIGNED>(bout, 0u, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u]);
                 }
             }
         }
@@ -300,14 +369,16 @@ __global__ void __launch_bounds__(1024)
     __shared__ State lds[2][W];
 
     const int tid = threadIdx.x;
-    const int nvec = vec_count<BF16, ALIGNED>(cols);
-    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    const bool same = same_phase(in, out);
     int par = 0;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const Buf bin(static_cast<const char*>(in) + row * row_bytes, row_bytes);
+        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const Buf bin(si.base, si.bytes);
+        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
+        const int nvec = slot_count<BF16, ALIGNED>(cols, ri.ph);
         float xr[VPL][VEC];
-        load_slots<BF16, VPL, ALIGNED, true>(bin, 0u, tid, BLOCK, nvec, cols, true, xr);
+        load_slots<BF16, VPL, ALIGNED, true>(bin, ri, tid, BLOCK, nvec, cols, true, xr);
         float mr = kFloor;
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
@@ -324,7 +395,7 @@ __global__ void __launch_bounds__(1024)
         float ml = mr;
         for (int base = RES; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-            load_slots<BF16, U, ALIGNED, false>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+            load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
             float mc = kFloor;
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -350,21 +421,23 @@ __global__ void __launch_bounds__(1024)
         if (out != nullptr) {
             const float inv_d = rcp(s.d);
             const float scale = exp_e(mr - s.m) * inv_d;
-            const Buf bout(static_cast<char*>(out) + row * row_bytes, row_bytes);
+            const Span so = span_of<BF16, ALIGNED>(out, row * cols, cols);
+            const Buf bout(so.base, so.bytes);
+            const RowAt ro = row_at<BF16, ALIGNED>(so.lead);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) xr[v][k] *= scale;
-                store_slot<BF16, ALIGNED>(bout, 0u, v * BLOCK + tid, nvec, cols, true, xr[v]);
+                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * BLOCK + tid, nvec, cols, true, xr[v]);
             }
             for (int base = RES; base < nvec; base += BLOCK * U) {
                 float x[U][VEC];
-                load_slots<BF16, U, ALIGNED, true>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+                load_slots<BF16, U, ALIGNED, true>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - s.m) * inv_d;
-                    store_slot<BF16, ALIGNED>(bout, 0u, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u]);
                 }
             }
         }
@@ -386,17 +459,19 @@ __global__ void __launch_bounds__(W * 64)
     __shared__ float lds_d[2][W];
 
     const int tid = threadIdx.x;
-    const int nvec = vec_count<BF16, ALIGNED>(cols);
-    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    const bool same = same_phase(in, out);
     int par = 0;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const Buf bin(static_cast<const char*>(in) + row * row_bytes, row_bytes);
+        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const Buf bin(si.base, si.bytes);
+        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
+        const int nvec = slot_count<BF16, ALIGNED>(cols, ri.ph);
         // pass 1: maximum
         float m = kFloor;
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-            load_slots<BF16, U, ALIGNED, false>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+            load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -414,7 +489,7 @@ __global__ void __launch_bounds__(W * 64)
         float d = 0.0f;
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-            load_slots<BF16, U, ALIGNED, false>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+            load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -431,15 +506,17 @@ __global__ void __launch_bounds__(W * 64)
         }
         // pass 3: normalise and store
         const float inv_d = rcp(d);
-        const Buf bout(static_cast<char*>(out) + row * row_bytes, row_bytes);
+        const Span so = span_of<BF16, ALIGNED>(out, row * cols, cols);
+        const Buf bout(so.base, so.bytes);
+        const RowAt ro = row_at<BF16, ALIGNED>(so.lead);
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
-            load_slots<BF16, U, ALIGNED, true>(bin, 0u, base + tid, BLOCK, nvec, cols, true, x);
+            load_slots<BF16, U, ALIGNED, true>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - m) * inv_d;
-                store_slot<BF16, ALIGNED>(bout, 0u, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u]);
             }
         }
     }
@@ -468,20 +545,22 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
     const int tid = threadIdx.x;
     const int j = tid % LPR;
     const int g = tid / LPR;
-    const int nvec = vec_count<BF16, ALIGNED>(cols);
     const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    const bool same = same_phase(in, out);
     int par = 0;
 
     for (int64_t rb = blockIdx.x; rb * RPB < rows; rb += gridDim.x) {
         const int64_t row0 = rb * RPB;
         const int64_t nrows = (rows - row0) < RPB ? (rows - row0) : RPB;
         const bool live = g < nrows;
-        const uint32_t row_off = static_cast<uint32_t>(g) * row_bytes;
-        const Buf bin(static_cast<const char*>(in) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
+        const Span si = span_of<BF16, ALIGNED>(in, row0 * cols, nrows * cols);
+        const Buf bin(si.base, si.bytes);
+        const RowAt ri = row_at<BF16, ALIGNED>(si.lead + static_cast<uint32_t>(g) * row_bytes);
+        const int nvec = slot_count<BF16, ALIGNED>(cols, ri.ph);
         float x[VPL][VEC];
 
         // pass 1: maximum
-        load_slots<BF16, VPL, ALIGNED, false>(bin, row_off, j, LPR, nvec, cols, live, x);
+        load_slots<BF16, VPL, ALIGNED, false>(bin, ri, j, LPR, nvec, cols, live, x);
         float m = kFloor;
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
@@ -496,7 +575,7 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
             for (int w = 1; w < W; ++w) m = fmaxf(m, lds_m[par][w]);
         }
         // pass 2: sum of e^{x - m}
-        load_slots<BF16, VPL, ALIGNED, false>(bin, row_off, j, LPR, nvec, cols, live, x);
+        load_slots<BF16, VPL, ALIGNED, false>(bin, ri, j, LPR, nvec, cols, live, x);
         float d = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
@@ -512,14 +591,16 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
             par ^= 1;
         }
         // pass 3: normalise and store
-        load_slots<BF16, VPL, ALIGNED, true>(bin, row_off, j, LPR, nvec, cols, live, x);
+        load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, nvec, cols, live, x);
         const float inv_d = rcp(d);
-        const Buf bout(static_cast<char*>(out) + row0 * row_bytes, static_cast<uint32_t>(nrows) * row_bytes);
+        const Span so = span_of<BF16, ALIGNED>(out, row0 * cols, nrows * cols);
+        const Buf bout(so.base, so.bytes);
+        const RowAt ro = row_at<BF16, ALIGNED>(so.lead + static_cast<uint32_t>(g) * row_bytes);
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
 #pragma unroll
             for (int k = 0; k < VEC; ++k) x[v][k] = exp_e(x[v][k] - m) * inv_d;
-            store_slot<BF16, ALIGNED>(bout, row_off, v * LPR + j, nvec, cols, live, x[v]);
+            store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, nvec, cols, live, x[v]);
         }
     }
 }
@@ -538,36 +619,18 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
 // touch no memory and stores past it are dropped.
 // ---------------------------------------------------------------------------
 struct Slice {
-    int v0, v1;       // vector slots [v0, v1) of the row
-    uint32_t bytes;   // bytes of the row from its start to the end of the slice
+    int v0, v1;      // vector slots [v0, v1) of the row
+    uint32_t bytes;  // resource bytes from the row's first block to the end of the slice
 };
 
-template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ Slice slice_of(int seg, int S, int cols) {
-    using E = Elt<BF16>;
-    const int nvec = vec_count<BF16, ALIGNED>(cols);
-    const int seg_vec = (nvec + S - 1) / S;
-    const int v0 = seg * seg_vec < nvec ? seg * seg_vec : nvec;
-    const int v1 = v0 + seg_vec < nvec ? v0 + seg_vec : nvec;
-    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
-    const uint32_t end = static_cast<uint32_t>(v1) * static_cast<uint32_t>(E::kVec * E::kSize);
-    return Slice{v0, v1, end < row_bytes ? end : row_bytes};
-}
-
-// U slots per lane from slot `base`: lane tid reads slots base + u * BLOCK + tid;
-// slots at or past v1 become -inf.
-template <bool BF16, int BLOCK, int U, bool ALIGNED, bool STREAM>
-__device__ __forceinline__ void load_tile(const Buf& b, int base, int tid, int v1, int cols,
-                                          float (&x)[U][Elt<BF16>::kVec]) {
-    if constexpr (ALIGNED) {
-        load_slots<BF16, U, true, STREAM>(b, 0u, base + tid, BLOCK, v1, cols, true, x);
-    } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int slot = base + u * BLOCK + tid;
-            load_slot<BF16, false, STREAM>(b, 0u, slot, v1, cols, slot < v1, x[u]);
-        }
-    }
+// Slice `seg` of S over a row of `ns` slots whose widened span has
+// `span_bytes` bytes.
+__device__ __forceinline__ Slice slice_of(int seg, int S, int ns, uint32_t span_bytes) {
+    const int seg_vec = (ns + S - 1) / S;
+    const int v0 = seg * seg_vec < ns ? seg * seg_vec : ns;
+    const int v1 = v0 + seg_vec < ns ? v0 + seg_vec : ns;
+    const uint32_t end = static_cast<uint32_t>(v1) * 16u;
+    return Slice{v0, v1, end < span_bytes ? end : span_bytes};
 }
 
 template <bool BF16, int W, int U, bool ALIGNED>
@@ -578,17 +641,19 @@ __global__ void __launch_bounds__(W * 64)
     constexpr int BLOCK = W * 64;
     __shared__ State lds[2][W];
     const int tid = threadIdx.x;
-    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
     const int64_t units = rows * S;
     int par = 0;
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t row = unit / S;
-        const Slice sl = slice_of<BF16, ALIGNED>(static_cast<int>(unit - row * S), S, cols);
-        const Buf bin(static_cast<const char*>(in) + row * row_bytes, sl.bytes);
+        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
+        const Slice sl =
+            slice_of(static_cast<int>(unit - row * S), S, slot_count<BF16, ALIGNED>(cols, ri.ph), si.bytes);
+        const Buf bin(si.base, sl.bytes);
         float ml = kFloor, dl = 0.0f;
         for (int base = sl.v0; base < sl.v1; base += BLOCK * U) {
             float x[U][VEC];
-            load_tile<BF16, BLOCK, U, ALIGNED, false>(bin, base, tid, sl.v1, cols, x);
+            load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, sl.v1, cols, true, x);
             float mc = kFloor;
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -624,11 +689,14 @@ __global__ void __launch_bounds__(W * 64)
     constexpr int BLOCK = W * 64;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int64_t row_bytes = static_cast<int64_t>(cols) * E::kSize;
     const int64_t units = rows * S;
+    const bool same = same_phase(in, out);
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t row = unit / S;
-        const Slice sl = slice_of<BF16, ALIGNED>(static_cast<int>(unit - row * S), S, cols);
+        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
+        const Slice sl =
+            slice_of(static_cast<int>(unit - row * S), S, slot_count<BF16, ALIGNED>(cols, ri.ph), si.bytes);
         // the row's S slice states: lane l folds states l, l + 64, ... in
         // order, then the wave merges the 64 lane states (same bits in every
         // lane, and in every workgroup of the row)
@@ -637,17 +705,18 @@ __global__ void __launch_bounds__(W * 64)
         t = group_merge<64>(t);
         const float m = t.m;
         const float inv_d = rcp(t.d);
-        const Buf bin(static_cast<const char*>(in) + row * row_bytes, sl.bytes);
-        const Buf bout(static_cast<char*>(out) + row * row_bytes, sl.bytes);
+        const Buf bin(si.base, sl.bytes);
+        const Span so = span_of<BF16, ALIGNED>(out, row * cols, cols);
+        const Buf bout(so.base, so.bytes);
+        const RowAt ro = row_at<BF16, ALIGNED>(so.lead);
         for (int base = sl.v0; base < sl.v1; base += BLOCK * U) {
             float x[U][VEC];
-            load_tile<BF16, BLOCK, U, ALIGNED, true>(bin, base, tid, sl.v1, cols, x);
+            load_slots<BF16, U, ALIGNED, true>(bin, ri, base + tid, BLOCK, sl.v1, cols, true, x);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int slot = base + u * BLOCK + tid;
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - m) * inv_d;
-                store_slot<BF16, ALIGNED>(bout, 0u, slot, sl.v1, cols, slot < sl.v1, x[u]);
+                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, sl.v1, cols, true, x[u]);
             }
         }
     }
@@ -864,21 +933,18 @@ __global__ void __launch_bounds__(W * 64)
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
     const uint64_t kmask = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
-    const int nvec = vec_count<BF16, ALIGNED>(cols);
-    const int seg_vec = SPLIT ? (nvec + S - 1) / S : nvec;
     const int64_t units = SPLIT ? rows * S : rows;
-    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
 
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t row = SPLIT ? unit / S : unit;
         const int seg = SPLIT ? static_cast<int>(unit - row * S) : 0;
-        const int v0 = seg * seg_vec;
-        const int v1 = (v0 + seg_vec < nvec) ? v0 + seg_vec : nvec;
+        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const int ph = row_at<BF16, ALIGNED>(si.lead).ph;  // the row's first block is at byte 0
         // The resource ends with the segment, so loads issued ahead past its
         // end (into the next segment or past the row) touch no memory.
-        const uint32_t seg_end = static_cast<uint32_t>(v1) * 16u;
-        const Buf bin(static_cast<const char*>(in) + row * static_cast<int64_t>(row_bytes),
-                      seg_end < row_bytes ? seg_end : row_bytes);
+        const Slice sl = slice_of(seg, SPLIT ? S : 1, slot_count<BF16, ALIGNED>(cols, ph), si.bytes);
+        const int v0 = sl.v0, v1 = sl.v1;
+        const Buf bin(si.base, sl.bytes);
         if (tid == 0) s_thr = ordered_bits(-INFINITY);
         if (tid < 128) s_rank[tid / 64][tid % 64] = 0;
         __syncthreads();
@@ -891,16 +957,17 @@ __global__ void __launch_bounds__(W * 64)
         const int refresh = ntiles >= 4 ? ntiles / 4 : -1;  // tile index of the refreshed bound
         int t = 0;
 
-        // One tile: unpack the raw loads (slots past the segment become
-        // -inf), issue the next tile's loads into the same registers, fold
-        // (m, d), then look for candidates.
+        // One tile: unpack the raw loads (entries outside the segment or the
+        // row become -inf), issue the next tile's loads into the same
+        // registers, fold (m, d), then look for candidates.
         auto tile = [&](u32x4 (&raw)[U], const int base) {
             float x[U][VEC];
-            if constexpr (ALIGNED) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) E::unpack(raw[u], x[u]);
-                // only a segment's last tile can hold slots past its end (read
-                // as 0 by the range check); the test is uniform
+            for (int u = 0; u < U; ++u) E::unpack(raw[u], x[u]);
+            // Only a segment's last tile can hold slots past its end (read as
+            // 0 by the range check), and, for an unaligned row, its first and
+            // last tiles entries outside the row; the tests are uniform.
+            if constexpr (ALIGNED) {
                 if (base + STEP > v1) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
@@ -909,17 +976,24 @@ __global__ void __launch_bounds__(W * 64)
                         for (int k = 0; k < VEC; ++k) x[u][k] = ok ? x[u][k] : -INFINITY;
                     }
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    raw[u] = bin.load16<true>(static_cast<uint32_t>(base + STEP + u * BLOCK + tid) * 16u);
-                __builtin_amdgcn_sched_barrier(0);
             } else {
+                if (base == v0 || base + STEP >= v1) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int slot = base + u * BLOCK + tid;
-                    load_slot<BF16, false, true>(bin, 0u, slot, v1, cols, slot < v1, x[u]);
+                    for (int u = 0; u < U; ++u) {
+                        const int slot = base + u * BLOCK + tid;
+                        const int e0 = slot * VEC - ph;
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k)
+                            x[u][k] = (slot < v1 && static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols))
+                                          ? x[u][k]
+                                          : -INFINITY;
+                    }
                 }
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                raw[u] = bin.load16<true>(static_cast<uint32_t>(base + STEP + u * BLOCK + tid) * 16u);
+            __builtin_amdgcn_sched_barrier(0);
 
             float mx = -INFINITY;
 #pragma unroll
@@ -960,9 +1034,10 @@ __global__ void __launch_bounds__(W * 64)
                         while (mask != 0) {
                             const int l = __builtin_ctzll(mask);
                             mask &= mask - 1;
-                            const int i = (wave_slot0 + l) * VEC + k;
+                            const int i = (wave_slot0 + l) * VEC + k - ph;  // column index
                             const float v = readlane(x[u][k], l);
-                            if ((wave_slot0 + l < v1) & (i < cols)) list_insert(L, I, v, i, K, lane, kmask);
+                            if ((wave_slot0 + l < v1) & (static_cast<uint32_t>(i) < static_cast<uint32_t>(cols)))
+                                list_insert(L, I, v, i, K, lane, kmask);
                         }
                     }
                 }
@@ -980,10 +1055,8 @@ __global__ void __launch_bounds__(W * 64)
         // tile are in flight while one is folded.  Loads past the end of the
         // segment touch no memory (buffer range check).
         u32x4 raw[U];
-        if constexpr (ALIGNED) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(v0 + u * BLOCK + tid) * 16u);
-        }
+        for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(v0 + u * BLOCK + tid) * 16u);
         for (int base = v0; base < v1; base += STEP) tile(raw, base);
 
         const State st = group_merge<64>(State{ml, dl});

@@ -90,6 +90,13 @@ def test_tuned_validation(L, ons):
     assert rc == EUNSUP  # that shape exists for fp32 only
     rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 1025, F32, 64, 4, 0, None)
     assert rc == EINVAL and "cannot hold" in ons.os_last_error()
+    # rows that are not 16-byte aligned span up to one more 16-byte block
+    rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 1023, F32, 64, 4, 0, None)
+    assert rc == EINVAL and "16-byte block" in ons.os_last_error()
+    rc = L.os_softmax_forward_tuned(FAKE + 4, FAKE + 4, 4, 1024, F32, 64, 4, 0, None)
+    assert rc == EINVAL and "16-byte block" in ons.os_last_error()
+    rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 2042, BF16, 64, 4, 0, None)
+    assert rc == EINVAL and "16-byte block" in ons.os_last_error()
     rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 64, F32, 64, 4, -1, None)
     assert rc == EINVAL
     rc = L.os_softmax_forward_tuned(FAKE, FAKE, 4, 64, F32, -4, 4, 0, None)
@@ -225,11 +232,18 @@ def test_forward_plan(ons):
     assert ons.os_forward_plan(1024) == (128, 2)
     assert ons.os_forward_plan(2048, torch.bfloat16) == (128, 2)
     assert ons.os_forward_plan(4096) == (512, 2)
-    assert ons.os_forward_plan(4097) == (1024, 2)
-    for cols in range(1, 70000, 97):  # every automatic shape holds its row
+    assert ons.os_forward_plan(4097) == (512, 4)   # 1025 slots: half the lanes, twice the vectors
+    assert ons.os_forward_plan(4100) == (512, 4)
+    assert ons.os_forward_plan(2052) == (256, 4)
+    # every automatic shape holds its row, and a row that is not 16-byte
+    # aligned (row bytes not a multiple of 16) gets room for one more block
+    for cols in range(1, 70000, 97):
         for dt, vec in ((torch.float32, 4), (torch.bfloat16, 8)):
             lanes, vecs = ons.os_forward_plan(cols, dt)
-            assert lanes == 0 or lanes * vecs * vec >= cols
+            extra = 0 if cols % vec == 0 else vec - 1
+            assert lanes == 0 or lanes * vecs * vec >= cols + extra
+    assert ons.os_forward_plan(127) == (32, 2)   # 127 fp32 may span 33 blocks
+    assert ons.os_forward_plan(124) == (32, 1)
     assert ons.os_forward_plan(32000) == (1024, 8)
     assert ons.os_forward_plan(65536) == (1024, 16)
     assert ons.os_forward_plan(65537) == (0, 0)

@@ -35,6 +35,25 @@ def bf16_bits(x32: np.ndarray) -> np.ndarray:
     return workloads.f32_to_bf16_bits(x32)
 
 
+def device_at(x: np.ndarray, shift: int, guard: float = 7.0):
+    """A contiguous device copy of x whose first element lies `shift` elements
+    past a 256-byte aligned allocation, with `guard`-valued elements around it."""
+    t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16 else torch.from_numpy(x)
+    buf = torch.full((t.numel() + shift + 16,), guard, dtype=t.dtype, device="cuda")
+    d = buf[shift:shift + t.numel()].view(t.shape)
+    d.copy_(t.cuda())
+    return d
+
+
+def guards_intact(t, shift: int, guard: float = 7.0) -> bool:
+    """True when the elements around the view made by device_at still hold `guard`."""
+    base = t.untyped_storage()
+    flat = torch.empty(0, dtype=t.dtype, device=t.device).set_(base, 0, (base.nbytes() // t.element_size(),))
+    head = flat[:shift]
+    tail = flat[shift + t.numel():]
+    return bool((head == guard).all()) and bool((tail == guard).all())
+
+
 def run_forward(ons, x: np.ndarray, **kw):
     xd = to_device(x)
     if "lanes" in kw:
@@ -93,13 +112,25 @@ def test_every_resident_shape(ons, orc, lanes, vecs, bf16):
         pytest.skip("fp32-only shape")
     vec = 8 if bf16 else 4
     cap = lanes * vecs * vec
-    for cols in sorted({cap, cap - 1, cap - vec, max(1, cap // 2 + 3), max(1, cap // 3)}):
+    # aligned rows may fill the shape; a row that is not 16-byte aligned may
+    # span one more 16-byte block, so it fits when cols + vec - 1 <= cap
+    cases = {cap, cap - vec, cap - vec + 1, max(1, cap // 2 + 3), max(1, cap // 3)}
+    for cols in sorted(c for c in cases if c + (0 if c % vec == 0 else vec - 1) <= cap):
         rows = 37
         say(f"resident {lanes}x{vecs} bf16={bf16} rows={rows} cols={cols}")
         x32 = workloads.normal(rows, cols, seed=cols * 7 + lanes, scale=2.0)
         x = bf16_bits(x32) if bf16 else x32
         y = run_forward(ons, x, lanes=lanes, vecs=vecs)
         assert_parity(y, orc.softmax(x), bf16, f"{lanes}x{vecs} cols={cols}")
+    # the longest row the shape holds from an element-aligned base
+    cols = cap - vec + 1
+    say(f"resident {lanes}x{vecs} bf16={bf16} cols={cols} from an element-aligned base")
+    x32 = workloads.normal(9, cols, seed=cols + 3 * lanes, scale=2.0)
+    x = bf16_bits(x32) if bf16 else x32
+    xin = device_at(x, 1)
+    y = ons.os_softmax_forward_tuned(xin, lanes, vecs)
+    torch.cuda.synchronize()
+    assert_parity(to_host(y), orc.softmax(x), bf16, f"{lanes}x{vecs} cols={cols} shifted")
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
@@ -222,6 +253,65 @@ def test_misaligned_base_and_in_place(ons, orc):
     ons.safe_softmax_forward(xd, out=xd)
     torch.cuda.synchronize()
     assert_fp32_parity(to_host(xd), ref, "in-place safe")
+
+
+UNALIGNED_COLS = [1, 3, 5, 127, 1001, 2047, 4099, 32001, 50257, 65535, 65537, 100003, 262147]
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_unaligned_rows_every_path(ons, orc, bf16):
+    """Rows that are not 16-byte aligned (odd lengths, element-aligned bases,
+    input and output at different offsets) through every forward entry point,
+    the safe baseline and the top-K: parity, and no store outside the output."""
+    shifts = [(0, 0), (1, 1), (1, 3), (2, 0), (0, 1)] + ([(3, 5), (7, 7)] if bf16 else [(3, 3)])
+    for cols in UNALIGNED_COLS:
+        rows = 37 if cols < 5000 else (7 if cols < 100000 else 3)
+        x32 = workloads.normal(rows, cols, seed=7 * cols + bf16, scale=3.0)
+        x = bf16_bits(x32) if bf16 else x32
+        ref = orc.softmax(x)
+        lse_ref = orc.logsumexp(x, threads=8)
+        for si, so in shifts:
+            what = f"bf16={bf16} rows={rows} cols={cols} in+{si} out+{so}"
+            say(f"unaligned forward/safe/lse/split {what}")
+            xin = device_at(x, si)
+            for name, call in (("forward", lambda o: ons.os_softmax_forward(xin, out=o)),
+                               ("safe", lambda o: ons.safe_softmax_forward(xin, out=o)),
+                               ("lse", lambda o: ons.os_softmax_forward_lse(xin, out=o)),
+                               ("split3", lambda o: ons.os_softmax_forward_split(xin, splits=3, out=o)),
+                               ("split-plan", lambda o: ons.os_softmax_forward_split(xin, out=o))):
+                out = device_at(np.zeros_like(x), so)
+                r = call(out)
+                torch.cuda.synchronize()
+                assert_parity(to_host(out), ref, bf16, f"{name} {what}")
+                assert guards_intact(out, so), f"{name} {what}: a store landed outside the output"
+                if name == "lse":
+                    L = to_host(r[1]).astype(np.float64)
+                    assert np.all(np.abs(L - lse_ref) <= lse_tol(lse_ref)), what
+            assert guards_intact(xin, si), f"{what}: the input was written"
+        say(f"unaligned in place / stats / top-K bf16={bf16} cols={cols}")
+        for si in (1, 3):
+            xd = device_at(x, si)
+            ons.os_softmax_forward(xd, out=xd)
+            torch.cuda.synchronize()
+            assert_parity(to_host(xd), ref, bf16, f"in place +{si} cols={cols}")
+            assert guards_intact(xd, si)
+            xd = device_at(x, si)
+            ons.os_softmax_forward_split(xd, splits=2, out=xd)
+            torch.cuda.synchronize()
+            assert_parity(to_host(xd), ref, bf16, f"split in place +{si} cols={cols}")
+            xd = device_at(x, si)
+            m, d = ons.os_softmax_stats(xd)
+            torch.cuda.synchronize()
+            m_ref, d_ref = orc.stats(x)
+            assert np.array_equal(to_host(m).astype(np.float64), m_ref), f"stats m +{si} cols={cols}"
+            assert np.max(np.abs(to_host(d) - d_ref) / d_ref) <= 1e-5, f"stats d +{si} cols={cols}"
+            K = min(cols, 8)
+            for splits in (1, 3):
+                p, i = ons.os_softmax_topk(xd, K, splits=splits)
+                torch.cuda.synchronize()
+                pr, ir = orc.topk(x, K, threads=8)
+                assert np.array_equal(to_host(i), ir), f"top-{K} +{si} S={splits} cols={cols}: indices"
+                assert np.max(np.abs(to_host(p) - pr)) <= TOPK_PROB_ABS, f"top-{K} +{si} cols={cols}"
 
 
 @pytest.mark.parametrize("cols", [6, 128, 1024, 32000, 70000])
