@@ -77,8 +77,8 @@ int launched(const char* fn) {
 // ---------------------------------------------------------------------------
 // Register-resident shapes built into the library.
 // ---------------------------------------------------------------------------
-typedef void (*RowKernel)(const void*, void*, RowStats, int64_t, int);
-typedef void (*SafeKernel)(const void*, void*, int64_t, int);
+typedef void (*RowKernel)(const void*, void*, RowStats, int64_t, int, uint32_t);
+typedef void (*SafeKernel)(const void*, void*, int64_t, int, uint32_t);
 
 struct ResidentShape {
     int lpr, vpl;
@@ -173,6 +173,17 @@ int64_t vectors_needed(int64_t cols, int dtype) {
 // more at its front).
 int64_t slots_needed(int64_t cols, int dtype, bool al) {
     return vectors_needed(al ? cols : cols + 16 / elt_size(dtype) - 1, dtype);
+}
+
+// The grid origin of a register-resident launch: the 128-byte line holding
+// each row's first element when a workgroup takes one row and the shape holds
+// the row from there (up to 127 bytes more at its front; wavefronts then move
+// whole cache lines), else the 16-byte block.
+uint32_t resident_grid(int lpr, int vpl, int64_t cols, int dtype, bool al) {
+    const int64_t es = elt_size(dtype);
+    const int64_t lead = al ? 128 - 16 : 128 - es;  // bytes before the first element, at most
+    const bool one_row = lpr > 64;
+    return one_row && static_cast<int64_t>(lpr) * vpl * 16 >= lead + cols * es + 15 ? kGrid128 : kGrid16;
 }
 
 // Every plan entry names a built shape (for bf16: one built for bf16) that
@@ -331,14 +342,14 @@ int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t 
         if (allow_hybrid && cols <= kHybridMaxCols) {
             const RowKernel k = hybrid_kernel(dtype, al);
             hipLaunchKernelGGL(k, dim3(grid_for(rows, 1024, grid_req)), dim3(1024), 0, st, in, out, stats, rows,
-                               static_cast<int>(cols));
+                               static_cast<int>(cols), kGrid128);
             return launched(fn);
         }
         const int w = stream_waves(cols, dtype);
         const int block = w * 64;
         const int grid = grid_for(rows, block, grid_req);
         hipLaunchKernelGGL(stream_kernel(w, dtype, al), dim3(grid), dim3(block), 0, st, in, out, stats,
-                           rows, static_cast<int>(cols));
+                           rows, static_cast<int>(cols), kGrid128);
         return launched(fn);
     }
     const int block = lpr <= 64 ? 256 : lpr;
@@ -346,7 +357,7 @@ int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t 
     const int64_t groups = (rows + rpb - 1) / rpb;
     const int grid = grid_for(groups, block, grid_req);
     hipLaunchKernelGGL(shape->fn[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, stats, rows,
-                       static_cast<int>(cols));
+                       static_cast<int>(cols), resident_grid(lpr, vpl, cols, dtype, al));
     return launched(fn);
 }
 
@@ -513,13 +524,13 @@ int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, 
         const int rpb = block / lpr;
         const int grid = grid_for((rows + rpb - 1) / rpb, block, 0);
         hipLaunchKernelGGL(shape->safe[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, rows,
-                           static_cast<int>(cols));
+                           static_cast<int>(cols), resident_grid(lpr, vpl, cols, dtype, al));
     } else {
         const int w = stream_waves(cols, dtype);
         const int block = w * 64;
         const int grid = grid_for(rows, block, 0);
         hipLaunchKernelGGL(safe_kernel(w, dtype, al), dim3(grid), dim3(block), 0, st, in, out, rows,
-                           static_cast<int>(cols));
+                           static_cast<int>(cols), kGrid128);
     }
     return launched(fn);
 }

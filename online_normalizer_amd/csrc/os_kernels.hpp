@@ -6,19 +6,23 @@
 // (same page, section 2); and two plain copies used as bandwidth references.
 //
 // Row layout: row-major, stride == cols.  Every kernel moves rows in 16-byte
-// vector slots with 128-bit buffer accesses.  ALIGNED kernels serve rows whose
-// starts are all 16-byte aligned (an aligned base, row bytes a multiple of 16):
-// slot vi of a row holds its elements [vi*VEC, vi*VEC + VEC).  The others take
-// the 16-byte blocks of memory a row overlaps as its slots: a row whose first
-// element lies `ph` elements into its block has slot vi = elements
-// [vi*VEC - ph, vi*VEC - ph + VEC), and slot entries outside the row are
-// masked by their index.  Rows are read and written through buffer resources
-// that cover only the rows, or the row slice, a workgroup works on, widened to
-// whole 16-byte blocks: every block such a resource covers holds an element of
+// vector slots with 128-bit buffer accesses.  A row's slots are the 16-byte
+// blocks of memory from a grid origin: the 128-byte line holding its first
+// element where a workgroup works on one row at a time (each wavefront then
+// moves whole cache lines; a wavefront access that straddles lines costs
+// 5-20% on MI355X), else the 16-byte block holding it.  A row whose first
+// element lies `ph` elements past its origin has slot vi = elements
+// [vi*VEC - ph, vi*VEC - ph + VEC); slots wholly before the row are not
+// fetched, and entries outside the row are masked by their index.  ALIGNED
+// kernels serve rows whose starts are all 16-byte aligned (an aligned base,
+// row bytes a multiple of 16), so every slot is wholly inside or outside the
+// row.  Rows are read and written through buffer resources that cover only
+// the rows, or the row slice, a workgroup works on, widened to the grid: every
+// 16-byte block, or 128-byte line, such a resource covers holds an element of
 // the row range, so no access leaves the array's pages (memory is mapped in
-// pages, which 16-byte blocks never straddle).  Masked entries read as -inf
-// (e^{-inf} adds 0 to any state); stores outside the resource are dropped by
-// the hardware, and stores never touch an element outside the row.
+// pages, which lines never straddle).  Masked entries read as -inf (e^{-inf}
+// adds 0 to any state); stores outside the resource are dropped by the
+// hardware, and stores never touch an element outside the row.
 #pragma once
 
 #include "os_device.hpp"
@@ -31,46 +35,65 @@ constexpr int kTopKMaxSplits = 16;
 // An offset no buffer resource here reaches: accesses there are dropped.
 constexpr uint32_t kOutside = 0x80000000u;
 
+// Grid origins: the 16-byte block or the 128-byte line holding a row's first
+// element (the value is the mask of the address bits below the origin).
+constexpr uint32_t kGrid16 = 15u;
+constexpr uint32_t kGrid128 = 127u;
+
 // Where a row sits in its buffer resource: its first element lies `ph`
-// elements into the 16-byte block at byte `blk` (ph = 0 when ALIGNED).  Slot
-// vi is the block at blk + 16 vi; element e of the row is at byte
-// blk + (e + ph) * element size.
+// elements past the grid origin at byte `blk`.  Slot vi is the block at
+// blk + 16 vi; element e of the row is at byte blk + (e + ph) * element size.
 struct RowAt {
     uint32_t blk;
     int ph;
 };
 
 // A buffer resource's base and size over n elements from element e0 of the
-// array at p, widened to whole 16-byte blocks unless ALIGNED; `lead` is the
-// byte offset of element e0 in it (0 when ALIGNED).
+// array at p, widened down to the grid origin (`gmask`) and up to a whole
+// 16-byte block; `lead` is the byte offset of element e0 in it.
 struct Span {
     const char* base;
     uint32_t bytes;
     uint32_t lead;
 };
 
-template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ Span span_of(const void* p, int64_t e0, int64_t n) {
+template <bool BF16>
+__device__ __forceinline__ Span span_of(const void* p, int64_t e0, int64_t n, uint32_t gmask) {
     constexpr int SZ = Elt<BF16>::kSize;
     const char* a = static_cast<const char*>(p) + e0 * SZ;
     const uint32_t bytes = static_cast<uint32_t>(n * SZ);
-    if constexpr (ALIGNED) return Span{a, bytes, 0u};
-    const uint32_t lead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a) & 15u);
+    const uint32_t lead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a) & gmask);
     return Span{a - lead, (lead + bytes + 15u) & ~15u, lead};
 }
 
 // The row whose first element is at byte `start` of a resource.
-template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ RowAt row_at(uint32_t start) {
-    if constexpr (ALIGNED) return RowAt{start, 0};
-    return RowAt{start & ~15u, static_cast<int>((start & 15u) / Elt<BF16>::kSize)};
+template <bool BF16>
+__device__ __forceinline__ RowAt row_at(uint32_t start, uint32_t gmask) {
+    return RowAt{start & ~gmask, static_cast<int>((start & gmask) / Elt<BF16>::kSize)};
 }
 
-// Slots a row of `cols` elements spans.
-template <bool BF16, bool ALIGNED>
+// A run of rows that a multi-row workgroup reads through one resource.  On
+// the 16-byte grid an ALIGNED row starts its first block exactly, which the
+// compiler is told (ph = 0), so no per-slot row-start test survives.
+template <bool BF16, bool ALIGNED, bool MULTI>
+__device__ __forceinline__ Span rows_span(const void* p, int64_t e0, int64_t n, uint32_t gmask) {
+    if constexpr (ALIGNED && MULTI)
+        return Span{static_cast<const char*>(p) + e0 * Elt<BF16>::kSize, static_cast<uint32_t>(n * Elt<BF16>::kSize),
+                    0u};
+    return span_of<BF16>(p, e0, n, MULTI ? kGrid16 : gmask);
+}
+
+template <bool BF16, bool ALIGNED, bool MULTI>
+__device__ __forceinline__ RowAt rows_row(uint32_t start, uint32_t gmask) {
+    if constexpr (ALIGNED && MULTI) return RowAt{start, 0};
+    return row_at<BF16>(start, MULTI ? kGrid16 : gmask);
+}
+
+// Slots from a row's grid origin to its last element.
+template <bool BF16>
 __device__ __forceinline__ int slot_count(int cols, int ph) {
     constexpr int VEC = Elt<BF16>::kVec;
-    return ALIGNED ? cols / VEC : (cols + ph + VEC - 1) / VEC;
+    return (cols + ph + VEC - 1) / VEC;
 }
 
 // True when in and out rows lie at the same offset within their 16-byte
@@ -79,13 +102,19 @@ __device__ __forceinline__ bool same_phase(const void* a, const void* b) {
     return ((reinterpret_cast<uintptr_t>(a) ^ reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
 }
 
+// Slots that begin before a row's first element lie within the 128 bytes
+// before it, so their indices are below 8; every caller steps by at least 8
+// slots (on the 16-byte grid only slot 0 can begin before the row), so only a
+// lane's first step can meet one and the test is made there alone.
+constexpr int kHeadSlots = 8;
+
 // Load VPL slots first, first + stride, ... of row r into x: issue the raw
 // 128-bit loads of all of them, fence the scheduler, then unpack.  Without
 // the fence the scheduler may sink each load next to its unpack code, and
 // every load then waits for the previous one to return.  Slots at or past
-// `lim` and rows that are not live are not fetched (their loads go outside
-// the resource); their entries, and (unaligned rows) entries outside the
-// row's elements, become -inf.
+// `lim`, slots wholly before the row, and rows that are not live are not
+// fetched (their loads go outside the resource); their entries, and
+// (unaligned rows) entries outside the row's elements, become -inf.
 template <bool BF16, int VPL, bool ALIGNED, bool STREAM>
 __device__ __forceinline__ void load_slots(const Buf& b, RowAt r, int first, int stride, int lim, int cols,
                                            bool live, float (&x)[VPL][Elt<BF16>::kVec]) {
@@ -95,22 +124,24 @@ __device__ __forceinline__ void load_slots(const Buf& b, RowAt r, int first, int
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int slot = first + v * stride;
-        raw[v] = b.load16<STREAM>(live && slot < lim ? r.blk + static_cast<uint32_t>(slot) * 16u : kOutside);
+        const bool fetch = live && slot < lim && (v > 0 || slot * VEC - r.ph > -VEC);
+        raw[v] = b.load16<STREAM>(fetch ? r.blk + static_cast<uint32_t>(slot) * 16u : kOutside);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         E::unpack(raw[v], x[v]);
         const int slot = first + v * stride;
-        const bool ok = live && slot < lim;
+        const int e0 = slot * VEC - r.ph;  // row index of the slot's first entry
+        const bool ok = live && slot < lim && (v > 0 || e0 > -VEC);
         if constexpr (ALIGNED) {
+            // e0 is a multiple of VEC: the slot is wholly inside the row or out
 #pragma unroll
             for (int k = 0; k < VEC; ++k) x[v][k] = ok ? x[v][k] : -INFINITY;
         } else {
             // only a row's first and last slots are partial: mask entry by
             // entry in a branch the other lanes skip
-            const int e0 = slot * VEC - r.ph;  // row index of the slot's first entry
-            if (!(ok && e0 >= 0 && e0 + VEC <= cols)) {
+            if (!(ok && (v > 0 || e0 >= 0) && e0 + VEC <= cols)) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k)
                     x[v][k] =
@@ -124,21 +155,26 @@ __device__ __forceinline__ void load_slots(const Buf& b, RowAt r, int first, int
 // ro.  Only the row's own elements are written: a slot wholly inside the row
 // goes out as one 128-bit store when the output has the input's phase
 // (`same`), entries at the row's ends, and every entry when the phases differ,
-// element by element.  Slots at or past `lim` and rows that are not live
-// store nothing.
+// element by element.  Slots at or past `lim`, slots wholly before the row
+// (possible only where `first_step`, a lane's first step) and rows that are
+// not live store nothing.
 template <bool BF16, bool ALIGNED>
 __device__ __forceinline__ void store_slot(const Buf& b, RowAt ro, int ph, bool same, int vi, int lim, int cols,
-                                           bool live, const float* v) {
+                                           bool live, const float* v, bool first_step) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
-    const bool ok = live && vi < lim;
+    const int e0 = vi * VEC - ph;  // row index of the slot's first entry
+    const bool ok = live && vi < lim && (!first_step || e0 > -VEC);
+    // with equal 16-byte offsets, element e0 starts a 16-byte block of the
+    // output: byte ro.blk + (e0 + ro.ph) * size, a fixed distance from 16 vi
+    const uint32_t blk_out =
+        ro.blk + static_cast<uint32_t>(ro.ph - ph) * E::kSize + static_cast<uint32_t>(vi) * 16u;
     if constexpr (ALIGNED) {
-        b.store16(ok ? ro.blk + static_cast<uint32_t>(vi) * 16u : kOutside, E::pack(v));
+        b.store16(ok ? blk_out : kOutside, E::pack(v));
     } else {
-        const int e0 = vi * VEC - ph;
         if (same) {
-            const bool whole = ok && e0 >= 0 && e0 + VEC <= cols;
-            b.store16(whole ? ro.blk + static_cast<uint32_t>(vi) * 16u : kOutside, E::pack(v));
+            const bool whole = ok && (!first_step || e0 >= 0) && e0 + VEC <= cols;
+            b.store16(whole ? blk_out : kOutside, E::pack(v));
             if (ok && !whole) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
@@ -205,7 +241,7 @@ __device__ __forceinline__ void put_stats(const RowStats& o, int64_t row, State 
 // ---------------------------------------------------------------------------
 template <bool BF16, int LPR, int VPL, bool ALIGNED>
 __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
-    k_resident(const void* in, void* out, RowStats st, int64_t rows, int cols) {
+    k_resident(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int BLOCK = LPR <= 64 ? 256 : LPR;
@@ -228,10 +264,10 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         const int64_t nrows = (rows - row0) < RPB ? (rows - row0) : RPB;
         const int64_t row = row0 + g;
         const bool live = g < nrows;
-        const Span si = span_of<BF16, ALIGNED>(in, row0 * cols, nrows * cols);
+        const Span si = rows_span<BF16, ALIGNED, (LPR <= 64)>(in, row0 * cols, nrows * cols, gmask);
         const Buf bin(si.base, si.bytes);
-        const RowAt ri = row_at<BF16, ALIGNED>(si.lead + static_cast<uint32_t>(g) * row_bytes);
-        const int ns = slot_count<BF16, ALIGNED>(cols, ri.ph);
+        const RowAt ri = rows_row<BF16, ALIGNED, (LPR <= 64)>(si.lead + static_cast<uint32_t>(g) * row_bytes, gmask);
+        const int ns = slot_count<BF16>(cols, ri.ph);
 
         float x[VPL][VEC];
         load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, ns, cols, live, x);
@@ -263,14 +299,14 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         if (any_stats(st) && live && j == 0) put_stats(st, row, s);
         if (out != nullptr) {
             const float scale = exp_e(ml - s.m) * rcp(s.d);
-            const Span so = span_of<BF16, ALIGNED>(out, row0 * cols, nrows * cols);
+            const Span so = rows_span<BF16, ALIGNED, (LPR <= 64)>(out, row0 * cols, nrows * cols, gmask);
             const Buf bout(so.base, so.bytes);
-            const RowAt ro = row_at<BF16, ALIGNED>(so.lead + static_cast<uint32_t>(g) * row_bytes);
+            const RowAt ro = rows_row<BF16, ALIGNED, (LPR <= 64)>(so.lead + static_cast<uint32_t>(g) * row_bytes, gmask);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) x[v][k] *= scale;
-                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, ns, cols, live, x[v]);
+                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, ns, cols, live, x[v], v == 0);
             }
         }
     }
@@ -286,7 +322,7 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
 // ---------------------------------------------------------------------------
 template <bool BF16, int W, int U, bool ALIGNED>
 __global__ void __launch_bounds__(W * 64)
-    k_stream(const void* in, void* out, RowStats st, int64_t rows, int cols) {
+    k_stream(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int BLOCK = W * 64;
@@ -297,10 +333,10 @@ __global__ void __launch_bounds__(W * 64)
     int par = 0;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const Span si = span_of<BF16>(in, row * cols, cols, gmask);
         const Buf bin(si.base, si.bytes);
-        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
-        const int nvec = slot_count<BF16, ALIGNED>(cols, ri.ph);
+        const RowAt ri = row_at<BF16>(si.lead, gmask);
+        const int nvec = slot_count<BF16>(cols, ri.ph);
         float ml = kFloor, dl = 0.0f;
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
@@ -331,9 +367,9 @@ __global__ void __launch_bounds__(W * 64)
         if (any_stats(st) && tid == 0) put_stats(st, row, s);
         if (out != nullptr) {
             const float inv_d = rcp(s.d);
-            const Span so = span_of<BF16, ALIGNED>(out, row * cols, cols);
+            const Span so = span_of<BF16>(out, row * cols, cols, gmask);
             const Buf bout(so.base, so.bytes);
-            const RowAt ro = row_at<BF16, ALIGNED>(so.lead);
+            const RowAt ro = row_at<BF16>(so.lead, gmask);
             for (int base = 0; base < nvec; base += BLOCK * U) {
                 float x[U][VEC];
                 load_slots<BF16, U, ALIGNED, true>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
@@ -341,7 +377,7 @@ __global__ void __launch_bounds__(W * 64)
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - s.m) * inv_d;
-                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u], u == 0);
                 }
             }
         }
@@ -360,7 +396,7 @@ __global__ void __launch_bounds__(W * 64)
 // ---------------------------------------------------------------------------
 template <bool BF16, int VPL, int U, bool ALIGNED>
 __global__ void __launch_bounds__(1024)
-    k_hybrid(const void* in, void* out, RowStats st, int64_t rows, int cols) {
+    k_hybrid(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int W = 16;
@@ -373,10 +409,10 @@ __global__ void __launch_bounds__(1024)
     int par = 0;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const Span si = span_of<BF16>(in, row * cols, cols, gmask);
         const Buf bin(si.base, si.bytes);
-        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
-        const int nvec = slot_count<BF16, ALIGNED>(cols, ri.ph);
+        const RowAt ri = row_at<BF16>(si.lead, gmask);
+        const int nvec = slot_count<BF16>(cols, ri.ph);
         float xr[VPL][VEC];
         load_slots<BF16, VPL, ALIGNED, true>(bin, ri, tid, BLOCK, nvec, cols, true, xr);
         float mr = kFloor;
@@ -421,14 +457,14 @@ __global__ void __launch_bounds__(1024)
         if (out != nullptr) {
             const float inv_d = rcp(s.d);
             const float scale = exp_e(mr - s.m) * inv_d;
-            const Span so = span_of<BF16, ALIGNED>(out, row * cols, cols);
+            const Span so = span_of<BF16>(out, row * cols, cols, gmask);
             const Buf bout(so.base, so.bytes);
-            const RowAt ro = row_at<BF16, ALIGNED>(so.lead);
+            const RowAt ro = row_at<BF16>(so.lead, gmask);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) xr[v][k] *= scale;
-                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * BLOCK + tid, nvec, cols, true, xr[v]);
+                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * BLOCK + tid, nvec, cols, true, xr[v], v == 0);
             }
             for (int base = RES; base < nvec; base += BLOCK * U) {
                 float x[U][VEC];
@@ -437,7 +473,7 @@ __global__ void __launch_bounds__(1024)
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - s.m) * inv_d;
-                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u], u == 0);
                 }
             }
         }
@@ -451,7 +487,7 @@ __global__ void __launch_bounds__(1024)
 // ---------------------------------------------------------------------------
 template <bool BF16, int W, int U, bool ALIGNED>
 __global__ void __launch_bounds__(W * 64)
-    k_safe3(const void* in, void* out, int64_t rows, int cols) {
+    k_safe3(const void* in, void* out, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int BLOCK = W * 64;
@@ -463,10 +499,10 @@ __global__ void __launch_bounds__(W * 64)
     int par = 0;
 
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
+        const Span si = span_of<BF16>(in, row * cols, cols, gmask);
         const Buf bin(si.base, si.bytes);
-        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
-        const int nvec = slot_count<BF16, ALIGNED>(cols, ri.ph);
+        const RowAt ri = row_at<BF16>(si.lead, gmask);
+        const int nvec = slot_count<BF16>(cols, ri.ph);
         // pass 1: maximum
         float m = kFloor;
         for (int base = 0; base < nvec; base += BLOCK * U) {
@@ -506,9 +542,9 @@ __global__ void __launch_bounds__(W * 64)
         }
         // pass 3: normalise and store
         const float inv_d = rcp(d);
-        const Span so = span_of<BF16, ALIGNED>(out, row * cols, cols);
+        const Span so = span_of<BF16>(out, row * cols, cols, gmask);
         const Buf bout(so.base, so.bytes);
-        const RowAt ro = row_at<BF16, ALIGNED>(so.lead);
+        const RowAt ro = row_at<BF16>(so.lead, gmask);
         for (int base = 0; base < nvec; base += BLOCK * U) {
             float x[U][VEC];
             load_slots<BF16, U, ALIGNED, true>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
@@ -516,7 +552,7 @@ __global__ void __launch_bounds__(W * 64)
             for (int u = 0; u < U; ++u) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - m) * inv_d;
-                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u]);
+                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u], u == 0);
             }
         }
     }
@@ -532,7 +568,7 @@ __global__ void __launch_bounds__(W * 64)
 // ---------------------------------------------------------------------------
 template <bool BF16, int LPR, int VPL, bool ALIGNED>
 __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
-    k_safe3_rows(const void* in, void* out, int64_t rows, int cols) {
+    k_safe3_rows(const void* in, void* out, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int BLOCK = LPR <= 64 ? 256 : LPR;
@@ -553,10 +589,10 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         const int64_t row0 = rb * RPB;
         const int64_t nrows = (rows - row0) < RPB ? (rows - row0) : RPB;
         const bool live = g < nrows;
-        const Span si = span_of<BF16, ALIGNED>(in, row0 * cols, nrows * cols);
+        const Span si = rows_span<BF16, ALIGNED, (LPR <= 64)>(in, row0 * cols, nrows * cols, gmask);
         const Buf bin(si.base, si.bytes);
-        const RowAt ri = row_at<BF16, ALIGNED>(si.lead + static_cast<uint32_t>(g) * row_bytes);
-        const int nvec = slot_count<BF16, ALIGNED>(cols, ri.ph);
+        const RowAt ri = rows_row<BF16, ALIGNED, (LPR <= 64)>(si.lead + static_cast<uint32_t>(g) * row_bytes, gmask);
+        const int nvec = slot_count<BF16>(cols, ri.ph);
         float x[VPL][VEC];
 
         // pass 1: maximum
@@ -593,14 +629,14 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         // pass 3: normalise and store
         load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, nvec, cols, live, x);
         const float inv_d = rcp(d);
-        const Span so = span_of<BF16, ALIGNED>(out, row0 * cols, nrows * cols);
+        const Span so = rows_span<BF16, ALIGNED, (LPR <= 64)>(out, row0 * cols, nrows * cols, gmask);
         const Buf bout(so.base, so.bytes);
-        const RowAt ro = row_at<BF16, ALIGNED>(so.lead + static_cast<uint32_t>(g) * row_bytes);
+        const RowAt ro = rows_row<BF16, ALIGNED, (LPR <= 64)>(so.lead + static_cast<uint32_t>(g) * row_bytes, gmask);
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
 #pragma unroll
             for (int k = 0; k < VEC; ++k) x[v][k] = exp_e(x[v][k] - m) * inv_d;
-            store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, nvec, cols, live, x[v]);
+            store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, nvec, cols, live, x[v], v == 0);
         }
     }
 }
@@ -624,9 +660,9 @@ struct Slice {
 };
 
 // Slice `seg` of S over a row of `ns` slots whose widened span has
-// `span_bytes` bytes.
-__device__ __forceinline__ Slice slice_of(int seg, int S, int ns, uint32_t span_bytes) {
-    const int seg_vec = (ns + S - 1) / S;
+// `span_bytes` bytes; slices start on multiples of `quant` slots.
+__device__ __forceinline__ Slice slice_of(int seg, int S, int ns, uint32_t span_bytes, int quant) {
+    const int seg_vec = ((ns + S - 1) / S + quant - 1) / quant * quant;
     const int v0 = seg * seg_vec < ns ? seg * seg_vec : ns;
     const int v1 = v0 + seg_vec < ns ? v0 + seg_vec : ns;
     const uint32_t end = static_cast<uint32_t>(v1) * 16u;
@@ -645,10 +681,10 @@ __global__ void __launch_bounds__(W * 64)
     int par = 0;
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t row = unit / S;
-        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
-        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
+        const Span si = span_of<BF16>(in, row * cols, cols, kGrid128);
+        const RowAt ri = row_at<BF16>(si.lead, kGrid128);
         const Slice sl =
-            slice_of(static_cast<int>(unit - row * S), S, slot_count<BF16, ALIGNED>(cols, ri.ph), si.bytes);
+            slice_of(static_cast<int>(unit - row * S), S, slot_count<BF16>(cols, ri.ph), si.bytes, 8);
         const Buf bin(si.base, sl.bytes);
         float ml = kFloor, dl = 0.0f;
         for (int base = sl.v0; base < sl.v1; base += BLOCK * U) {
@@ -693,10 +729,10 @@ __global__ void __launch_bounds__(W * 64)
     const bool same = same_phase(in, out);
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t row = unit / S;
-        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
-        const RowAt ri = row_at<BF16, ALIGNED>(si.lead);
+        const Span si = span_of<BF16>(in, row * cols, cols, kGrid128);
+        const RowAt ri = row_at<BF16>(si.lead, kGrid128);
         const Slice sl =
-            slice_of(static_cast<int>(unit - row * S), S, slot_count<BF16, ALIGNED>(cols, ri.ph), si.bytes);
+            slice_of(static_cast<int>(unit - row * S), S, slot_count<BF16>(cols, ri.ph), si.bytes, 8);
         // the row's S slice states: lane l folds states l, l + 64, ... in
         // order, then the wave merges the 64 lane states (same bits in every
         // lane, and in every workgroup of the row)
@@ -706,9 +742,9 @@ __global__ void __launch_bounds__(W * 64)
         const float m = t.m;
         const float inv_d = rcp(t.d);
         const Buf bin(si.base, sl.bytes);
-        const Span so = span_of<BF16, ALIGNED>(out, row * cols, cols);
+        const Span so = span_of<BF16>(out, row * cols, cols, kGrid128);
         const Buf bout(so.base, so.bytes);
-        const RowAt ro = row_at<BF16, ALIGNED>(so.lead);
+        const RowAt ro = row_at<BF16>(so.lead, kGrid128);
         for (int base = sl.v0; base < sl.v1; base += BLOCK * U) {
             float x[U][VEC];
             load_slots<BF16, U, ALIGNED, true>(bin, ri, base + tid, BLOCK, sl.v1, cols, true, x);
@@ -716,7 +752,7 @@ __global__ void __launch_bounds__(W * 64)
             for (int u = 0; u < U; ++u) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - m) * inv_d;
-                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, sl.v1, cols, true, x[u]);
+                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, sl.v1, cols, true, x[u], u == 0);
             }
         }
     }
@@ -938,11 +974,11 @@ __global__ void __launch_bounds__(W * 64)
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t row = SPLIT ? unit / S : unit;
         const int seg = SPLIT ? static_cast<int>(unit - row * S) : 0;
-        const Span si = span_of<BF16, ALIGNED>(in, row * cols, cols);
-        const int ph = row_at<BF16, ALIGNED>(si.lead).ph;  // the row's first block is at byte 0
+        const Span si = span_of<BF16>(in, row * cols, cols, kGrid16);
+        const int ph = row_at<BF16>(si.lead, kGrid16).ph;  // the row's first block is at byte 0
         // The resource ends with the segment, so loads issued ahead past its
         // end (into the next segment or past the row) touch no memory.
-        const Slice sl = slice_of(seg, SPLIT ? S : 1, slot_count<BF16, ALIGNED>(cols, ph), si.bytes);
+        const Slice sl = slice_of(seg, SPLIT ? S : 1, slot_count<BF16>(cols, ph), si.bytes, 1);
         const int v0 = sl.v0, v1 = sl.v1;
         const Buf bin(si.base, sl.bytes);
         if (tid == 0) s_thr = ordered_bits(-INFINITY);
