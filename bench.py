@@ -380,6 +380,29 @@ def all_configs(ons, stream):
                                 "us_flushed": round(tsf * 1e6, 2)},
                       "speedup": round(tu / ts, 2)})
         del x, y, ws
+
+    # rows that are not 16-byte aligned (odd lengths such as a 50257-entry
+    # vocabulary): not one of the five workloads; the same kernels move them
+    # as the 16-byte blocks they overlap
+    for rows, cols, dt in ((4096, 32001, torch.float32), (4096, 50257, torch.float32),
+                           (524288, 2047, torch.bfloat16)):
+        g = torch.Generator("cuda").manual_seed(cols)
+        x = (torch.randn(rows, cols, device="cuda", generator=g) * 2).to(dt)
+        y = torch.empty_like(x)
+        nbytes = rows * cols * x.element_size() * 2
+        t, _ = measure(lambda: ons.os_softmax_forward(x, out=y), 30)
+        table.append({"case": "unaligned_forward", "rows": rows, "cols": cols,
+                      "dtype": str(dt).replace("torch.", ""), "algorithmic_bytes": nbytes,
+                      "online": {"us": round(t * 1e6, 2), "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1)}})
+        del x, y
+    rows, cols = 256, 50257
+    x = torch.randn(rows, cols, device="cuda", generator=torch.Generator("cuda").manual_seed(cols)) * 3
+    nbytes = rows * cols * 4 + rows * workloads.TOPK_K * 8
+    t, _ = measure(lambda: ons.os_softmax_topk(x, workloads.TOPK_K), 200)
+    table.append({"case": "unaligned_topk", "rows": rows, "cols": cols, "dtype": "float32", "K": workloads.TOPK_K,
+                  "algorithmic_bytes": nbytes,
+                  "topk": {"us": round(t * 1e6, 2), "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1)}})
+    del x
     return table
 
 
