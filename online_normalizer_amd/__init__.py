@@ -318,17 +318,19 @@ def os_softmax_forward_split(x: torch.Tensor, splits: int | None = None, out: to
     return out
 
 
-def os_softmax_topk_ex(x: torch.Tensor, K: int, splits: int, workspace: torch.Tensor,
+def os_softmax_topk_ex(x: torch.Tensor, K: int, splits: int, workspace: torch.Tensor | None,
                        probs: torch.Tensor | None = None,
                        idx: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
-    """Fused softmax + top-K for float32 or bfloat16 input (dtype from the tensor)."""
+    """Fused softmax + top-K for float32 or bfloat16 input (dtype from the tensor).
+    workspace may be None when splits == 1."""
     rows, cols, p_new, i_new = _topk_out(x, K)
     probs = p_new if probs is None else probs
     idx = i_new if idx is None else idx
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("os_softmax_topk_ex",
            lib().os_softmax_topk_ex(x.data_ptr(), _dtype_code(x), probs.data_ptr(), idx.data_ptr(), rows, cols, K,
-                                    splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                    _stream(x)))
+                                    splits, ws_ptr, ws_bytes, _stream(x)))
     return probs, idx
 
 

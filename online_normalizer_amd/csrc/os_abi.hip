@@ -585,20 +585,58 @@ TopkKernel topk_kernel(int dtype, bool al, bool split) {
     return dtype == OS_BF16 ? topk_kernel_t<W, true>(al, split) : topk_kernel_t<W, false>(al, split);
 }
 
+// Waves per workgroup for the top-K of `units` rows (or row slices) of
+// `seg_cols` columns, from a sweep on MI355X over 64..16384 rows of 512..128256
+// columns, K = 1, 8, 32, fp32 and bf16, every width from 1 to 16 timed.
+//   - Long rows on few workgroups want 16 waves, to keep enough loads in
+//     flight per CU.
+//   - Short rows, or many workgroups, want few, since every wave pays for its
+//     own threshold and K-list and the workgroup for the final merge.  A large
+//     K wants more, so that the lists build in parallel.
+//   - The first bound on the K-th value is taken over 64 parts of the
+//     workgroup's first tile, so a row should give each of at least 2 K parts
+//     some of its 16-byte slots: W <= slots / (2 K).
+// Tables by K (<= 8, more), columns (<= 512, 2048, 8192, 32768, longer) and
+// workgroups (<= 64, 256, 1024, 4096, more).  The choice is within 6.3% of
+// the best width at every swept point, and 0.4% on average.  A fixed width
+// was up to 10x off for short rows on many workgroups.
+int topk_waves(int64_t units, int64_t seg_cols, int K, int dtype) {
+    static const int kWaves[2][5][5] = {
+        {
+            {4, 4, 2, 1, 1},       // K <= 8: <= 512 columns
+            {4, 4, 2, 1, 1},       // <= 2048
+            {8, 8, 4, 4, 2},       // <= 8192
+            {16, 16, 4, 4, 4},     // <= 32768
+            {16, 16, 4, 8, 8},     // longer
+        },
+        {
+            {2, 2, 2, 1, 1},       // K > 8
+            {4, 4, 4, 2, 2},
+            {8, 8, 4, 4, 4},
+            {16, 16, 8, 8, 8},
+            {16, 16, 8, 8, 8},
+        }};
+    const int cb = seg_cols <= 512 ? 0 : seg_cols <= 2048 ? 1 : seg_cols <= 8192 ? 2 : seg_cols <= 32768 ? 3 : 4;
+    const int rb = units <= 64 ? 0 : units <= 256 ? 1 : units <= 1024 ? 2 : units <= 4096 ? 3 : 4;
+    int W = kWaves[K > 8 ? 1 : 0][cb][rb];
+    const int64_t slots = vectors_needed(seg_cols, dtype);
+    while (W > 1 && static_cast<int64_t>(W) * 2 * K > slots) W /= 2;
+    return W;
+}
+
 int launch_topk(const char* fn, const void* in, int dtype, float* probs, int32_t* idx, int64_t rows, int64_t cols,
                 int K, int S, void* workspace, void* stream) {
     const bool al = aligned(in, 16) && ((cols * elt_size(dtype)) % 16) == 0;
     const int64_t units = rows * S;
-    // 8-wave workgroups, except on at most 256 workgroups for K > 8 (fp32) or
-    // any K (bf16), where 16 waves per row hide more of the per-element
-    // arithmetic and spread the candidate inserts (measured on MI355X over
-    // 16..4096 rows of 32000 and 128256 columns, K = 1..32: this choice is
-    // within 2% of the faster width everywhere for fp32; for bf16 16 waves
-    // are 10-25% faster on 256 rows and 15-40% slower on >= 1024).
-    const bool wide = units <= 256 && (K > 8 || dtype == OS_BF16);
-    const int block = wide ? 1024 : 512;
+    const int W = topk_waves(units, (cols + S - 1) / S, K, dtype);
+    const int block = W * 64;
     const int grid = grid_for(units, block, 0);
-    const TopkKernel k = wide ? topk_kernel<16>(dtype, al, S > 1) : topk_kernel<8>(dtype, al, S > 1);
+    const bool split = S > 1;
+    const TopkKernel k = W == 1   ? topk_kernel<1>(dtype, al, split)
+                         : W == 2 ? topk_kernel<2>(dtype, al, split)
+                         : W == 4 ? topk_kernel<4>(dtype, al, split)
+                         : W == 8 ? topk_kernel<8>(dtype, al, split)
+                                  : topk_kernel<16>(dtype, al, split);
     State* states = nullptr;
     TopkEntry* lists = nullptr;
     if (S > 1) {
@@ -665,12 +703,16 @@ int64_t os_softmax_topk_workspace_bytes(int64_t rows, int K, int splits) {
 int os_topk_plan(int64_t rows, int64_t cols, int K) {
     if (rows <= 0 || cols <= 0 || K < 1) return 1;
     // Splitting pays only for batches far smaller than the CU count, and only
-    // for rows long enough that streaming one on a single CU outlasts the
-    // second (merge) launch (measured on MI355X: 16 rows x 128256 best at 8
-    // slices, 64 rows at 4, 256 rows unsplit; 64 rows x 32000 unsplit): at
-    // most 256 workgroups and 8 slices, rows of >= 64K columns, slices of
-    // >= 8K columns.
-    if (cols < 65536) return 1;
+    // for rows long enough that streaming one on a single workgroup outlasts
+    // the second (merge) launch.  Measured on MI355X with graph-timed
+    // launches:
+    //   - 16 and 32 rows x 128256 are best at 8 slices, 64 rows at 4 or 8;
+    //   - 128 and 256 rows are best unsplit, or within 2% of it;
+    //   - rows of 32000..65536 columns are best unsplit at 32..256 rows
+    //     (128 x 65536: 10.1 us unsplit, 13.8 us at 2 slices).
+    // So: at most 64 rows, rows of >= 96K columns, at most 256 workgroups and
+    // 8 slices, slices of >= 8K columns.
+    if (cols < 98304 || rows > 64) return 1;
     int S = 1;
     while (S < 8 && rows * S * 2 <= 256 && cols / (S * 2) >= 8192) S *= 2;
     return S;

@@ -762,7 +762,8 @@ __global__ void __launch_bounds__(W * 64)
 // Fused softmax + top-K (paper summary, section 4), one read of the input.
 //
 // One W-wave workgroup per row (per row slice with SPLIT), fp32 or bf16
-// logits.  Every lane folds (m, d) over its slots as in k_stream.  Candidates: each wave keeps ONE sorted list of the best K
+// logits.  Every lane folds (m, d) over its slots as in k_stream.
+// Candidates: each wave keeps ONE sorted list of the best K
 // (value, index) pairs it has seen, spread over lanes 0..K-1 (lane k holds
 // rank k) under the total order (value desc, index asc).  Most elements are
 // rejected by a compare with a wave-uniform threshold T, a lower bound on the
@@ -775,7 +776,9 @@ __global__ void __launch_bounds__(W * 64)
 //     tile so far, and its maximum the lanes' running maxima);
 //   - then: the K-th entry of the wave's own list, and the largest K-th entry
 //     published by any wave of the workgroup (an LDS atomic max).
-// Survivors (x >= T, so ties at T are kept) are inserted one at a time:
+// Survivors (x >= T, so ties at T are kept; while T is still -inf, entries
+// in the row that rank ahead of the wave's K-th entry) are inserted one at a
+// time:
 // position p = number of entries ahead of the new pair, entries from p on
 // shift down one lane (DPP wave_shr:1).  Every true top-K element survives
 // every filter and stays in its wave's list, so the final merge of the W
@@ -954,7 +957,8 @@ __global__ void __launch_bounds__(W * 64)
     k_topk(const void* in, float* probs, int* idx, int64_t rows, int cols, int K, int S, State* ws_state,
            TopkEntry* ws_list) {
     using E = Elt<BF16>;
-    static_assert(W == 4 || W == 8 || W == 16, "the final merge packs W lists of up to 32 entries into 8 registers");
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16,
+                  "the final merge packs W lists of up to 32 entries into at most 8 registers");
     constexpr int BLOCK = W * 64;
     constexpr int VEC = E::kVec;
     constexpr int STEP = BLOCK * U;
@@ -1059,21 +1063,47 @@ __global__ void __launch_bounds__(W * 64)
             T = fmaxf(T, from_ordered_bits(__hip_atomic_load(&s_thr, __ATOMIC_RELAXED,
                                                              __HIP_MEMORY_SCOPE_WORKGROUP)));
             if (__ballot(mx >= T) != 0) {
+                if (T > -INFINITY) {
+                    // entries outside the segment or the row read -inf, and
+                    // cannot reach T
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int wave_slot0 = base + u * BLOCK + w * kWave;
+                    for (int u = 0; u < U; ++u) {
+                        const int wave_slot0 = base + u * BLOCK + w * kWave;
 #pragma unroll
-                    for (int k = 0; k < VEC; ++k) {
-                        // slots past the segment hold -inf; they pass only
-                        // when T is -inf and are dropped below
-                        uint64_t mask = __ballot(x[u][k] >= T);
-                        while (mask != 0) {
-                            const int l = __builtin_ctzll(mask);
-                            mask &= mask - 1;
-                            const int i = (wave_slot0 + l) * VEC + k - ph;  // column index
-                            const float v = readlane(x[u][k], l);
-                            if ((wave_slot0 + l < v1) & (static_cast<uint32_t>(i) < static_cast<uint32_t>(cols)))
-                                list_insert(L, I, v, i, K, lane, kmask);
+                        for (int k = 0; k < VEC; ++k) {
+                            uint64_t mask = __ballot(x[u][k] >= T);
+                            while (mask != 0) {
+                                const int l = __builtin_ctzll(mask);
+                                mask &= mask - 1;
+                                list_insert(L, I, readlane(x[u][k], l), (wave_slot0 + l) * VEC + k - ph, K, lane,
+                                            kmask);
+                            }
+                        }
+                    }
+                } else {
+                    // T = -inf (a row or slice shorter than the workgroup's
+                    // first tile, or with few entries above -inf): every
+                    // entry would pass, so take only in-row entries that rank
+                    // ahead of the wave's K-th entry, re-read every round
+                    // (once the list holds K entries of -inf, later -inf
+                    // entries of higher index are skipped)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int wave_slot0 = base + u * BLOCK + w * kWave;
+                        const int my_slot = wave_slot0 + lane;
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) {
+                            const int i_me = my_slot * VEC + k - ph;  // column index
+                            const bool in_row =
+                                (my_slot < v1) & (static_cast<uint32_t>(i_me) < static_cast<uint32_t>(cols));
+                            const float xv = x[u][k];
+                            uint64_t mask =
+                                __ballot(in_row & ahead_of(xv, i_me, readlane(L, K - 1), readlane(I, K - 1)));
+                            while (mask != 0) {
+                                const int l = __builtin_ctzll(mask);
+                                mask &= mask - 1;
+                                list_insert(L, I, readlane(xv, l), (wave_slot0 + l) * VEC + k - ph, K, lane, kmask);
+                            }
                         }
                     }
                 }

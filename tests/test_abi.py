@@ -160,6 +160,9 @@ def test_topk_split_validation(L, ons):
     assert ons.os_topk_plan(16, 1000, 8) == 1
     assert ons.os_topk_plan(64, 32000, 8) == 1
     assert ons.os_topk_plan(16, 1 << 20, 8) == 8
+    assert ons.os_topk_plan(128, 65536, 8) == 1    # measured faster unsplit
+    assert ons.os_topk_plan(64, 65536, 8) == 1
+    assert ons.os_topk_plan(128, 128256, 8) == 1
 
 
 def test_forward_split_validation(L, ons):

@@ -657,6 +657,35 @@ def test_topk_special_rows(ons, orc):
     check_topk(ons, orc, x[:, 1:4999], 8, "unaligned cols")
 
 
+# batches that the width table maps to 1, 2, 4, 8 and 16 waves per row (and,
+# for K = 32, the cap of 2 K parts per wave), each with heavy ties
+TOPK_WIDTH_CASES = [(4200, 512, 8), (1024, 512, 8), (64, 2048, 8), (64, 8192, 8), (64, 32000, 8),
+                    (64, 512, 32), (1024, 2048, 32), (300, 600, 17)]
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_topk_every_width(ons, orc, bf16):
+    for rows, cols, K in TOPK_WIDTH_CASES:
+        x32 = workloads.normal(rows, cols, seed=rows + cols + K, scale=3.0)
+        x32[::5, cols // 3: cols // 3 + 2 * K] = 7.5  # ties across the K-th rank
+        x = bf16_bits(x32) if bf16 else x32
+        check_topk(ons, orc, x, K, f"width case bf16={bf16}")
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_topk_rows_mostly_neg_inf(ons, orc, bf16):
+    """Rows with fewer entries above -inf than K, or only a few: the -inf fill
+    goes by index, and the bound stays -inf through the first tiles."""
+    for rows, cols, K in [(256, 32000, 8), (64, 5000, 32), (300, 700, 13), (40, 128256, 8)]:
+        x32 = workloads.normal(rows, cols, seed=cols + K, scale=2.0)
+        x32[:, 5:] = -np.inf                            # 5 entries above -inf in every row
+        x32[1::3, : cols // 2] = -np.inf                # then some rows with one late block
+        x32[1::3, cols - 100:] = 1.0
+        x32[2::7, :] = -np.inf                          # and rows of -inf only
+        x = bf16_bits(x32) if bf16 else x32
+        check_topk(ons, orc, x, K, f"mostly -inf bf16={bf16}")
+
+
 def test_topk_many_rows(ons, orc):
     """Enough rows for the 8-wave-per-row launch, with ties and a ragged K."""
     x = workloads.normal(1500, 3001, seed=99, scale=3.0)
