@@ -149,6 +149,9 @@ def main(argv=None) -> int:
     ap.add_argument("--all-configs", metavar="FILE", default=None,
                     help="also time every workload (forward, three-pass baseline, copy; top-K for the "
                          "top-K workload) and write the table to FILE as JSON")
+    ap.add_argument("--perf-map", metavar="FILE", default=None,
+                    help="also time the forward over row lengths from 64 to 2^20 (16-byte aligned and not, "
+                         "fp32 and bf16) and the top-K over batches, row lengths and K; write a text table to FILE")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
@@ -264,9 +267,67 @@ def main(argv=None) -> int:
     if args.all_configs:
         with open(args.all_configs, "w") as f:
             json.dump(all_configs(ons, stream), f, indent=1)
+    if args.perf_map:
+        with open(args.perf_map, "w") as f:
+            f.write(perf_map(ons, stream))
 
     print(json.dumps(out), flush=True)
     return 0
+
+
+def perf_map(ons, stream) -> str:
+    """The performance envelope beyond the five workloads: the forward over
+    row lengths (about 256 MiB of input per launch, or 256 rows where rows are
+    longer), and the fused top-K over batches, row lengths and K.  Inputs are
+    N(0, 3^2) from a seeded generator.  Times are the average launch of a
+    captured HIP graph of 20 launches; GB/s counts the algorithmic bytes (in +
+    out for the forward, in for the top-K)."""
+    import torch
+
+    def graph_us(fn):
+        _, avg = time_graph(fn, 20, 3, stream)
+        return avg * 1e6
+
+    lines = ["# Forward and fused top-K across shapes on MI355X (gfx950), from:",
+             "#   python bench.py --perf-map <file>",
+             "# us = average launch of a captured HIP graph of 20 launches; % = of the 8 TB/s HBM peak;",
+             "# 'odd' rows are not 16-byte aligned (row bytes not a multiple of 16)",
+             "",
+             f"{'forward':>8s} {'dtype':>8s} {'rows':>9s} {'cols':>8s} {'shape':>9s} {'us':>10s} {'GB/s':>8s} {'%':>6s}"]
+    gen = torch.Generator("cuda").manual_seed(1234)
+    for dt in (torch.float32, torch.bfloat16):
+        es = 2 if dt == torch.bfloat16 else 4
+        for cols in (64, 128, 127, 512, 1000, 1024, 2047, 2048, 4096, 8191, 8192, 16384, 32000, 32001,
+                     50257, 65536, 100000, 128256, 131072, 262144, 1 << 20):
+            rows = max(256, (256 << 20) // (cols * es))
+            x = (torch.randn(rows, cols, device="cuda", generator=gen) * 3).to(dt)
+            y = torch.empty_like(x)
+            t = graph_us(lambda: ons.os_softmax_forward(x, out=y))
+            nb = 2 * rows * cols * es
+            shape = "x".join(map(str, ons.os_forward_plan(cols, dt))) if cols <= 65536 else "long"
+            odd = " odd" if (cols * es) % 16 else ""
+            lines.append(f"{'':>8s} {str(dt)[6:]:>8s} {rows:>9d} {cols:>8d} {shape:>9s} {t:>10.2f} "
+                         f"{nb / t / 1e3:>8.1f} {100 * nb / t / 1e3 / PEAK_HBM_GBS:>6.1f}{odd}")
+            del x, y
+    lines += ["", f"{'top-K':>8s} {'dtype':>8s} {'rows':>9s} {'cols':>8s} {'K':>3s} {'splits':>6s} {'us':>10s} "
+                  f"{'GB/s':>8s} {'%':>6s}"]
+    for dt in (torch.float32, torch.bfloat16):
+        es = 2 if dt == torch.bfloat16 else 4
+        for rows, cols in ((16384, 512), (4096, 2048), (2048, 8192), (1024, 32000), (4096, 32000), (256, 50257),
+                           (16, 128256), (64, 128256), (256, 128256), (1024, 128256), (16, 1 << 20)):
+            x = (torch.randn(rows, cols, device="cuda", generator=gen) * 3).to(dt)
+            for K in (1, 8, 32):
+                S = ons.os_topk_plan(rows, cols, K)
+                ws = None
+                if S > 1:
+                    ws = torch.empty(ons.os_softmax_topk_workspace_bytes(rows, K, S), dtype=torch.uint8,
+                                     device="cuda")
+                t = graph_us(lambda: ons.os_softmax_topk_ex(x, K, S, ws))
+                nb = rows * cols * es + rows * K * 8
+                lines.append(f"{'':>8s} {str(dt)[6:]:>8s} {rows:>9d} {cols:>8d} {K:>3d} {S:>6d} {t:>10.2f} "
+                             f"{nb / t / 1e3:>8.1f} {100 * nb / t / 1e3 / PEAK_HBM_GBS:>6.1f}")
+            del x
+    return "\n".join(lines) + "\n"
 
 
 def all_configs(ons, stream):

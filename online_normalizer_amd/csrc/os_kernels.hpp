@@ -124,7 +124,7 @@ __device__ __forceinline__ void load_slots(const Buf& b, RowAt r, int first, int
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int slot = first + v * stride;
-        const bool fetch = live && slot < lim && (v > 0 || slot * VEC - r.ph > -VEC);
+        const bool fetch = live & (slot < lim) & ((v > 0) | (slot * VEC - r.ph > -VEC));
         raw[v] = b.load16<STREAM>(fetch ? r.blk + static_cast<uint32_t>(slot) * 16u : kOutside);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -133,7 +133,7 @@ __device__ __forceinline__ void load_slots(const Buf& b, RowAt r, int first, int
         E::unpack(raw[v], x[v]);
         const int slot = first + v * stride;
         const int e0 = slot * VEC - r.ph;  // row index of the slot's first entry
-        const bool ok = live && slot < lim && (v > 0 || e0 > -VEC);
+        const bool ok = live & (slot < lim) & ((v > 0) | (e0 > -VEC));
         if constexpr (ALIGNED) {
             // e0 is a multiple of VEC: the slot is wholly inside the row or out
 #pragma unroll
@@ -141,11 +141,11 @@ __device__ __forceinline__ void load_slots(const Buf& b, RowAt r, int first, int
         } else {
             // only a row's first and last slots are partial: mask entry by
             // entry in a branch the other lanes skip
-            if (!(ok && (v > 0 || e0 >= 0) && e0 + VEC <= cols)) {
+            if (!(ok & ((v > 0) | (e0 >= 0)) & (e0 + VEC <= cols))) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k)
                     x[v][k] =
-                        (ok && static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols)) ? x[v][k] : -INFINITY;
+                        (ok & (static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols))) ? x[v][k] : -INFINITY;
             }
         }
     }
@@ -164,7 +164,7 @@ __device__ __forceinline__ void store_slot(const Buf& b, RowAt ro, int ph, bool 
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     const int e0 = vi * VEC - ph;  // row index of the slot's first entry
-    const bool ok = live && vi < lim && (!first_step || e0 > -VEC);
+    const bool ok = live & (vi < lim) & (!first_step | (e0 > -VEC));
     // with equal 16-byte offsets, element e0 starts a 16-byte block of the
     // output: byte ro.blk + (e0 + ro.ph) * size, a fixed distance from 16 vi
     const uint32_t blk_out =
@@ -173,9 +173,9 @@ __device__ __forceinline__ void store_slot(const Buf& b, RowAt ro, int ph, bool 
         b.store16(ok ? blk_out : kOutside, E::pack(v));
     } else {
         if (same) {
-            const bool whole = ok && (!first_step || e0 >= 0) && e0 + VEC <= cols;
+            const bool whole = ok & (!first_step | (e0 >= 0)) & (e0 + VEC <= cols);
             b.store16(whole ? blk_out : kOutside, E::pack(v));
-            if (ok && !whole) {
+            if (ok & !whole) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
                     const int e = e0 + k;
@@ -191,7 +191,7 @@ __device__ __forceinline__ void store_slot(const Buf& b, RowAt ro, int ph, bool 
             for (int k = 0; k < VEC; ++k) {
                 const int e = e0 + k;
                 E::store1(b,
-                          (ok && static_cast<uint32_t>(e) < static_cast<uint32_t>(cols))
+                          (ok & (static_cast<uint32_t>(e) < static_cast<uint32_t>(cols)))
                               ? ro.blk + static_cast<uint32_t>(e + ro.ph) * E::kSize
                               : kOutside,
                           v[k]);
@@ -1024,7 +1024,7 @@ __global__ void __launch_bounds__(W * 64)
                         const int e0 = slot * VEC - ph;
 #pragma unroll
                         for (int k = 0; k < VEC; ++k)
-                            x[u][k] = (slot < v1 && static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols))
+                            x[u][k] = ((slot < v1) & (static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols)))
                                           ? x[u][k]
                                           : -INFINITY;
                     }

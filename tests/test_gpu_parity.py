@@ -360,9 +360,10 @@ def test_deterministic(ons):
 
 
 def test_graph_replays_match_eager(ons):
-    """The forward, the baseline, the top-K and the split forward captured in a HIP graph: every
-    replay, with eager work and synchronisations between replays, equals the
-    eager result bit for bit."""
+    """The forward (aligned and unaligned rows), the baseline, the top-K (one
+    launch at several widths, and split over two launches) and the split
+    forward captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager result bit for bit."""
     x = to_device(workloads.config(2, 0, 512))
     xt = to_device(workloads.config(5, 0, 8))
     say("graph capture")
@@ -372,22 +373,31 @@ def test_graph_replays_match_eager(ons):
     xs = to_device(workloads.normal(4, 100003, seed=9, scale=3.0))
     ws = torch.empty(ons.os_softmax_forward_workspace_bytes(4, 8), dtype=torch.uint8, device="cuda")
     sp_ref = ons.os_softmax_forward_split(xs, splits=8, workspace=ws)
+    # the split top-K (two launches), a one-wave-per-row top-K, and an unaligned forward
+    xk = to_device(workloads.normal(16, 128256, seed=10, scale=3.0))
+    wk = torch.empty(ons.os_softmax_topk_workspace_bytes(16, 8, 4), dtype=torch.uint8, device="cuda")
+    pk_ref, ik_ref = ons.os_softmax_topk_ex(xk, 8, 4, wk)
+    xw = to_device(workloads.normal(4200, 512, seed=11, scale=3.0))
+    pw_ref, iw_ref = ons.os_softmax_topk_ex(xw, 8, 1, None)
+    xu = to_device(workloads.normal(64, 50257, seed=12, scale=3.0))
+    yu_ref = ons.os_softmax_forward(xu)
     torch.cuda.synchronize()
     y = torch.empty_like(x)
     s3 = torch.empty_like(x)
     sp = torch.empty_like(xs)
+    yu = torch.empty_like(xu)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         ons.os_softmax_forward(x, out=y)
         ons.safe_softmax_forward(x, out=s3)
         p, i = ons.os_softmax_topk(xt, 8)
         ons.os_softmax_forward_split(xs, splits=8, out=sp, workspace=ws)
+        pk, ik = ons.os_softmax_topk_ex(xk, 8, 4, wk)
+        pw, iw = ons.os_softmax_topk_ex(xw, 8, 1, None)
+        ons.os_softmax_forward(xu, out=yu)
     for rep in range(4):
-        y.zero_()
-        s3.zero_()
-        p.zero_()
-        i.zero_()
-        sp.zero_()
+        for t in (y, s3, p, i, sp, pk, ik, pw, iw, yu):
+            t.zero_()
         junk = ons.os_softmax_forward(torch.randn(64, 1000, device="cuda"))  # eager work between replays
         torch.cuda.synchronize()
         say(f"graph replay {rep}")
@@ -397,6 +407,9 @@ def test_graph_replays_match_eager(ons):
         assert torch.equal(s3.view(torch.int32), s_ref.view(torch.int32)), rep
         assert torch.equal(p, p_ref) and torch.equal(i, i_ref), rep
         assert torch.equal(sp.view(torch.int32), sp_ref.view(torch.int32)), rep
+        assert torch.equal(pk, pk_ref) and torch.equal(ik, ik_ref), rep
+        assert torch.equal(pw, pw_ref) and torch.equal(iw, iw_ref), rep
+        assert torch.equal(yu.view(torch.int32), yu_ref.view(torch.int32)), rep
         del junk
 
 
