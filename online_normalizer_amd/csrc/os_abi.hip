@@ -149,7 +149,7 @@ constexpr PlanEntry kPlanF32Unaligned[] = {
 constexpr PlanEntry kPlanBF16[] = {
     {4, 4, 1},       {8, 8, 1},        {10, 8, 2},       {16, 16, 1},      {32, 16, 2},      {64, 32, 2},
     {128, 64, 2},    {192, 64, 4},     {256, 128, 2},    {384, 64, 8},     {512, 256, 2},    {1024, 256, 4},
-    {2048, 256, 8},  {4096, 1024, 4},  {8192, 1024, 8}};
+    {2048, 256, 8},  {3072, 512, 8},   {4096, 1024, 4},  {8192, 1024, 8}};
 constexpr PlanEntry kPlanBF16Unaligned[] = {
     {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {32, 32, 1},      {48, 32, 2},      {64, 64, 1},
     {80, 32, 4},     {128, 64, 2},     {256, 64, 4},     {320, 128, 4},    {512, 256, 2},    {640, 256, 4},

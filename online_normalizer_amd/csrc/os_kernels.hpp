@@ -239,8 +239,18 @@ __device__ __forceinline__ void put_stats(const RowStats& o, int64_t row, State 
 // y_k = e_k * (e^{m_l - m} / d): one exponential per element in all.
 // Writes y when out != nullptr, and the statistics that `st` asks for.
 // ---------------------------------------------------------------------------
+// Shapes of at most 4 vectors per lane fit in 64 VGPRs, so 8 waves per SIMD
+// are requested: two 1024-lane (four 512-lane) workgroups then stay resident
+// on a CU, which the register count would otherwise decide by a few
+// registers.  Unaligned bf16 rows on 256 or more lanes of 4 vectors would
+// spill to fit, and are left to the compiler.
 template <bool BF16, int LPR, int VPL, bool ALIGNED>
-__global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
+constexpr int resident_min_waves() {
+    return (VPL <= 4 && !(BF16 && !ALIGNED && LPR >= 256 && VPL == 4)) ? 8 : 1;
+}
+
+template <bool BF16, int LPR, int VPL, bool ALIGNED>
+__global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF16, LPR, VPL, ALIGNED>()))
     k_resident(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
