@@ -624,9 +624,69 @@ int topk_waves(int64_t units, int64_t seg_cols, int K, int dtype) {
     return W;
 }
 
+// Register-resident top-K shapes for short rows (up to 1024 columns): lanes
+// per row x 16-byte slots per lane, at most 32 entries per lane (fp32 up to 8
+// slots, bf16 up to 4), by capacity.
+typedef void (*TopkRowsKernel)(const void*, float*, int*, int64_t, int, int);
+struct TopkRowsShape {
+    int lpr, vpl;
+    TopkRowsKernel fn[2];  // [aligned]
+};
+#define ONORM_TOPK_ROWS(B, L, V) {L, V, {k_topk_rows<B, L, V, false>, k_topk_rows<B, L, V, true>}}
+const TopkRowsShape kTopkRowsF32[] = {
+    ONORM_TOPK_ROWS(false, 4, 1),  ONORM_TOPK_ROWS(false, 4, 2),  ONORM_TOPK_ROWS(false, 4, 4),
+    ONORM_TOPK_ROWS(false, 4, 8),  ONORM_TOPK_ROWS(false, 8, 8),  ONORM_TOPK_ROWS(false, 16, 8),
+    ONORM_TOPK_ROWS(false, 32, 8)};
+const TopkRowsShape kTopkRowsBF16[] = {
+    ONORM_TOPK_ROWS(true, 4, 1),  ONORM_TOPK_ROWS(true, 4, 2),  ONORM_TOPK_ROWS(true, 4, 4),
+    ONORM_TOPK_ROWS(true, 8, 4),  ONORM_TOPK_ROWS(true, 16, 4), ONORM_TOPK_ROWS(true, 32, 4)};
+#undef ONORM_TOPK_ROWS
+
+// The short-row shape for these rows, or nullptr when they are too long.
+const TopkRowsShape* topk_rows_shape(int64_t cols, int dtype, bool al) {
+    const int64_t need = slots_needed(cols, dtype, al);
+    const TopkRowsShape* t = dtype == OS_BF16 ? kTopkRowsBF16 : kTopkRowsF32;
+    const int n = dtype == OS_BF16 ? sizeof(kTopkRowsBF16) / sizeof(kTopkRowsBF16[0])
+                                   : sizeof(kTopkRowsF32) / sizeof(kTopkRowsF32[0]);
+    for (int i = 0; i < n; ++i)
+        if (static_cast<int64_t>(t[i].lpr) * t[i].vpl >= need) return &t[i];
+    return nullptr;
+}
+
+// Whether the short-row kernel serves this batch (unsplit rows only).  It
+// pays K rounds of a dependent scan per row, so it wins on short rows, on
+// many rows (where the tiled kernel pays its per-workgroup cost per row) and
+// for small K.  Largest K it serves, by row length (<= 16, 64, 128, 256, 512,
+// 1024 columns; longer rows never) and batch (< 1024, < 16384, more rows),
+// measured on MI355X against the tiled kernel over 64..65536 rows, K = 1..32,
+// both dtypes: where it is used it was as fast or faster (up to 19x at 65536
+// rows of 16), and where it is not it was slower.
+bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
+    static const int kMaxK[6][3] = {
+        {16, 16, 32},  // <= 16 columns
+        {16, 16, 32},  // <= 64
+        {0, 2, 32},    // <= 128
+        {0, 0, 32},    // <= 256
+        {0, 0, 8},     // <= 512
+        {0, 0, 2},     // <= 1024
+    };
+    if (topk_rows_shape(cols, dtype, al) == nullptr || cols > 1024) return false;
+    const int cb = cols <= 16 ? 0 : cols <= 64 ? 1 : cols <= 128 ? 2 : cols <= 256 ? 3 : cols <= 512 ? 4 : 5;
+    const int rb = rows < 1024 ? 0 : rows < 16384 ? 1 : 2;
+    return K <= kMaxK[cb][rb];
+}
+
 int launch_topk(const char* fn, const void* in, int dtype, float* probs, int32_t* idx, int64_t rows, int64_t cols,
                 int K, int S, void* workspace, void* stream) {
     const bool al = aligned(in, 16) && ((cols * elt_size(dtype)) % 16) == 0;
+    if (S == 1 && use_topk_rows(rows, cols, K, dtype, al)) {
+        const TopkRowsShape* sh = topk_rows_shape(cols, dtype, al);
+        const int rpb = 256 / sh->lpr;
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(sh->fn[al ? 1 : 0], dim3(grid_for((rows + rpb - 1) / rpb, 256, 0)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), in, probs, idx, rows, static_cast<int>(cols), K);
+        return launched(fn);
+    }
     const int64_t units = rows * S;
     const int W = topk_waves(units, (cols + S - 1) / S, K, dtype);
     const int block = W * 64;

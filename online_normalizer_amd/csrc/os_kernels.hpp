@@ -1165,6 +1165,136 @@ __global__ void __launch_bounds__(W * 64)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused softmax + top-K for short rows (paper summary, section 4), the shape
+// of a mixture-of-experts router: many rows of up to 1024 entries.  LPR <= 64
+// lanes share a row and hold it in registers (VPL 16-byte slots each, at most
+// 32 entries per lane), several rows per wavefront, no barriers; the row is
+// read once.
+//   - State: the row maximum M and d = sum e^{x - M} by reductions over the
+//     row's lanes.
+//   - Selection, K rounds: each lane keeps the best entry it still holds
+//     under (value desc, index asc); a butterfly over the row's lanes finds
+//     the row's best; its owner retires it and rescans its own entries.  The
+//     order is the total order of the oracle, so ties go to the lower index
+//     and -0.0 ties +0.0.  NaN entries are never ahead of anything and are
+//     not selected (rows holding NaN have NaN probabilities and unspecified
+//     indices).
+//   - Output, each round: probs = e^{u - M} / d over the whole row, and the
+//     index, written by the row's first lane.
+// ---------------------------------------------------------------------------
+template <int LPR>
+__device__ __forceinline__ void group_best(float& v, int& i, int lane) {
+    // every lane of each aligned group of LPR lanes ends with the group's best
+    // (v, i) under (value desc, index asc)
+    auto step = [&](float ov, int oi) {
+        const bool t = ahead_of(ov, oi, v, i);
+        v = t ? ov : v;
+        i = t ? oi : i;
+    };
+    if constexpr (LPR >= 2) step(lane_xor<1>(v, lane), lane_xor<1>(i, lane));
+    if constexpr (LPR >= 4) step(lane_xor<2>(v, lane), lane_xor<2>(i, lane));
+    if constexpr (LPR >= 8) step(lane_xor<4>(v, lane), lane_xor<4>(i, lane));
+    if constexpr (LPR >= 16) step(lane_xor<8>(v, lane), lane_xor<8>(i, lane));
+    if constexpr (LPR >= 32) step(lane_xor<16>(v, lane), lane_xor<16>(i, lane));
+    if constexpr (LPR >= 64) step(lane_xor<32>(v, lane), lane_xor<32>(i, lane));
+}
+
+template <bool BF16, int LPR, int VPL, bool ALIGNED>
+__global__ void __launch_bounds__(256)
+    k_topk_rows(const void* in, float* probs, int* idx, int64_t rows, int cols, int K) {
+    using E = Elt<BF16>;
+    constexpr int VEC = E::kVec;
+    constexpr int RPB = 256 / LPR;
+    constexpr int N = VPL * VEC;  // entries per lane
+    static_assert(LPR >= 4 && LPR <= 64 && N <= 32, "one row within a wavefront, at most 32 entries per lane");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int j = tid % LPR;
+    const int g = tid / LPR;
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+
+    for (int64_t rb = blockIdx.x; rb * RPB < rows; rb += gridDim.x) {
+        const int64_t row0 = rb * RPB;
+        const int64_t nrows = (rows - row0) < RPB ? (rows - row0) : RPB;
+        const int64_t row = row0 + g;
+        const bool live = g < nrows;
+        const Span si = rows_span<BF16, ALIGNED, true>(in, row0 * cols, nrows * cols, kGrid16);
+        const Buf bin(si.base, si.bytes);
+        const RowAt ri = rows_row<BF16, ALIGNED, true>(si.lead + static_cast<uint32_t>(g) * row_bytes, kGrid16);
+        const int ns = slot_count<BF16>(cols, ri.ph);
+
+        float x[VPL][VEC];
+        load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, ns, cols, live, x);
+
+        // entries of the row this lane holds (bit v * VEC + k)
+        uint32_t avail = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e0 = (v * LPR + j) * VEC - ri.ph;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k)  // NaN entries are never taken
+                avail |= static_cast<uint32_t>(live & ((v * LPR + j) < ns) &
+                                               (static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols)) &
+                                               (x[v][k] == x[v][k]))
+                         << (v * VEC + k);
+        }
+
+        // the row's state: M and d = sum e^{x - M} (entries outside the row
+        // read -inf and add 0)
+        float ml = kFloor;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) ml = fmaxf(ml, x[v][k]);
+        const float M = group_max<LPR>(ml);
+        float dl = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) dl += exp_e(x[v][k] - M);
+        const float inv_d = rcp(group_sum<LPR>(dl));
+
+        // This lane's best remaining entry.  A lane's entries (v, k) run in
+        // increasing column order, so scanning them in order with a strict
+        // compare keeps the lower column on ties; the winner's entry number
+        // bb = v * VEC + k gives its column.
+        constexpr int LGV = VEC == 8 ? 3 : 2;
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF, bb = -1;
+        auto rescan = [&]() {
+            bv = -INFINITY;
+            bb = -1;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float xv = x[v][k];
+                    const bool t = ((avail >> (v * VEC + k)) & 1u) & ((xv > bv) | (bb < 0));
+                    bv = t ? xv : bv;
+                    bb = t ? v * VEC + k : bb;
+                }
+            }
+            bi = bb < 0 ? 0x7FFFFFFF : (((bb >> LGV) * LPR + j) * VEC + (bb & (VEC - 1)) - ri.ph);
+        };
+        rescan();
+        for (int r = 0; r < K; ++r) {
+            float gv = bv;
+            int gi = bi;
+            group_best<LPR>(gv, gi, lane);
+            if (live & (j == 0)) {
+                probs[row * K + r] = exp_e(gv - M) * inv_d;
+                idx[row * K + r] = gi;
+            }
+            if ((bi == gi) & (gi != 0x7FFFFFFF)) {  // this lane held the row's best: retire it
+                avail &= ~(1u << bb);
+                rescan();
+            }
+        }
+    }
+}
+
 // Second launch of the split top-K: one wavefront per row folds the S slice
 // states with (+) in slice order and merges the S sorted lists (bitonic, as
 // above), then writes the K probabilities and indices.

@@ -627,13 +627,18 @@ def test_lse_full_configs(ons, orc, n):
 
 # -- fused softmax + top-K ---------------------------------------------------------
 
-def check_topk(ons, orc, x: np.ndarray, K: int, what: str, splits=None):
+def check_topk(ons, orc, x: np.ndarray, K: int, what: str, splits=None, nan_rows=None):
+    """Indices bit-exact and probabilities within the bound; rows listed in
+    nan_rows hold a NaN, so only their (NaN) probabilities are compared."""
     say(f"topk {what} rows={x.shape[0]} cols={x.shape[1]} K={K} splits={splits}")
     xd = to_device(np.ascontiguousarray(x))
     p, i = ons.os_softmax_topk(xd, K, splits=splits)
     torch.cuda.synchronize()
     pr, ir = orc.topk(x, K, threads=8)
     i = to_host(i)
+    if nan_rows is not None:
+        i[nan_rows] = ir[nan_rows]
+        assert np.all(np.isnan(pr[nan_rows])), "the oracle gives NaN probabilities for rows holding NaN"
     bad = np.argwhere(i != ir)
     assert bad.size == 0, f"{what}: first index mismatch at {bad[:3].tolist()}: {i[bad[0][0]]} vs {ir[bad[0][0]]}"
     p = to_host(p).astype(np.float64)
@@ -697,6 +702,30 @@ def test_topk_rows_mostly_neg_inf(ons, orc, bf16):
         x32[2::7, :] = -np.inf                          # and rows of -inf only
         x = bf16_bits(x32) if bf16 else x32
         check_topk(ons, orc, x, K, f"mostly -inf bf16={bf16}")
+
+
+# batches the short-row (register-resident) top-K serves: many rows of up to
+# 1024 columns, rows of <= 64 columns at any batch; K up to 32
+TOPK_ROWS_CASES = [(16384, 100, 32), (16384, 512, 8), (20000, 1000, 2), (2000, 60, 16), (300, 16, 8), (5000, 127, 2),
+                   (16384, 255, 32), (64, 5, 5)]
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_topk_short_rows(ons, orc, bf16):
+    rng = np.random.Generator(np.random.PCG64(77 + bf16))
+    for rows, cols, K in TOPK_ROWS_CASES:
+        x32 = workloads.normal(rows, cols, seed=rows * 3 + cols, scale=3.0)
+        x32[::3] = rng.integers(-2, 3, size=x32[::3].shape)     # heavy ties
+        x32[1::7, cols // 2:] = -np.inf                          # half -inf
+        x32[2::11, :] = -np.inf                                  # only -inf
+        x32[4::13, cols - 1] = 20.0                              # the best at the row end
+        x32[5::17, cols // 3] = np.nan                           # NaN rows: probabilities NaN
+        x = bf16_bits(x32) if bf16 else x32
+        nan_rows = np.arange(5, rows, 17)
+        check_topk(ons, orc, x, K, f"short rows bf16={bf16}", nan_rows=nan_rows)
+        # one column fewer: rows that are no longer 16-byte aligned
+        check_topk(ons, orc, x[:, 1:], min(K, cols - 1), f"short rows shifted bf16={bf16}",
+                   nan_rows=nan_rows if cols // 3 >= 1 else None)
 
 
 def test_topk_many_rows(ons, orc):
