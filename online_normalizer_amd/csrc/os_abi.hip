@@ -653,26 +653,28 @@ const TopkRowsShape* topk_rows_shape(int64_t cols, int dtype, bool al) {
     return nullptr;
 }
 
-// Whether the short-row kernel serves this batch (unsplit rows only).  It
-// pays K rounds of a dependent scan per row, so it wins on short rows, on
-// many rows (where the tiled kernel pays its per-workgroup cost per row) and
-// for small K.  Largest K it serves, by row length (<= 16, 64, 128, 256, 512,
-// 1024 columns; longer rows never) and batch (< 1024, < 16384, more rows),
-// measured on MI355X against the tiled kernel over 64..65536 rows, K = 1..32,
-// both dtypes: where it is used it was as fast or faster (up to 19x at 65536
-// rows of 16), and where it is not it was slower.
+// Whether the short-row kernel serves this batch (unsplit rows only).  Each
+// of its rows is one dependent chain of K rounds, so it wins on short rows,
+// on many rows (where the tiled kernel pays its per-workgroup cost per row)
+// and for small K; on a few wide rows the tiled kernel's waves share the
+// selection instead.  Largest K it serves, by row length (<= 16, 64, 128,
+// 256, 512, 1024 columns; longer rows never) and batch (< 2048, < 4096,
+// < 8192, more rows), measured on MI355X against the tiled kernel over
+// 64..65536 rows, K = 1..32, both dtypes: where it is used it was as fast or
+// faster (up to 23x at 65536 rows of 16, 4.6x at 65536 x 256 for K = 8), and
+// where it is not it was slower.
 bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
-    static const int kMaxK[6][3] = {
-        {16, 16, 32},  // <= 16 columns
-        {16, 16, 32},  // <= 64
-        {0, 2, 32},    // <= 128
-        {0, 0, 32},    // <= 256
-        {0, 0, 8},     // <= 512
-        {0, 0, 2},     // <= 1024
+    static const int kMaxK[6][4] = {
+        {32, 32, 32, 32},  // <= 16 columns
+        {16, 16, 32, 32},  // <= 64
+        {8, 16, 32, 32},   // <= 128
+        {2, 4, 8, 32},     // <= 256
+        {2, 4, 8, 32},     // <= 512
+        {2, 4, 16, 16},    // <= 1024
     };
     if (topk_rows_shape(cols, dtype, al) == nullptr || cols > 1024) return false;
     const int cb = cols <= 16 ? 0 : cols <= 64 ? 1 : cols <= 128 ? 2 : cols <= 256 ? 3 : cols <= 512 ? 4 : 5;
-    const int rb = rows < 1024 ? 0 : rows < 16384 ? 1 : 2;
+    const int rb = rows < 2048 ? 0 : rows < 4096 ? 1 : rows < 8192 ? 2 : 3;
     return K <= kMaxK[cb][rb];
 }
 

@@ -25,6 +25,8 @@
 // hardware, and stores never touch an element outside the row.
 #pragma once
 
+#include <climits>
+
 #include "os_device.hpp"
 
 namespace onorm {
@@ -1173,31 +1175,56 @@ __global__ void __launch_bounds__(W * 64)
 // read once.
 //   - State: the row maximum M and d = sum e^{x - M} by reductions over the
 //     row's lanes.
-//   - Selection, K rounds: each lane keeps the best entry it still holds
-//     under (value desc, index asc); a butterfly over the row's lanes finds
-//     the row's best; its owner retires it and rescans its own entries.  The
-//     order is the total order of the oracle, so ties go to the lower index
-//     and -0.0 ties +0.0.  NaN entries are never ahead of anything and are
-//     not selected (rows holding NaN have NaN probabilities and unspecified
-//     indices).
-//   - Output, each round: probs = e^{u - M} / d over the whole row, and the
-//     index, written by the row's first lane.
+//   - Selection keys: each entry becomes an integer that orders as the value
+//     does (-0.0 and +0.0 equal); entries outside the row, and entries
+//     already output, take the lowest key.  Ties between keys go to the lower
+//     column, the order of the oracle.  NaN entries get keys too (above +inf
+//     or below -inf by sign), so a row holding NaN still yields K distinct
+//     in-row indices, in no specified order, with NaN probabilities.
+//   - K rounds: each lane offers its best remaining entry; a butterfly over
+//     the row's lanes finds the row's best, written by the row's first lane
+//     (probability e^{u - M} / d over the whole row, and the index).  The
+//     lane that held it retires it and finds its next best.  With more than
+//     8 entries per lane they sit in 4 groups with a best per group, and the
+//     keys also live in LDS (each lane only touches its own words, so no
+//     barrier): retiring an entry is one store and refreshing its group reads
+//     a quarter of the keys instead of rescanning all of them.
 // ---------------------------------------------------------------------------
+constexpr int kKeyRetired = INT_MIN;  // outside the row, or already output
+
+__device__ __forceinline__ int order_key(float x) {
+    const int b = __float_as_int(x + 0.0f);  // -0.0 + 0.0 = +0.0
+    const int k = b ^ ((b >> 31) & 0x7FFFFFFF);
+    return k > kKeyRetired ? k : kKeyRetired + 1;  // the all-ones NaN pattern
+}
+
+__device__ __forceinline__ float key_value(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+// Every lane of each aligned group of LPR lanes ends with the group's best
+// (key, column): larger key first, then lower column.
 template <int LPR>
-__device__ __forceinline__ void group_best(float& v, int& i, int lane) {
-    // every lane of each aligned group of LPR lanes ends with the group's best
-    // (v, i) under (value desc, index asc)
-    auto step = [&](float ov, int oi) {
-        const bool t = ahead_of(ov, oi, v, i);
-        v = t ? ov : v;
-        i = t ? oi : i;
+__device__ __forceinline__ void group_best_key(int& k, int& c) {
+    auto take = [&](int ok, int oc) {
+        const bool t = (ok > k) | ((ok == k) & (oc < c));
+        k = t ? ok : k;
+        c = t ? oc : c;
     };
-    if constexpr (LPR >= 2) step(lane_xor<1>(v, lane), lane_xor<1>(i, lane));
-    if constexpr (LPR >= 4) step(lane_xor<2>(v, lane), lane_xor<2>(i, lane));
-    if constexpr (LPR >= 8) step(lane_xor<4>(v, lane), lane_xor<4>(i, lane));
-    if constexpr (LPR >= 16) step(lane_xor<8>(v, lane), lane_xor<8>(i, lane));
-    if constexpr (LPR >= 32) step(lane_xor<16>(v, lane), lane_xor<16>(i, lane));
-    if constexpr (LPR >= 64) step(lane_xor<32>(v, lane), lane_xor<32>(i, lane));
+    if constexpr (LPR >= 2) take(dpp<kDppXor1>(k), dpp<kDppXor1>(c));
+    if constexpr (LPR >= 4) take(dpp<kDppXor2>(k), dpp<kDppXor2>(c));
+    if constexpr (LPR >= 8) take(dpp<kDppHalfMirror>(k), dpp<kDppHalfMirror>(c));
+    if constexpr (LPR >= 16) take(dpp<kDppMirror>(k), dpp<kDppMirror>(c));
+    if constexpr (LPR >= 32) {
+        const f32x2 tk = swap_rows16(__int_as_float(k)), tc = swap_rows16(__int_as_float(c));
+        k = __float_as_int(tk[0]);
+        c = __float_as_int(tc[0]);
+        take(__float_as_int(tk[1]), __float_as_int(tc[1]));
+    }
+    if constexpr (LPR >= 64) {
+        const f32x2 tk = swap_rows32(__int_as_float(k)), tc = swap_rows32(__int_as_float(c));
+        k = __float_as_int(tk[0]);
+        c = __float_as_int(tc[0]);
+        take(__float_as_int(tk[1]), __float_as_int(tc[1]));
+    }
 }
 
 template <bool BF16, int LPR, int VPL, bool ALIGNED>
@@ -1206,14 +1233,22 @@ __global__ void __launch_bounds__(256)
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int RPB = 256 / LPR;
-    constexpr int N = VPL * VEC;  // entries per lane
+    constexpr int N = VPL * VEC;                // entries per lane
+    constexpr bool kLds = N > 8;                // keys in LDS, in groups
+    constexpr int NG = kLds ? 4 : 1;            // groups per lane
+    constexpr int G = N / NG;                   // entries per group
+    constexpr int NQ = kLds ? N / 4 : 1;        // 4-key LDS words per lane
     static_assert(LPR >= 4 && LPR <= 64 && N <= 32, "one row within a wavefront, at most 32 entries per lane");
+    static_assert(!kLds || G % 4 == 0, "groups of whole 4-key words");
+    // lane t's keys 4q..4q+3 at s_keys[q][t]: each lane reads and writes only
+    // its own words, with consecutive lanes on consecutive 16 bytes
+    __shared__ int4 s_keys[NQ][kLds ? 256 : 1];
 
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
     const int j = tid % LPR;
     const int g = tid / LPR;
     const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+    constexpr int LGV = VEC == 8 ? 3 : 2;
 
     for (int64_t rb = blockIdx.x; rb * RPB < rows; rb += gridDim.x) {
         const int64_t row0 = rb * RPB;
@@ -1227,19 +1262,6 @@ __global__ void __launch_bounds__(256)
 
         float x[VPL][VEC];
         load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, ns, cols, live, x);
-
-        // entries of the row this lane holds (bit v * VEC + k)
-        uint32_t avail = 0;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-            const int e0 = (v * LPR + j) * VEC - ri.ph;
-#pragma unroll
-            for (int k = 0; k < VEC; ++k)  // NaN entries are never taken
-                avail |= static_cast<uint32_t>(live & ((v * LPR + j) < ns) &
-                                               (static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols)) &
-                                               (x[v][k] == x[v][k]))
-                         << (v * VEC + k);
-        }
 
         // the row's state: M and d = sum e^{x - M} (entries outside the row
         // read -inf and add 0)
@@ -1256,40 +1278,102 @@ __global__ void __launch_bounds__(256)
             for (int k = 0; k < VEC; ++k) dl += exp_e(x[v][k] - M);
         const float inv_d = rcp(group_sum<LPR>(dl));
 
-        // This lane's best remaining entry.  A lane's entries (v, k) run in
-        // increasing column order, so scanning them in order with a strict
-        // compare keeps the lower column on ties; the winner's entry number
-        // bb = v * VEC + k gives its column.
-        constexpr int LGV = VEC == 8 ? 3 : 2;
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF, bb = -1;
-        auto rescan = [&]() {
-            bv = -INFINITY;
-            bb = -1;
+        // keys; entry e = v * VEC + k of this lane is column
+        // ((e >> LGV) * LPR + j) * VEC + (e & (VEC - 1)) - ph.  Rows whose
+        // length is a whole number of slots hold only in-row entries in
+        // their slots.
+        int key[N];
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) {
+        for (int v = 0; v < VPL; ++v) {
+            const int e0 = (v * LPR + j) * VEC - ri.ph;
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float xv = x[v][k];
-                    const bool t = ((avail >> (v * VEC + k)) & 1u) & ((xv > bv) | (bb < 0));
-                    bv = t ? xv : bv;
-                    bb = t ? v * VEC + k : bb;
-                }
+            for (int k = 0; k < VEC; ++k) {
+                const bool in_row = live & ((v * LPR + j) < ns) &
+                                    (ALIGNED | (static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols)));
+                key[v * VEC + k] = in_row ? order_key(x[v][k]) : kKeyRetired;
             }
-            bi = bb < 0 ? 0x7FFFFFFF : (((bb >> LGV) * LPR + j) * VEC + (bb & (VEC - 1)) - ri.ph);
+        }
+        auto column = [&](int e) { return ((e >> LGV) * LPR + j) * VEC + (e & (VEC - 1)) - ri.ph; };
+
+        // best of each group (entries scanned in column order with a strict
+        // compare, so the lower column wins ties)
+        int gk[NG], ge[NG];
+        auto scan_group = [&](int q, const int* t) {
+            int nk = t[0], ne = 0;
+#pragma unroll
+            for (int u = 1; u < G; ++u) {
+                const bool b = t[u] > nk;
+                nk = b ? t[u] : nk;
+                ne = b ? u : ne;
+            }
+            gk[q] = nk;
+            ge[q] = q * G + ne;
         };
-        rescan();
-        for (int r = 0; r < K; ++r) {
-            float gv = bv;
-            int gi = bi;
-            group_best<LPR>(gv, gi, lane);
-            if (live & (j == 0)) {
-                probs[row * K + r] = exp_e(gv - M) * inv_d;
-                idx[row * K + r] = gi;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) scan_group(q, key + q * G);
+        int bk, be;
+        auto best_of_groups = [&]() {
+            bk = gk[0];
+            be = ge[0];
+#pragma unroll
+            for (int q = 1; q < NG; ++q) {
+                const bool b = gk[q] > bk;
+                bk = b ? gk[q] : bk;
+                be = b ? ge[q] : be;
             }
-            if ((bi == gi) & (gi != 0x7FFFFFFF)) {  // this lane held the row's best: retire it
-                avail &= ~(1u << bb);
-                rescan();
+        };
+        best_of_groups();
+        if constexpr (kLds) {
+            if (K > 1) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    s_keys[q][tid] = int4{key[4 * q], key[4 * q + 1], key[4 * q + 2], key[4 * q + 3]};
+            }
+        }
+
+        for (int r = 0; r < K; ++r) {
+            const int bc = bk == kKeyRetired ? INT_MAX : column(be);
+            int wk = bk, wc = bc;
+            group_best_key<LPR>(wk, wc);
+            if (live & (j == 0)) {
+                probs[row * K + r] = exp_e(key_value(wk) - M) * inv_d;
+                idx[row * K + r] = wc;
+            }
+            if ((r + 1 < K) & (bc == wc) & (wc != INT_MAX)) {
+                // this lane held the row's best: retire it, then refresh the
+                // best of its group
+                if constexpr (kLds) {
+                    const int q = be / G;
+                    // the store comes first: one lane's LDS accesses complete
+                    // in order, so the group read below sees it
+                    reinterpret_cast<int*>(&s_keys[be >> 2][tid])[be & 3] = kKeyRetired;
+                    int t[G];
+#pragma unroll
+                    for (int w = 0; w < G / 4; ++w) {
+                        const int4 kk = s_keys[q * (G / 4) + w][tid];
+                        t[4 * w] = kk.x;
+                        t[4 * w + 1] = kk.y;
+                        t[4 * w + 2] = kk.z;
+                        t[4 * w + 3] = kk.w;
+                    }
+                    int nk = t[0], ne = 0;
+#pragma unroll
+                    for (int u = 1; u < G; ++u) {
+                        const bool b = t[u] > nk;
+                        nk = b ? t[u] : nk;
+                        ne = b ? u : ne;
+                    }
+#pragma unroll
+                    for (int p = 0; p < NG; ++p) {
+                        gk[p] = p == q ? nk : gk[p];
+                        ge[p] = p == q ? q * G + ne : ge[p];
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < N; ++u) key[u] = u == be ? kKeyRetired : key[u];
+                    scan_group(0, key);
+                }
+                best_of_groups();
             }
         }
     }

@@ -707,7 +707,8 @@ def test_topk_rows_mostly_neg_inf(ons, orc, bf16):
 # batches the short-row (register-resident) top-K serves: many rows of up to
 # 1024 columns, rows of <= 64 columns at any batch; K up to 32
 TOPK_ROWS_CASES = [(16384, 100, 32), (16384, 512, 8), (20000, 1000, 2), (2000, 60, 16), (300, 16, 8), (5000, 127, 2),
-                   (16384, 255, 32), (64, 5, 5)]
+                   (16384, 255, 32), (64, 5, 5), (9000, 1000, 16), (5000, 300, 8), (3000, 100, 16), (1500, 128, 8),
+                   (3000, 500, 4), (10000, 512, 32), (100, 16, 16)]
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
@@ -719,6 +720,8 @@ def test_topk_short_rows(ons, orc, bf16):
         x32[1::7, cols // 2:] = -np.inf                          # half -inf
         x32[2::11, :] = -np.inf                                  # only -inf
         x32[4::13, cols - 1] = 20.0                              # the best at the row end
+        x32[6::19] = -1.0                                        # -0.0 ties +0.0: lower index first
+        x32[6::19, [0, cols - 1]] = [-0.0, 0.0]
         x32[5::17, cols // 3] = np.nan                           # NaN rows: probabilities NaN
         x = bf16_bits(x32) if bf16 else x32
         nan_rows = np.arange(5, rows, 17)
