@@ -313,10 +313,13 @@ def perf_map(ons, stream) -> str:
                   f"{'GB/s':>8s} {'%':>6s}"]
     for dt in (torch.float32, torch.bfloat16):
         es = 2 if dt == torch.bfloat16 else 4
-        for rows, cols in ((16384, 512), (4096, 2048), (2048, 8192), (1024, 32000), (4096, 32000), (256, 50257),
+        for rows, cols in ((65536, 16), (65536, 64), (65536, 128), (1024, 256), (16384, 256), (65536, 256),
+                           (16384, 512), (4096, 2048), (2048, 8192), (1024, 32000), (4096, 32000), (256, 50257),
                            (16, 128256), (64, 128256), (256, 128256), (1024, 128256), (16, 1 << 20)):
             x = (torch.randn(rows, cols, device="cuda", generator=gen) * 3).to(dt)
             for K in (1, 8, 32):
+                if K > cols:
+                    continue
                 S = ons.os_topk_plan(rows, cols, K)
                 ws = None
                 if S > 1:
@@ -464,6 +467,19 @@ def all_configs(ons, stream):
                   "algorithmic_bytes": nbytes,
                   "topk": {"us": round(t * 1e6, 2), "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1)}})
     del x
+
+    # a mixture-of-experts router's shape (many tokens, a few hundred experts):
+    # not one of the five workloads; served by the short-row top-K kernel
+    for rows, cols, dt, K in ((65536, 256, torch.float32, 8), (16384, 128, torch.bfloat16, 8),
+                              (65536, 64, torch.float32, 2)):
+        g = torch.Generator("cuda").manual_seed(rows + cols)
+        x = (torch.randn(rows, cols, device="cuda", generator=g) * 3).to(dt)
+        nbytes = rows * cols * x.element_size() + rows * K * 8
+        t, _ = measure(lambda: ons.os_softmax_topk_ex(x, K, 1, None), 200)
+        table.append({"case": "router_topk", "rows": rows, "cols": cols, "dtype": str(dt).replace("torch.", ""),
+                      "K": K, "algorithmic_bytes": nbytes,
+                      "topk": {"us": round(t * 1e6, 2), "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 1)}})
+        del x
     return table
 
 
