@@ -624,7 +624,7 @@ int topk_waves(int64_t units, int64_t seg_cols, int K, int dtype) {
     return W;
 }
 
-// Register-resident top-K shapes for short rows (up to 1024 columns): lanes
+// Register-resident top-K shapes for short rows (up to 2048 columns): lanes
 // per row x 16-byte slots per lane, at most 32 entries per lane (fp32 up to 8
 // slots, bf16 up to 4), by capacity.
 typedef void (*TopkRowsKernel)(const void*, float*, int*, int64_t, int, int);
@@ -636,10 +636,10 @@ struct TopkRowsShape {
 const TopkRowsShape kTopkRowsF32[] = {
     ONORM_TOPK_ROWS(false, 4, 1),  ONORM_TOPK_ROWS(false, 4, 2),  ONORM_TOPK_ROWS(false, 4, 4),
     ONORM_TOPK_ROWS(false, 4, 8),  ONORM_TOPK_ROWS(false, 8, 8),  ONORM_TOPK_ROWS(false, 16, 8),
-    ONORM_TOPK_ROWS(false, 32, 8)};
+    ONORM_TOPK_ROWS(false, 32, 8), ONORM_TOPK_ROWS(false, 64, 8)};
 const TopkRowsShape kTopkRowsBF16[] = {
     ONORM_TOPK_ROWS(true, 4, 1),  ONORM_TOPK_ROWS(true, 4, 2),  ONORM_TOPK_ROWS(true, 4, 4),
-    ONORM_TOPK_ROWS(true, 8, 4),  ONORM_TOPK_ROWS(true, 16, 4), ONORM_TOPK_ROWS(true, 32, 4)};
+    ONORM_TOPK_ROWS(true, 8, 4),  ONORM_TOPK_ROWS(true, 16, 4), ONORM_TOPK_ROWS(true, 32, 4), ONORM_TOPK_ROWS(true, 64, 4)};
 #undef ONORM_TOPK_ROWS
 
 // The short-row shape for these rows, or nullptr when they are too long.
@@ -658,22 +658,30 @@ const TopkRowsShape* topk_rows_shape(int64_t cols, int dtype, bool al) {
 // on many rows (where the tiled kernel pays its per-workgroup cost per row)
 // and for small K; on a few wide rows the tiled kernel's waves share the
 // selection instead.  Largest K it serves, by row length (<= 16, 64, 128,
-// 256, 512, 1024 columns; longer rows never) and batch (< 2048, < 4096,
-// < 8192, more rows), measured on MI355X against the tiled kernel over
-// 64..65536 rows, K = 1..32, both dtypes: where it is used it was as fast or
-// faster (up to 23x at 65536 rows of 16, 4.6x at 65536 x 256 for K = 8), and
-// where it is not it was slower.
+// 256, 512, 1024, 2048 columns; longer rows never) and batch (< 2048,
+// < 4096, < 8192, more rows), measured on MI355X against the tiled kernel
+// over 64..65536 rows, K = 1..32, both dtypes: where it is used it was as
+// fast or faster (up to 23x at 65536 rows of 16, 4.6x at 65536 x 256 for
+// K = 8, 1.2-1.6x on rows of 1500-2048 for K <= 2), and where it is not it
+// was slower.
 bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
-    static const int kMaxK[6][4] = {
+    static const int kMaxK[7][4] = {
         {32, 32, 32, 32},  // <= 16 columns
         {16, 16, 32, 32},  // <= 64
         {8, 16, 32, 32},   // <= 128
         {2, 4, 8, 32},     // <= 256
         {2, 4, 8, 32},     // <= 512
         {2, 4, 16, 16},    // <= 1024
+        {2, 4, 4, 4},      // <= 2048
     };
-    if (topk_rows_shape(cols, dtype, al) == nullptr || cols > 1024) return false;
-    const int cb = cols <= 16 ? 0 : cols <= 64 ? 1 : cols <= 128 ? 2 : cols <= 256 ? 3 : cols <= 512 ? 4 : 5;
+    if (topk_rows_shape(cols, dtype, al) == nullptr || cols > 2048) return false;
+    const int cb = cols <= 16    ? 0
+                   : cols <= 64  ? 1
+                   : cols <= 128 ? 2
+                   : cols <= 256 ? 3
+                   : cols <= 512 ? 4
+                   : cols <= 1024 ? 5
+                                  : 6;
     const int rb = rows < 2048 ? 0 : rows < 4096 ? 1 : rows < 8192 ? 2 : 3;
     return K <= kMaxK[cb][rb];
 }

@@ -1169,7 +1169,7 @@ __global__ void __launch_bounds__(W * 64)
 
 // ---------------------------------------------------------------------------
 // Fused softmax + top-K for short rows (paper summary, section 4), the shape
-// of a mixture-of-experts router: many rows of up to 1024 entries.  LPR <= 64
+// of a mixture-of-experts router: many rows of up to 2048 entries.  LPR <= 64
 // lanes share a row and hold it in registers (VPL 16-byte slots each, at most
 // 32 entries per lane), several rows per wavefront, no barriers; the row is
 // read once.

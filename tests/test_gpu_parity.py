@@ -705,10 +705,11 @@ def test_topk_rows_mostly_neg_inf(ons, orc, bf16):
 
 
 # batches the short-row (register-resident) top-K serves: many rows of up to
-# 1024 columns, rows of <= 64 columns at any batch; K up to 32
+# 2048 columns, rows of <= 64 columns at any batch; K up to 32
 TOPK_ROWS_CASES = [(16384, 100, 32), (16384, 512, 8), (20000, 1000, 2), (2000, 60, 16), (300, 16, 8), (5000, 127, 2),
                    (16384, 255, 32), (64, 5, 5), (9000, 1000, 16), (5000, 300, 8), (3000, 100, 16), (1500, 128, 8),
-                   (3000, 500, 4), (10000, 512, 32), (100, 16, 16)]
+                   (3000, 500, 4), (10000, 512, 32), (100, 16, 16), (5000, 2000, 2), (3000, 2048, 4),
+                   (300, 1500, 1)]
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
