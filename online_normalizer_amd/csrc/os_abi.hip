@@ -302,11 +302,13 @@ int grid_for(int64_t groups, int block, int requested) {
     return static_cast<int>(g);
 }
 
-// Rows past the register-resident limit: on aligned rows of up to this many
-// columns the hybrid kernel keeps the first 65536 elements in registers and
-// streams the rest (measured 15-20% faster than streaming the whole row twice
-// up to 262144 columns; no better on longer rows, where the resident share is
-// small).
+// Rows past the register-resident limit: on rows of up to this many columns
+// the hybrid kernel keeps the first 65536 fp32 (57344 bf16) elements in
+// registers and the next 32768 fp32 (65536 bf16) in LDS, and streams the rest
+// twice (measured 15-30% faster than streaming the whole row twice up to
+// 262144 columns; no better on longer rows, where the on-chip share is small).
+// bf16 keeps 7 vectors per lane: with 8 the registers left for the streamed
+// tiles were measured 2-4% slower.
 constexpr int64_t kHybridMaxCols = 4 * 65536;
 
 // The register-resident shape os_softmax_forward takes for these rows
@@ -316,8 +318,8 @@ void plan_rows(const void* in, const void* out, int64_t cols, int dtype, int* lp
 }
 
 RowKernel hybrid_kernel(int dtype, bool al) {
-    if (dtype == OS_BF16) return al ? k_hybrid<true, 8, 2, true> : k_hybrid<true, 8, 2, false>;
-    return al ? k_hybrid<false, 16, 2, true> : k_hybrid<false, 16, 2, false>;
+    if (dtype == OS_BF16) return al ? k_hybrid<true, 7, 2, true, 4> : k_hybrid<true, 7, 2, false, 4>;
+    return al ? k_hybrid<false, 16, 2, true, 4> : k_hybrid<false, 16, 2, false, 4>;
 }
 
 int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t rows,

@@ -403,10 +403,26 @@ __global__ void __launch_bounds__(W * 64)
 // k_stream).  Pass 1: e_k = e^{x_k - m_r} over the resident slots (m_r the
 // lane's resident maximum), then the streamed tiles fold into the same lane
 // state by the tile form of the recurrence; lanes and waves merge with (+).
-// Pass 2 writes the resident slots as e_k * (e^{m_r - m} / d) and re-reads
-// the streamed ones.  HBM traffic per row: in + out + the streamed part again.
+// Pass 2 writes the resident slots as e_k * (e^{m_r - m} / d).  The first
+// STASH streamed tiles are also kept in LDS during pass 1 (up to 128 KiB: the
+// workgroup has the CU to itself), so pass 2 re-reads only the streamed tiles
+// past them.  HBM traffic per row: in + out + the streamed part beyond
+// the LDS copy again.
 // ---------------------------------------------------------------------------
-template <bool BF16, int VPL, int U, bool ALIGNED>
+template <bool BF16>
+__device__ __forceinline__ u32x4 pack_exact(const float* v) {
+    if constexpr (BF16) {  // values widened from bf16: their top halves
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = __builtin_amdgcn_perm(__float_as_uint(v[2 * i + 1]), __float_as_uint(v[2 * i]), 0x07060302u);
+        return r;
+    } else {
+        return Elt<false>::pack(v);
+    }
+}
+
+template <bool BF16, int VPL, int U, bool ALIGNED, int STASH>
 __global__ void __launch_bounds__(1024)
     k_hybrid(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
@@ -414,7 +430,13 @@ __global__ void __launch_bounds__(1024)
     constexpr int W = 16;
     constexpr int BLOCK = W * 64;
     constexpr int RES = BLOCK * VPL;  // resident vector slots per row
+    constexpr int TILE = BLOCK * U;   // streamed slots per step
+    static_assert(STASH * TILE * 16 <= 128 * 1024, "LDS copy of at most 128 KiB");
     __shared__ State lds[2][W];
+    // streamed tile t < STASH, slot u * BLOCK + lane at
+    // stash[t * TILE + u * BLOCK + lane]: each lane reads back only what it
+    // wrote, so pass 2 needs no barrier for it
+    __shared__ u32x4 stash[STASH > 0 ? STASH * TILE : 1];
 
     const int tid = threadIdx.x;
     const bool same = same_phase(in, out);
@@ -441,9 +463,7 @@ __global__ void __launch_bounds__(1024)
                 dl += xr[v][k];
             }
         float ml = mr;
-        for (int base = RES; base < nvec; base += BLOCK * U) {
-            float x[U][VEC];
-            load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
+        auto fold = [&](const float (&x)[U][VEC]) {
             float mc = kFloor;
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -457,6 +477,21 @@ __global__ void __launch_bounds__(1024)
                 for (int k = 0; k < VEC; ++k) acc += exp_e(x[u][k] - mn);
             dl = acc;
             ml = mn;
+        };
+        int base = RES;
+        if (out != nullptr) {  // the tiles kept in LDS
+            for (int t = 0; (t < STASH) & (base < nvec); ++t, base += TILE) {
+                float x[U][VEC];
+                load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
+#pragma unroll
+                for (int u = 0; u < U; ++u) stash[t * TILE + u * BLOCK + tid] = pack_exact<BF16>(x[u]);
+                fold(x);
+            }
+        }
+        for (; base < nvec; base += TILE) {
+            float x[U][VEC];
+            load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
+            fold(x);
         }
         State s = group_merge<64>(State{ml, dl});
         if ((tid & (kWave - 1)) == 0) lds[par][tid / kWave] = s;
@@ -478,15 +513,25 @@ __global__ void __launch_bounds__(1024)
                 for (int k = 0; k < VEC; ++k) xr[v][k] *= scale;
                 store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * BLOCK + tid, nvec, cols, true, xr[v], v == 0);
             }
-            for (int base = RES; base < nvec; base += BLOCK * U) {
-                float x[U][VEC];
-                load_slots<BF16, U, ALIGNED, true>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
+            auto put = [&](float (&x)[U][VEC], int b) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) x[u][k] = exp_e(x[u][k] - s.m) * inv_d;
-                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, base + u * BLOCK + tid, nvec, cols, true, x[u], u == 0);
+                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, b + u * BLOCK + tid, nvec, cols, true, x[u], u == 0);
                 }
+            };
+            int b = RES;
+            for (int t = 0; (t < STASH) & (b < nvec); ++t, b += TILE) {
+                float x[U][VEC];
+#pragma unroll
+                for (int u = 0; u < U; ++u) E::unpack(stash[t * TILE + u * BLOCK + tid], x[u]);
+                put(x, b);
+            }
+            for (; b < nvec; b += TILE) {
+                float x[U][VEC];
+                load_slots<BF16, U, ALIGNED, true>(bin, ri, b + tid, BLOCK, nvec, cols, true, x);
+                put(x, b);
             }
         }
     }

@@ -159,10 +159,13 @@ def test_streaming_two_pass(ons, orc, bf16):
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_hybrid_long_rows(ons, orc, bf16):
     """Aligned rows past the register-resident limit (up to 262144 columns) take the
-    hybrid kernel: the first 65536 elements stay in registers, the rest stream.
-    Rows put the maximum in the streamed part only, make the resident part all
-    -inf, or hold NaN / +inf / only -inf."""
-    for rows, cols in ((3, 65544), (17, 100000), (5, 128256), (2, 200000), (2, 262144)):
+    hybrid kernel: the first 65536 (fp32) or 57344 (bf16) elements stay in
+    registers, the next 32768 (fp32) or 65536 (bf16) stream once and are kept
+    in LDS, the rest stream twice; lengths at and just past the end of the LDS
+    copy.  Rows put the maximum in the streamed part only, make the first 65536
+    entries all -inf, or hold NaN / +inf / only -inf."""
+    for rows, cols in ((3, 65544), (17, 100000), (5, 128256), (2, 200000), (2, 262144), (3, 98304), (3, 98308),
+                       (3, 122880), (3, 122888)):
         x32 = workloads.normal(rows, cols, seed=cols + 3, scale=3.0)
         x32[0, cols - 5] = 90.0                 # the row maximum, in the streamed part
         if rows > 2:
