@@ -251,7 +251,14 @@ constexpr int resident_min_waves() {
     return (VPL <= 4 && !(BF16 && !ALIGNED && LPR >= 256 && VPL == 4)) ? 8 : 1;
 }
 
-template <bool BF16, int LPR, int VPL, bool ALIGNED>
+//
+// STAGE (multi-row workgroups on rows that are not 16-byte aligned): the
+// workgroup's rows are one contiguous run of the output, so pass 2 assembles
+// that run in LDS, with each lane placing only its own row's elements, and the
+// workgroup then writes it as whole 16-byte blocks.  Only the run's first and
+// last blocks, shared with the neighbouring workgroups, go out element by
+// element, instead of every row's two partial slots.
+template <bool BF16, int LPR, int VPL, bool ALIGNED, bool STAGE>
 __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF16, LPR, VPL, ALIGNED>()))
     k_resident(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
@@ -260,7 +267,11 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF1
     constexpr int RPB = BLOCK / LPR;
     constexpr int W = LPR > 64 ? LPR / 64 : 1;
     constexpr int GROUP = LPR < 64 ? LPR : 64;
+    static_assert(!STAGE || (LPR <= 64 && !ALIGNED), "staged stores are for multi-row unaligned rows");
     __shared__ State lds[2][W];
+    // the run's bytes: each row spans at most LPR * VPL blocks, and the run
+    // starts inside its first block
+    __shared__ u32x4 img[STAGE ? RPB * LPR * VPL + 2 : 1];
 
     const int tid = threadIdx.x;
     const int j = tid % LPR;
@@ -314,11 +325,63 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF1
             const Span so = rows_span<BF16, ALIGNED, (LPR <= 64)>(out, row0 * cols, nrows * cols, gmask);
             const Buf bout(so.base, so.bytes);
             const RowAt ro = rows_row<BF16, ALIGNED, (LPR <= 64)>(so.lead + static_cast<uint32_t>(g) * row_bytes, gmask);
+            if constexpr (STAGE) {
+                // place this lane's entries at their byte offsets in the run
+                char* const ib = reinterpret_cast<char*>(img);
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) {
+                for (int v = 0; v < VPL; ++v) {
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) x[v][k] *= scale;
-                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, ns, cols, live, x[v], v == 0);
+                    for (int k = 0; k < VEC; ++k) x[v][k] *= scale;
+                    const int vi = v * LPR + j;
+                    const int e0 = vi * VEC - ri.ph;
+                    const bool ok = live & (vi < ns) & ((v > 0) | (e0 > -VEC));
+                    const bool whole = ok & (e0 >= 0) & (e0 + VEC <= cols) & same;
+                    if (whole) img[(ro.blk + static_cast<uint32_t>(ro.ph - ri.ph) * E::kSize) / 16u + vi] = E::pack(x[v]);
+                    if (ok & !whole) {
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) {
+                            const int e = e0 + k;
+                            if (static_cast<uint32_t>(e) < static_cast<uint32_t>(cols)) {
+                                const uint32_t at = ro.blk + static_cast<uint32_t>(e + ro.ph) * E::kSize;
+                                if constexpr (BF16)
+                                    *reinterpret_cast<uint16_t*>(ib + at) =
+                                        static_cast<uint16_t>(pack_bf16x2(x[v][k], 0.0f) & 0xFFFFu);
+                                else
+                                    *reinterpret_cast<float*>(ib + at) = x[v][k];
+                            }
+                        }
+                    }
+                }
+                __syncthreads();
+                // the run: bytes [so.lead, so.lead + n) of so.bytes / 16 blocks;
+                // blocks holding bytes of other workgroups' rows go out entry by entry
+                const uint32_t n = static_cast<uint32_t>(nrows) * row_bytes;
+                const int nblk = static_cast<int>(so.bytes / 16u);
+                for (int i = tid; i < nblk; i += BLOCK) {
+                    const uint32_t b0 = static_cast<uint32_t>(i) * 16u;
+                    const bool edge = (b0 < so.lead) | (b0 + 16u > so.lead + n);
+                    if (!edge) {
+                        bout.store16(b0, img[i]);
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) {
+                            const uint32_t at = b0 + static_cast<uint32_t>(k) * E::kSize;
+                            const bool mine = (at >= so.lead) & (at < so.lead + n);
+                            if constexpr (BF16)
+                                bout.store2(mine ? at : kOutside, *reinterpret_cast<const uint16_t*>(ib + at));
+                            else
+                                bout.store4(mine ? at : kOutside, *reinterpret_cast<const uint32_t*>(ib + at));
+                        }
+                    }
+                }
+                __syncthreads();
+            } else {
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) x[v][k] *= scale;
+                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, ns, cols, live, x[v], v == 0);
+                }
             }
         }
     }
