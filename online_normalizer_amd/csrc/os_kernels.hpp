@@ -257,8 +257,12 @@ constexpr int resident_min_waves() {
 // that run in LDS, with each lane placing only its own row's elements, and the
 // workgroup then writes it as whole 16-byte blocks.  Only the run's first and
 // last blocks, shared with the neighbouring workgroups, go out element by
-// element, instead of every row's two partial slots.
-template <bool BF16, int LPR, int VPL, bool ALIGNED, bool STAGE>
+// element, instead of every row's two partial slots.  STAGE = 2 also reads the
+// input run into LDS as whole blocks first; a lane's slots then start at its
+// row's first element (slot vi holds entries vi * VEC ..), so such rows need
+// only cols / VEC slots, as aligned rows do, and no row pays a partial slot at
+// its front.
+template <bool BF16, int LPR, int VPL, bool ALIGNED, int STAGE>
 __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF16, LPR, VPL, ALIGNED>()))
     k_resident(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
@@ -267,11 +271,12 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF1
     constexpr int RPB = BLOCK / LPR;
     constexpr int W = LPR > 64 ? LPR / 64 : 1;
     constexpr int GROUP = LPR < 64 ? LPR : 64;
-    static_assert(!STAGE || (LPR <= 64 && !ALIGNED), "staged stores are for multi-row unaligned rows");
+    static_assert(STAGE == 0 || (LPR <= 64 && !ALIGNED), "staging is for multi-row unaligned rows");
     __shared__ State lds[2][W];
     // the run's bytes: each row spans at most LPR * VPL blocks, and the run
     // starts inside its first block
     __shared__ u32x4 img[STAGE ? RPB * LPR * VPL + 2 : 1];
+    char* const ib = reinterpret_cast<char*>(img);
 
     const int tid = threadIdx.x;
     const int j = tid % LPR;
@@ -293,7 +298,40 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF1
         const int ns = slot_count<BF16>(cols, ri.ph);
 
         float x[VPL][VEC];
-        load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, ns, cols, live, x);
+        if constexpr (STAGE == 2) {
+            // the run, as whole blocks, into LDS; then this lane's entries
+            const int nbi = static_cast<int>(si.bytes / 16u);
+            u32x4 t[VPL + 1];
+#pragma unroll
+            for (int q = 0; q <= VPL; ++q) {
+                const int i = tid + q * BLOCK;
+                t[q] = bin.load16<true>(i < nbi ? static_cast<uint32_t>(i) * 16u : kOutside);
+            }
+#pragma unroll
+            for (int q = 0; q <= VPL; ++q)
+                if (tid + q * BLOCK < nbi) img[tid + q * BLOCK] = t[q];
+            __syncthreads();
+            const uint32_t r0 = si.lead + static_cast<uint32_t>(g) * row_bytes;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const int e = (v * LPR + j) * VEC + k;
+                    const uint32_t at = r0 + static_cast<uint32_t>(e) * E::kSize;
+                    float val = -INFINITY;
+                    if (live & (e < cols)) {
+                        if constexpr (BF16)
+                            val = __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(ib + at)) << 16);
+                        else
+                            val = *reinterpret_cast<const float*>(ib + at);
+                    }
+                    x[v][k] = val;
+                }
+            // every lane has its entries: the image may be overwritten
+            __syncthreads();
+        } else {
+            load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, ns, cols, live, x);
+        }
 
         float ml = kFloor;
 #pragma unroll
@@ -325,9 +363,26 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF1
             const Span so = rows_span<BF16, ALIGNED, (LPR <= 64)>(out, row0 * cols, nrows * cols, gmask);
             const Buf bout(so.base, so.bytes);
             const RowAt ro = rows_row<BF16, ALIGNED, (LPR <= 64)>(so.lead + static_cast<uint32_t>(g) * row_bytes, gmask);
-            if constexpr (STAGE) {
+            if constexpr (STAGE == 2) {
+                // the output run's image
+                const uint32_t r0 = so.lead + static_cast<uint32_t>(g) * row_bytes;
+#pragma unroll
+                for (int v = 0; v < VPL; ++v)
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) {
+                        const int e = (v * LPR + j) * VEC + k;
+                        const uint32_t at = r0 + static_cast<uint32_t>(e) * E::kSize;
+                        const float val = x[v][k] * scale;
+                        if (live & (e < cols)) {
+                            if constexpr (BF16)
+                                *reinterpret_cast<uint16_t*>(ib + at) = static_cast<uint16_t>(pack_bf16x2(val, 0.0f) & 0xFFFFu);
+                            else
+                                *reinterpret_cast<float*>(ib + at) = val;
+                        }
+                    }
+            }
+            if constexpr (STAGE == 1) {
                 // place this lane's entries at their byte offsets in the run
-                char* const ib = reinterpret_cast<char*>(img);
 #pragma unroll
                 for (int v = 0; v < VPL; ++v) {
 #pragma unroll
@@ -352,6 +407,8 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF1
                         }
                     }
                 }
+            }
+            if constexpr (STAGE != 0) {
                 __syncthreads();
                 // the run: bytes [so.lead, so.lead + n) of so.bytes / 16 blocks;
                 // blocks holding bytes of other workgroups' rows go out entry by entry

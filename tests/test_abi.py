@@ -239,14 +239,20 @@ def test_forward_plan(ons):
     assert ons.os_forward_plan(4100) == (512, 4)
     assert ons.os_forward_plan(2052) == (256, 4)
     # every automatic shape holds its row, and a row that is not 16-byte
-    # aligned (row bytes not a multiple of 16) gets room for one more block
+    # aligned (row bytes not a multiple of 16) gets room for one more block,
+    # unless a multi-row shape (<= 64 lanes per row) reads it through LDS,
+    # where its length alone counts
     for cols in range(1, 70000, 97):
         for dt, vec in ((torch.float32, 4), (torch.bfloat16, 8)):
             lanes, vecs = ons.os_forward_plan(cols, dt)
             extra = 0 if cols % vec == 0 else vec - 1
-            assert lanes == 0 or lanes * vecs * vec >= cols + extra
-    assert ons.os_forward_plan(127) == (32, 2)   # 127 fp32 may span 33 blocks
+            assert lanes == 0 or lanes * vecs * vec >= cols + extra or (lanes <= 64 and lanes * vecs * vec >= cols)
+    assert ons.os_forward_plan(127) == (32, 1)   # 33 blocks, but read through LDS: 32 slots of its own
+    assert ons.os_forward_plan(129) == (32, 2)
     assert ons.os_forward_plan(124) == (32, 1)
+    assert ons.os_forward_plan(127, torch.bfloat16) == (16, 1)
+    assert ons.os_forward_plan(1001, torch.bfloat16) == (64, 2)   # the same shape either way: direct loads
+    assert ons.os_forward_plan(1023) == (128, 4)   # the aligned shape takes one row per workgroup
     assert ons.os_forward_plan(32000) == (1024, 8)
     assert ons.os_forward_plan(65536) == (1024, 16)
     assert ons.os_forward_plan(65537) == (0, 0)

@@ -258,7 +258,10 @@ def test_misaligned_base_and_in_place(ons, orc):
     assert_fp32_parity(to_host(xd), ref, "in-place safe")
 
 
-UNALIGNED_COLS = [1, 3, 5, 127, 1001, 2047, 4099, 32001, 50257, 65535, 65537, 100003, 262147]
+# 31, 63, 127, 255, 511 and 1023 (bf16) take multi-row shapes that read the rows
+# through LDS; 1001 (bf16) and 129 keep direct loads on the same shape
+UNALIGNED_COLS = [1, 3, 5, 31, 63, 127, 129, 255, 511, 1001, 1023, 2047, 4099, 32001, 50257, 65535, 65537, 100003,
+                  262147]
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
@@ -317,7 +320,7 @@ def test_unaligned_rows_every_path(ons, orc, bf16):
                 assert np.max(np.abs(to_host(p) - pr)) <= TOPK_PROB_ABS, f"top-{K} +{si} cols={cols}"
 
 
-@pytest.mark.parametrize("cols", [6, 128, 1024, 32000, 70000])
+@pytest.mark.parametrize("cols", [6, 63, 127, 128, 1024, 32000, 70000])
 def test_special_values(ons, orc, cols):
     """-inf entries give 0; rows with +inf, NaN, or only -inf give NaN rows."""
     x = workloads.normal(8, cols, seed=cols, scale=2.0)
