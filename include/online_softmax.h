@@ -52,7 +52,9 @@
  *              outside a mapped page).  Writes touch only output elements:
  *              whole blocks where out has in's offset within its 16-byte
  *              block, single elements at the ends of rows and when the offsets
- *              differ.
+ *              differ.  Several short rows handled together are written as
+ *              whole blocks of their common run, with single elements only at
+ *              the run's two ends.
  */
 #ifndef ONLINE_SOFTMAX_H
 #define ONLINE_SOFTMAX_H
@@ -125,7 +127,9 @@ int os_softmax_forward_tuned(const void *in, void *out, int64_t rows, int64_t co
  * The shape os_softmax_forward uses for rows of `cols` elements of `dtype` in
  * an array whose base is 16-byte aligned (the shape depends on whether the row
  * starts are all 16-byte aligned, i.e. on cols * element size % 16 here).
- * Host only: no HIP call.
+ * Short rows that are not aligned may get a shape that holds only `cols`
+ * elements per row, not the extra block they span: those are read through
+ * LDS.  Host only: no HIP call.
  *   *lanes_per_row, *vecs_per_lane receive the shape (0, 0 for rows longer
  *   than the register-resident kernels hold).
  *   Returns OS_OK or OS_EINVAL.
