@@ -366,8 +366,9 @@ def test_deterministic(ons):
 
 
 def test_graph_replays_match_eager(ons):
-    """The forward (aligned and unaligned rows), the baseline, the top-K (one
-    launch at several widths, and split over two launches) and the split
+    """The forward (aligned rows, unaligned rows with direct, LDS-assembled
+    and LDS-read stores, and long rows with their LDS copy), the baseline, the
+    top-K (tiled, short-row, and split over two launches) and the split
     forward captured in a HIP graph: every replay, with eager work and
     synchronisations between replays, equals the eager result bit for bit."""
     x = to_device(workloads.config(2, 0, 512))
@@ -379,7 +380,7 @@ def test_graph_replays_match_eager(ons):
     xs = to_device(workloads.normal(4, 100003, seed=9, scale=3.0))
     ws = torch.empty(ons.os_softmax_forward_workspace_bytes(4, 8), dtype=torch.uint8, device="cuda")
     sp_ref = ons.os_softmax_forward_split(xs, splits=8, workspace=ws)
-    # the split top-K (two launches), a one-wave-per-row top-K, and an unaligned forward
+    # the split top-K (two launches), the short-row top-K, and unaligned and long-row forwards
     xk = to_device(workloads.normal(16, 128256, seed=10, scale=3.0))
     wk = torch.empty(ons.os_softmax_topk_workspace_bytes(16, 8, 4), dtype=torch.uint8, device="cuda")
     pk_ref, ik_ref = ons.os_softmax_topk_ex(xk, 8, 4, wk)
@@ -387,11 +388,15 @@ def test_graph_replays_match_eager(ons):
     pw_ref, iw_ref = ons.os_softmax_topk_ex(xw, 8, 1, None)
     xu = to_device(workloads.normal(64, 50257, seed=12, scale=3.0))
     yu_ref = ons.os_softmax_forward(xu)
+    x1 = to_device(workloads.normal(5000, 127, seed=13, scale=3.0))   # read through LDS
+    x2 = to_device(workloads.normal(3000, 501, seed=14, scale=3.0))   # stores assembled in LDS
+    y1_ref, y2_ref, yk_ref = ons.os_softmax_forward(x1), ons.os_softmax_forward(x2), ons.os_softmax_forward(xk)
     torch.cuda.synchronize()
     y = torch.empty_like(x)
     s3 = torch.empty_like(x)
     sp = torch.empty_like(xs)
     yu = torch.empty_like(xu)
+    y1, y2, yk = torch.empty_like(x1), torch.empty_like(x2), torch.empty_like(xk)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         ons.os_softmax_forward(x, out=y)
@@ -401,8 +406,11 @@ def test_graph_replays_match_eager(ons):
         pk, ik = ons.os_softmax_topk_ex(xk, 8, 4, wk)
         pw, iw = ons.os_softmax_topk_ex(xw, 8, 1, None)
         ons.os_softmax_forward(xu, out=yu)
+        ons.os_softmax_forward(x1, out=y1)
+        ons.os_softmax_forward(x2, out=y2)
+        ons.os_softmax_forward(xk, out=yk)
     for rep in range(4):
-        for t in (y, s3, p, i, sp, pk, ik, pw, iw, yu):
+        for t in (y, s3, p, i, sp, pk, ik, pw, iw, yu, y1, y2, yk):
             t.zero_()
         junk = ons.os_softmax_forward(torch.randn(64, 1000, device="cuda"))  # eager work between replays
         torch.cuda.synchronize()
@@ -416,6 +424,8 @@ def test_graph_replays_match_eager(ons):
         assert torch.equal(pk, pk_ref) and torch.equal(ik, ik_ref), rep
         assert torch.equal(pw, pw_ref) and torch.equal(iw, iw_ref), rep
         assert torch.equal(yu.view(torch.int32), yu_ref.view(torch.int32)), rep
+        for got, want in ((y1, y1_ref), (y2, y2_ref), (yk, yk_ref)):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32)), rep
         del junk
 
 
