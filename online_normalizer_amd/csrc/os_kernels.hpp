@@ -1390,7 +1390,9 @@ __global__ void __launch_bounds__(W * 64)
 //     8 entries per lane they sit in 4 groups with a best per group, and the
 //     keys also live in LDS (each lane only touches its own words, so no
 //     barrier): retiring an entry is one store and refreshing its group reads
-//     a quarter of the keys instead of rescanning all of them.
+//     a quarter of the keys instead of rescanning all of them.  FEWK (K = 1:
+//     nothing is ever retired) keeps the keys in registers and needs no LDS,
+//     which leaves room for more workgroups per CU.
 // ---------------------------------------------------------------------------
 constexpr int kKeyRetired = INT_MIN;  // outside the row, or already output
 
@@ -1429,14 +1431,14 @@ __device__ __forceinline__ void group_best_key(int& k, int& c) {
     }
 }
 
-template <bool BF16, int LPR, int VPL, bool ALIGNED>
+template <bool BF16, int LPR, int VPL, bool ALIGNED, bool FEWK>
 __global__ void __launch_bounds__(256)
     k_topk_rows(const void* in, float* probs, int* idx, int64_t rows, int cols, int K) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int RPB = 256 / LPR;
     constexpr int N = VPL * VEC;                // entries per lane
-    constexpr bool kLds = N > 8;                // keys in LDS, in groups
+    constexpr bool kLds = (N > 8) & !FEWK;      // keys in LDS, in groups
     constexpr int NG = kLds ? 4 : 1;            // groups per lane
     constexpr int G = N / NG;                   // entries per group
     constexpr int NQ = kLds ? N / 4 : 1;        // 4-key LDS words per lane
