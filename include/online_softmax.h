@@ -92,12 +92,14 @@ extern "C" {
  * CUDA Online Softmax", section 2.2).
  *   in, out   [rows, cols] of `dtype`.
  *   The kernel is chosen from `cols`, `dtype` and the row alignment: rows of
- *   up to 65536 elements stay in registers and are read from HBM once
- *   (several rows per wavefront, one wavefront per row, or one workgroup per
- *   row); rows of up to 262144 elements keep their first 65536 (fp32) or
- *   57344 (bf16) in registers and the next 32768 (fp32) or 65536 (bf16) in
- *   LDS, and read the rest twice; longer rows are streamed in two passes
- *   (fold, then normalise), reading the row twice.
+ *   up to 32768 fp32 or 65536 bf16 elements stay in registers and are read
+ *   from HBM once (several rows per wavefront, one wavefront per row, or one
+ *   workgroup per row); rows of up to 262144 elements keep a leading part in
+ *   registers (32768 to 65536 fp32 elements by row length, 57344 bf16) and
+ *   the next 32768 fp32 or 65536 bf16 in LDS, and read the rest twice (fp32
+ *   rows of up to 65536 and bf16 rows of up to 122880 are so read once);
+ *   longer rows are streamed in two passes (fold, then normalise), reading
+ *   the row twice.
  *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
  */
 int os_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, int dtype,

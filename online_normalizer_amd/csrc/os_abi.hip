@@ -156,11 +156,11 @@ struct PlanEntry {
 constexpr PlanEntry kPlanF32[] = {
     {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {24, 16, 2},      {32, 32, 1},      {48, 32, 2},
     {64, 64, 1},     {128, 64, 2},     {256, 128, 2},    {512, 256, 2},    {640, 256, 4},    {1024, 512, 2},
-    {1536, 512, 4},  {2560, 512, 8},   {4096, 1024, 4},  {8192, 1024, 8},  {16384, 1024, 16}};
+    {1536, 512, 4},  {2560, 512, 8},   {4096, 1024, 4},  {8192, 1024, 8}};
 constexpr PlanEntry kPlanF32Unaligned[] = {
     {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {32, 32, 1},      {40, 32, 2},      {64, 64, 1},
     {128, 64, 2},    {256, 64, 4},     {320, 128, 4},    {512, 256, 2},    {640, 256, 4},    {1024, 512, 2},
-    {2048, 512, 4},  {4096, 1024, 4},  {8192, 1024, 8},  {16384, 1024, 16}};
+    {2048, 512, 4},  {4096, 1024, 4},  {8192, 1024, 8}};
 constexpr PlanEntry kPlanBF16[] = {
     {4, 4, 1},       {8, 8, 1},        {10, 8, 2},       {16, 16, 1},      {32, 16, 2},      {64, 32, 2},
     {128, 64, 2},    {192, 64, 4},     {256, 128, 2},    {384, 64, 8},     {512, 256, 2},    {1024, 256, 4},
@@ -222,9 +222,14 @@ template <size_t N>
 constexpr int last_slots(const PlanEntry (&t)[N]) {
     return t[N - 1].max_slots;
 }
-static_assert(last_slots(kPlanF32) == 16384 && last_slots(kPlanF32Unaligned) == 16384 &&
+// The tables end at 8192 slots (32768 fp32, 65536 bf16 elements).  Longer
+// fp32 rows take the hybrid kernel: 1024 lanes x 16 vectors in registers
+// (the 1024 x 16 shape, still built for os_softmax_forward_tuned) measured
+// 2-8% slower on 40000-65536 columns than 8 vectors in registers plus the
+// hybrid's LDS copy, which also reads such rows once.
+static_assert(last_slots(kPlanF32) == 8192 && last_slots(kPlanF32Unaligned) == 8192 &&
                   last_slots(kPlanBF16) == 8192 && last_slots(kPlanBF16Unaligned) == 8192,
-              "plans end at the register-resident limit (65536 elements)");
+              "plans end at 8192 slots; longer rows take the hybrid or streaming kernels");
 
 void auto_plan(int64_t cols, int dtype, bool al, int* lpr, int* vpl) {
     const int64_t need = slots_needed(cols, dtype, al);
@@ -317,13 +322,14 @@ int grid_for(int64_t groups, int block, int requested) {
     return static_cast<int>(g);
 }
 
-// Rows past the register-resident limit: on rows of up to this many columns
-// the hybrid kernel keeps the first 65536 fp32 (57344 bf16) elements in
-// registers and the next 32768 fp32 (65536 bf16) in LDS, and streams the rest
-// twice (measured 15-30% faster than streaming the whole row twice up to
-// 262144 columns; no better on longer rows, where the on-chip share is small).
-// bf16 keeps 7 vectors per lane: with 8 the registers left for the streamed
-// tiles were measured 2-4% slower.
+// Rows past the register-resident plans: on rows of up to this many columns
+// the hybrid kernel keeps the row's first 1024 x VPL vectors in registers
+// (VPL = 7 for bf16; 8, 12 or 16 for fp32 by row length) and the next 4
+// streamed tiles (128 KiB) in LDS, and streams the rest twice (measured
+// 15-30% faster than streaming the whole row twice up to 262144 columns; no
+// better on longer rows, where the on-chip share is small).  bf16 keeps 7
+// vectors per lane: with 8 the registers left for the streamed tiles were
+// measured 2-4% slower.
 constexpr int64_t kHybridMaxCols = 4 * 65536;
 
 // The register-resident shape os_softmax_forward takes for these rows
@@ -352,8 +358,13 @@ void plan_rows(const void* in, const void* out, int64_t cols, int dtype, int* lp
     plan_for(cols, dtype, vector_ok(in, out, cols, dtype), lpr, vpl, staged);
 }
 
-RowKernel hybrid_kernel(int dtype, bool al) {
+RowKernel hybrid_kernel(int64_t cols, int dtype, bool al) {
     if (dtype == OS_BF16) return al ? k_hybrid<true, 7, 2, true, 4> : k_hybrid<true, 7, 2, false, 4>;
+    // fp32: the register part grows with the row (measured best: 8 vectors
+    // per lane up to 65536 columns, all of it on chip with the LDS copy; 12 up
+    // to 131072; 16 beyond)
+    if (cols <= 65536) return al ? k_hybrid<false, 8, 2, true, 4> : k_hybrid<false, 8, 2, false, 4>;
+    if (cols <= 131072) return al ? k_hybrid<false, 12, 2, true, 4> : k_hybrid<false, 12, 2, false, 4>;
     return al ? k_hybrid<false, 16, 2, true, 4> : k_hybrid<false, 16, 2, false, 4>;
 }
 
@@ -379,7 +390,7 @@ int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t 
     (void)hipGetLastError();
     if (shape == nullptr) {
         if (allow_hybrid && cols <= kHybridMaxCols) {
-            const RowKernel k = hybrid_kernel(dtype, al);
+            const RowKernel k = hybrid_kernel(cols, dtype, al);
             hipLaunchKernelGGL(k, dim3(grid_for(rows, 1024, grid_req)), dim3(1024), 0, st, in, out, stats, rows,
                                static_cast<int>(cols), kGrid128);
             return launched(fn);
@@ -489,15 +500,13 @@ int64_t os_softmax_forward_workspace_bytes(int64_t rows, int splits) {
 
 int os_forward_split_plan(int64_t rows, int64_t cols, int dtype) {
     if (rows <= 0 || cols <= 0 || cols > OS_MAX_COLS || (dtype != OS_F32 && dtype != OS_BF16)) return 1;
-    // Rows that fit the register-resident kernels are read once and are not
-    // split (the second launch and read cost more than idle CUs on every
-    // batch measured).  Longer rows are split into the most slices that keep
-    // the batch at <= 256 workgroups (one per CU) and every slice >= 1024
-    // vectors (16 KB) (measured on MI355X over 1..256 rows of 128256 to 2^24
-    // columns, fp32 and bf16).
-    int lpr = 0, vpl = 0;
-    auto_plan(cols, dtype, true, &lpr, &vpl);
-    if (lpr != 0) return 1;
+    // Rows of up to 65536 elements are read once (registers, or registers
+    // and LDS) and are not split (the second launch and read cost more than
+    // idle CUs on every batch measured).  Longer rows are split into the most
+    // slices that keep the batch at <= 256 workgroups (one per CU) and every
+    // slice >= 1024 vectors (16 KB) (measured on MI355X over 1..256 rows of
+    // 128256 to 2^24 columns, fp32 and bf16).
+    if (cols <= 65536) return 1;
     const int64_t vecs = vectors_needed(cols, dtype);
     int S = 1;
     while (S < OS_FWD_MAX_SPLITS && rows * S * 2 <= 256 && vecs / (S * 2) >= 1024) S *= 2;

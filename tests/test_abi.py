@@ -254,7 +254,9 @@ def test_forward_plan(ons):
     assert ons.os_forward_plan(1001, torch.bfloat16) == (64, 2)   # the same shape either way: direct loads
     assert ons.os_forward_plan(1023) == (128, 4)   # the aligned shape takes one row per workgroup
     assert ons.os_forward_plan(32000) == (1024, 8)
-    assert ons.os_forward_plan(65536) == (1024, 16)
+    assert ons.os_forward_plan(32768) == (1024, 8)
+    assert ons.os_forward_plan(32769) == (0, 0)    # the hybrid: registers and LDS
+    assert ons.os_forward_plan(65536) == (0, 0)
     assert ons.os_forward_plan(65537) == (0, 0)
     assert ons.os_forward_plan(65536, torch.bfloat16) == (1024, 8)
     assert ons.os_forward_plan(65537, torch.bfloat16) == (0, 0)

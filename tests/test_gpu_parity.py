@@ -158,18 +158,20 @@ def test_streaming_two_pass(ons, orc, bf16):
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_hybrid_long_rows(ons, orc, bf16):
-    """Aligned rows past the register-resident limit (up to 262144 columns) take the
-    hybrid kernel: the first 65536 (fp32) or 57344 (bf16) elements stay in
-    registers, the next 32768 (fp32) or 65536 (bf16) stream once and are kept
-    in LDS, the rest stream twice; lengths at and just past the end of the LDS
-    copy.  Rows put the maximum in the streamed part only, make the first 65536
-    entries all -inf, or hold NaN / +inf / only -inf."""
+    """Aligned rows past the register-resident plans (up to 262144 columns) take the
+    hybrid kernel: the first 1024 x VPL vectors stay in registers (fp32: 32768,
+    49152 or 65536 elements by row length; bf16: 57344), the next 32768 (fp32)
+    or 65536 (bf16) stream once and are kept in LDS, the rest stream twice;
+    lengths at and just past the end of the LDS copy for each register part.
+    Rows put the maximum in the streamed part only, make the first 65536
+    entries (or all but the last 5) -inf, or hold NaN / +inf / only -inf."""
     for rows, cols in ((3, 65544), (17, 100000), (5, 128256), (2, 200000), (2, 262144), (3, 98304), (3, 98308),
-                       (3, 122880), (3, 122888)):
+                       (3, 122880), (3, 122888), (5, 32772), (5, 49152), (5, 65536), (3, 81920), (3, 81924),
+                       (3, 131072), (3, 131076)):
         x32 = workloads.normal(rows, cols, seed=cols + 3, scale=3.0)
         x32[0, cols - 5] = 90.0                 # the row maximum, in the streamed part
         if rows > 2:
-            x32[1, :65536] = -np.inf            # nothing in the resident part
+            x32[1, :min(65536, cols - 5)] = -np.inf  # nothing in the register part
             x32[2, 70000 % cols] = np.nan
         if rows > 4:
             x32[3, :] = -np.inf
