@@ -362,9 +362,10 @@ RowKernel hybrid_kernel(int64_t cols, int dtype, bool al) {
     if (dtype == OS_BF16) return al ? k_hybrid<true, 7, 2, true, 4> : k_hybrid<true, 7, 2, false, 4>;
     // fp32: the register part grows with the row (measured best: 8 vectors
     // per lane up to 65536 columns, all of it on chip with the LDS copy; 12 up
-    // to 131072; 16 beyond)
+    // to 110000; 16 beyond, where 12 and 16 measured within 1% on 128256 and
+    // 16 re-reads less)
     if (cols <= 65536) return al ? k_hybrid<false, 8, 2, true, 4> : k_hybrid<false, 8, 2, false, 4>;
-    if (cols <= 131072) return al ? k_hybrid<false, 12, 2, true, 4> : k_hybrid<false, 12, 2, false, 4>;
+    if (cols <= 110000) return al ? k_hybrid<false, 12, 2, true, 4> : k_hybrid<false, 12, 2, false, 4>;
     return al ? k_hybrid<false, 16, 2, true, 4> : k_hybrid<false, 16, 2, false, 4>;
 }
 
