@@ -304,7 +304,8 @@ def perf_map(ons, stream) -> str:
             y = torch.empty_like(x)
             t = graph_us(lambda: ons.os_softmax_forward(x, out=y))
             nb = 2 * rows * cols * es
-            shape = "x".join(map(str, ons.os_forward_plan(cols, dt))) if cols <= 65536 else "long"
+            lanes, vecs = ons.os_forward_plan(cols, dt)
+            shape = f"{lanes}x{vecs}" if lanes else ("hybrid" if cols <= 262144 else "stream")
             odd = " odd" if (cols * es) % 16 else ""
             lines.append(f"{'':>8s} {str(dt)[6:]:>8s} {rows:>9d} {cols:>8d} {shape:>9s} {t:>10.2f} "
                          f"{nb / t / 1e3:>8.1f} {100 * nb / t / 1e3 / PEAK_HBM_GBS:>6.1f}{odd}")
