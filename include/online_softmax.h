@@ -46,10 +46,13 @@
  *              os_last_error() describes the last failure on the calling thread.
  *   Alignment  pointers must be aligned to their element size.  Every row is
  *              moved with 128-bit accesses: rows whose starts are not 16-byte
- *              aligned are read as the 16-byte blocks they overlap, so a read
- *              may touch up to 15 bytes before a row range's first element or
- *              after its last, never outside those blocks (and so never
- *              outside a mapped page).  Writes touch only output elements:
+ *              aligned are read as the 16-byte blocks they overlap, and a
+ *              kernel that gives a whole workgroup to one row may start at
+ *              the 128-byte line holding the row's first element.  So a read
+ *              may touch up to 127 bytes before a row range's first element
+ *              (within that element's 128-byte line) and up to 15 bytes after
+ *              its last (within its 16-byte block), and so never leaves a
+ *              mapped page.  Writes touch only output elements:
  *              whole blocks where out has in's offset within its 16-byte
  *              block, single elements at the ends of rows and when the offsets
  *              differ.  Several short rows handled together are written as
