@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 N_CASES = 48
-COLS = [1, 2, 3, 5, 8, 17, 64, 100, 127, 1000, 2047, 4096, 4099, 8193, 16384, 32000, 65536, 65537, 131072, 200003]
+COLS = [1, 2, 3, 5, 8, 17, 63, 64, 100, 127, 255, 511, 1000, 2047, 4096, 4099, 8193, 16384, 32000, 40000, 65536,
+        65537, 81920, 131072, 200003]
 
 
 @pytest.fixture(scope="module")
