@@ -1404,31 +1404,44 @@ __device__ __forceinline__ int order_key(float x) {
 
 __device__ __forceinline__ float key_value(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(dpp<CTRL>(static_cast<int>(v)));
+}
+
 // Every lane of each aligned group of LPR lanes ends with the group's best
-// (key, column): larger key first, then lower column.
+// (key, column): larger key first, then lower column.  The pair is compared
+// as one unsigned 64-bit number, (key + 2^31) above (2^32 - 1 - column), so a
+// step is two DPP moves, one 64-bit compare and two selects.
 template <int LPR>
 __device__ __forceinline__ void group_best_key(int& k, int& c) {
-    auto take = [&](int ok, int oc) {
-        const bool t = (ok > k) | ((ok == k) & (oc < c));
-        k = t ? ok : k;
-        c = t ? oc : c;
+    uint32_t hi = static_cast<uint32_t>(k) ^ 0x80000000u;
+    uint32_t lo = ~static_cast<uint32_t>(c);
+    auto take = [&](uint32_t ohi, uint32_t olo) {
+        const uint64_t mine = (static_cast<uint64_t>(hi) << 32) | lo;
+        const uint64_t other = (static_cast<uint64_t>(ohi) << 32) | olo;
+        const bool t = other > mine;
+        hi = t ? ohi : hi;
+        lo = t ? olo : lo;
     };
-    if constexpr (LPR >= 2) take(dpp<kDppXor1>(k), dpp<kDppXor1>(c));
-    if constexpr (LPR >= 4) take(dpp<kDppXor2>(k), dpp<kDppXor2>(c));
-    if constexpr (LPR >= 8) take(dpp<kDppHalfMirror>(k), dpp<kDppHalfMirror>(c));
-    if constexpr (LPR >= 16) take(dpp<kDppMirror>(k), dpp<kDppMirror>(c));
+    if constexpr (LPR >= 2) take(dpp_u32<kDppXor1>(hi), dpp_u32<kDppXor1>(lo));
+    if constexpr (LPR >= 4) take(dpp_u32<kDppXor2>(hi), dpp_u32<kDppXor2>(lo));
+    if constexpr (LPR >= 8) take(dpp_u32<kDppHalfMirror>(hi), dpp_u32<kDppHalfMirror>(lo));
+    if constexpr (LPR >= 16) take(dpp_u32<kDppMirror>(hi), dpp_u32<kDppMirror>(lo));
     if constexpr (LPR >= 32) {
-        const f32x2 tk = swap_rows16(__int_as_float(k)), tc = swap_rows16(__int_as_float(c));
-        k = __float_as_int(tk[0]);
-        c = __float_as_int(tc[0]);
-        take(__float_as_int(tk[1]), __float_as_int(tc[1]));
+        const f32x2 th = swap_rows16(__uint_as_float(hi)), tl = swap_rows16(__uint_as_float(lo));
+        hi = __float_as_uint(th[0]);
+        lo = __float_as_uint(tl[0]);
+        take(__float_as_uint(th[1]), __float_as_uint(tl[1]));
     }
     if constexpr (LPR >= 64) {
-        const f32x2 tk = swap_rows32(__int_as_float(k)), tc = swap_rows32(__int_as_float(c));
-        k = __float_as_int(tk[0]);
-        c = __float_as_int(tc[0]);
-        take(__float_as_int(tk[1]), __float_as_int(tc[1]));
+        const f32x2 th = swap_rows32(__uint_as_float(hi)), tl = swap_rows32(__uint_as_float(lo));
+        hi = __float_as_uint(th[0]);
+        lo = __float_as_uint(tl[0]);
+        take(__float_as_uint(th[1]), __float_as_uint(tl[1]));
     }
+    k = static_cast<int>(hi ^ 0x80000000u);
+    c = static_cast<int>(~lo);
 }
 
 template <bool BF16, int LPR, int VPL, bool ALIGNED, bool FEWK>
