@@ -114,9 +114,9 @@ int os_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, in
  *   lanes_per_row   lanes that share one row: 4, 8, 16, 32, 64, 128, 256, 512
  *                   or 1024 (register-resident kernels), or 0 for the
  *                   streaming two-pass kernel.
- *   vecs_per_lane   16-byte vectors held per lane (1, 2, 4, 8 or 16, and 5 or 6
- *                   on 512 and 1024 lanes; only the combinations built into the
- *                   library are accepted).  The
+ *   vecs_per_lane   16-byte vectors held per lane (1, 2, 4, 8 or 16, 5 on 256
+ *                   lanes, 5 or 6 on 512 and 1024 lanes; only the combinations
+ *                   built into the library are accepted).  The
  *                   shape must hold the row: lanes_per_row * vecs_per_lane *
  *                   VEC >= cols, VEC = 16 / element size, and >= cols + VEC - 1
  *                   when the row starts are not all 16-byte aligned (such a

@@ -235,7 +235,7 @@ def test_forward_plan(ons):
     assert ons.os_forward_plan(1024) == (128, 2)
     assert ons.os_forward_plan(2048, torch.bfloat16) == (128, 2)
     assert ons.os_forward_plan(4096) == (512, 2)
-    assert ons.os_forward_plan(4097) == (512, 4)   # 1025 slots: half the lanes, twice the vectors
+    assert ons.os_forward_plan(4097) == (256, 5)   # not 16-byte aligned, 1025 slots: 256 lanes of 5 vectors
     assert ons.os_forward_plan(4100) == (512, 4)
     assert ons.os_forward_plan(2052) == (256, 4)
     # every automatic shape holds its row, and a row that is not 16-byte

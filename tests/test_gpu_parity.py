@@ -103,7 +103,7 @@ def test_config1(ons, orc):
 
 SHAPES = [(lanes, vecs) for lanes in (4, 8, 16, 32) for vecs in (1, 2, 4)] + \
     [(lanes, vecs) for lanes in (64, 128, 256, 512, 1024) for vecs in (1, 2, 4, 8)] + \
-    [(512, 5), (512, 6), (1024, 5), (1024, 6), (1024, 16)]
+    [(256, 5), (512, 5), (512, 6), (1024, 5), (1024, 6), (1024, 16)]
 
 
 @pytest.mark.parametrize("lanes,vecs", SHAPES, ids=[f"{a}x{b}" for a, b in SHAPES])
