@@ -693,8 +693,8 @@ int topk_waves(int64_t units, int64_t seg_cols, int K, int dtype) {
 }
 
 // Register-resident top-K shapes for short rows (up to 2048 columns): lanes
-// per row x 16-byte slots per lane, at most 32 entries per lane (fp32 up to 8
-// slots, bf16 up to 4), by capacity.
+// per row x 16-byte slots per lane, 32 entries per lane (fp32 8 slots, bf16 4)
+// or fewer on the shortest rows, by capacity.
 typedef void (*TopkRowsKernel)(const void*, float*, int*, int64_t, int, int);
 struct TopkRowsShape {
     int lpr, vpl;
@@ -715,16 +715,49 @@ const TopkRowsShape kTopkRowsBF16[] = {
     ONORM_TOPK_ROWS(true, 4, 1),  ONORM_TOPK_ROWS(true, 4, 2),  ONORM_TOPK_ROWS(true, 4, 4),
     ONORM_TOPK_ROWS(true, 8, 4),  ONORM_TOPK_ROWS(true, 16, 4), ONORM_TOPK_ROWS(true, 32, 4), ONORM_TOPK_ROWS(true, 64, 4)};
 #undef ONORM_TOPK_ROWS
+// 64 entries per lane (K >= 2 only): half the lanes per row of the shapes
+// above, so each of the K rounds serves twice the rows per wavefront with one
+// butterfly step fewer, at 64 KiB of LDS keys per workgroup (2 waves per SIMD).
+#define ONORM_TOPK_WIDE(B, L, V)                                                     \
+    {                                                                                \
+        L, V, {                                                                      \
+            {k_topk_rows<B, L, V, false, false>, k_topk_rows<B, L, V, true, false>}, \
+            {nullptr, nullptr}                                                       \
+        }                                                                            \
+    }
+// (fp32 rows of <= 256 columns keep 8 lanes: 4 x 16 ran 14% slower at
+// 40000 x 200 for K = 32 and gained 2% at 65536 x 256)
+const TopkRowsShape kTopkWideF32[] = {ONORM_TOPK_WIDE(false, 8, 16), ONORM_TOPK_WIDE(false, 16, 16)};
+const TopkRowsShape kTopkWideBF16[] = {ONORM_TOPK_WIDE(true, 4, 8), ONORM_TOPK_WIDE(true, 8, 8),
+                                       ONORM_TOPK_WIDE(true, 16, 8)};
+#undef ONORM_TOPK_WIDE
 
-// The short-row shape for these rows, or nullptr when they are too long.
-const TopkRowsShape* topk_rows_shape(int64_t cols, int dtype, bool al) {
+// The short-row shape for these rows, or nullptr when they are too long: the
+// fewest lanes per row that hold it (measured best on rows of 128..512
+// columns against 2..16 times the lanes).  Batches with many rounds (K >= 16
+// for bf16, K >= 32 for fp32) take the 64-entry shape when it has fewer lanes
+// and still gives each SIMD two waves (rows x lanes >= 2 x 256 CUs x 256
+// lanes); measured on MI355X over 256..1024 columns and 4096..65536 rows,
+// those cases ran 2..17% faster (16384 x 512 fp32 K = 32: 24.5 us instead of
+// 28.8 us; 65536 x 1024 bf16 K = 32: 155 us instead of 185 us), and with one
+// wave per SIMD (16384 x 256) they ran up to 28% slower.  Through the tiled
+// kernel before this rule, 65536 x 1024 for K = 32 took 242 us (fp32) and
+// 215 us (bf16); now 169 us and 155 us.
+const TopkRowsShape* topk_rows_shape(int64_t rows, int64_t cols, int K, int dtype, bool al) {
     const int64_t need = slots_needed(cols, dtype, al);
-    const TopkRowsShape* t = dtype == OS_BF16 ? kTopkRowsBF16 : kTopkRowsF32;
-    const int n = dtype == OS_BF16 ? sizeof(kTopkRowsBF16) / sizeof(kTopkRowsBF16[0])
-                                   : sizeof(kTopkRowsF32) / sizeof(kTopkRowsF32[0]);
-    for (int i = 0; i < n; ++i)
-        if (static_cast<int64_t>(t[i].lpr) * t[i].vpl >= need) return &t[i];
-    return nullptr;
+    const bool bf = dtype == OS_BF16;
+    const TopkRowsShape* t = bf ? kTopkRowsBF16 : kTopkRowsF32;
+    const int n = bf ? sizeof(kTopkRowsBF16) / sizeof(kTopkRowsBF16[0]) : sizeof(kTopkRowsF32) / sizeof(kTopkRowsF32[0]);
+    const TopkRowsShape* best = nullptr;
+    for (int i = 0; i < n && best == nullptr; ++i)
+        if (static_cast<int64_t>(t[i].lpr) * t[i].vpl >= need) best = &t[i];
+    if (best == nullptr || K < (bf ? 16 : 32)) return best;
+    const TopkRowsShape* w = bf ? kTopkWideBF16 : kTopkWideF32;
+    const int nw = bf ? sizeof(kTopkWideBF16) / sizeof(kTopkWideBF16[0]) : sizeof(kTopkWideF32) / sizeof(kTopkWideF32[0]);
+    for (int i = 0; i < nw; ++i)
+        if (static_cast<int64_t>(w[i].lpr) * w[i].vpl >= need)
+            return w[i].lpr < best->lpr && rows * w[i].lpr >= 2 * 256 * 256 ? &w[i] : best;
+    return best;
 }
 
 // Whether the short-row kernel serves this batch (unsplit rows only).  Each
@@ -736,19 +769,19 @@ const TopkRowsShape* topk_rows_shape(int64_t cols, int dtype, bool al) {
 // < 4096, < 8192, more rows), measured on MI355X against the tiled kernel
 // over 64..65536 rows, K = 1..32, both dtypes: where it is used it was as
 // fast or faster (up to 23x at 65536 rows of 16, 4.6x at 65536 x 256 for
-// K = 8, 1.2-1.6x on rows of 1500-2048 for K <= 2), and where it is not it
-// was slower.
+// K = 8, 1.2-1.6x on rows of 1500-2048 for K <= 2, 1.4x at 65536 x 1024 for
+// K = 32), and where it is not it was slower.
 bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
     static const int kMaxK[7][4] = {
         {32, 32, 32, 32},  // <= 16 columns
         {16, 16, 32, 32},  // <= 64
         {8, 16, 32, 32},   // <= 128
-        {2, 4, 8, 32},     // <= 256
-        {2, 4, 8, 32},     // <= 512
-        {2, 4, 16, 16},    // <= 1024
+        {2, 4, 16, 32},    // <= 256
+        {2, 4, 16, 32},    // <= 512
+        {2, 4, 16, 32},    // <= 1024
         {2, 4, 4, 4},      // <= 2048
     };
-    if (topk_rows_shape(cols, dtype, al) == nullptr || cols > 2048) return false;
+    if (cols > 2048 || topk_rows_shape(rows, cols, K, dtype, al) == nullptr) return false;
     const int cb = cols <= 16    ? 0
                    : cols <= 64  ? 1
                    : cols <= 128 ? 2
@@ -757,6 +790,9 @@ bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
                    : cols <= 1024 ? 5
                                   : 6;
     const int rb = rows < 2048 ? 0 : rows < 4096 ? 1 : rows < 8192 ? 2 : 3;
+    // bf16 rows of <= 256 columns: the tiled kernel's one wave per row took
+    // 29 us at 4096 x 256 for K = 32, this kernel 17 us
+    if (dtype == OS_BF16 && cb == 3 && rb == 2) return K <= 32;
     return K <= kMaxK[cb][rb];
 }
 
@@ -764,7 +800,7 @@ int launch_topk(const char* fn, const void* in, int dtype, float* probs, int32_t
                 int K, int S, void* workspace, void* stream) {
     const bool al = aligned(in, 16) && ((cols * elt_size(dtype)) % 16) == 0;
     if (S == 1 && use_topk_rows(rows, cols, K, dtype, al)) {
-        const TopkRowsShape* sh = topk_rows_shape(cols, dtype, al);
+        const TopkRowsShape* sh = topk_rows_shape(rows, cols, K, dtype, al);
         const int rpb = 256 / sh->lpr;
         (void)hipGetLastError();
         // K = 1 without LDS measured up to 8% faster; for K = 2 the register

@@ -244,11 +244,11 @@ __device__ __forceinline__ void put_stats(const RowStats& o, int64_t row, State 
 // Shapes of at most 4 vectors per lane fit in 64 VGPRs, so 8 waves per SIMD
 // are requested: two 1024-lane (four 512-lane) workgroups then stay resident
 // on a CU, which the register count would otherwise decide by a few
-// registers.  Unaligned bf16 rows on 256 or more lanes of 4 vectors would
-// spill to fit, and are left to the compiler.
-template <bool BF16, int LPR, int VPL, bool ALIGNED>
+// registers.  Unaligned bf16 rows of 4 vectors on 256 or more lanes, or read
+// through LDS (STAGE 2), would spill to fit, and are left to the compiler.
+template <bool BF16, int LPR, int VPL, bool ALIGNED, int STAGE>
 constexpr int resident_min_waves() {
-    return (VPL <= 4 && !(BF16 && !ALIGNED && LPR >= 256 && VPL == 4)) ? 8 : 1;
+    return (VPL <= 4 && !(BF16 && !ALIGNED && VPL == 4 && (LPR >= 256 || STAGE == 2))) ? 8 : 1;
 }
 
 //
@@ -263,7 +263,7 @@ constexpr int resident_min_waves() {
 // only cols / VEC slots, as aligned rows do, and no row pays a partial slot at
 // its front.
 template <bool BF16, int LPR, int VPL, bool ALIGNED, int STAGE>
-__global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF16, LPR, VPL, ALIGNED>()))
+__global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF16, LPR, VPL, ALIGNED, STAGE>()))
     k_resident(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
@@ -1373,7 +1373,7 @@ __global__ void __launch_bounds__(W * 64)
 // Fused softmax + top-K for short rows (paper summary, section 4), the shape
 // of a mixture-of-experts router: many rows of up to 2048 entries.  LPR <= 64
 // lanes share a row and hold it in registers (VPL 16-byte slots each, at most
-// 32 entries per lane), several rows per wavefront, no barriers; the row is
+// 64 entries per lane), several rows per wavefront, no barriers; the row is
 // read once.
 //   - State: the row maximum M and d = sum e^{x - M} by reductions over the
 //     row's lanes.
@@ -1387,10 +1387,11 @@ __global__ void __launch_bounds__(W * 64)
 //     the row's lanes finds the row's best, written by the row's first lane
 //     (probability e^{u - M} / d over the whole row, and the index).  The
 //     lane that held it retires it and finds its next best.  With more than
-//     8 entries per lane they sit in 4 groups with a best per group, and the
-//     keys also live in LDS (each lane only touches its own words, so no
-//     barrier): retiring an entry is one store and refreshing its group reads
-//     a quarter of the keys instead of rescanning all of them.  FEWK (K = 1:
+//     8 entries per lane they sit in groups of at most 8 (4 groups up to 32
+//     entries, 8 groups of 8 for 64) with a best per group, and the keys also
+//     live in LDS (each lane only touches its own words, so no barrier):
+//     retiring an entry is one store and refreshing its group reads that
+//     group's keys instead of rescanning all of them.  FEWK (K = 1:
 //     nothing is ever retired) keeps the keys in registers and needs no LDS,
 //     which leaves room for more workgroups per CU.
 // ---------------------------------------------------------------------------
@@ -1452,10 +1453,11 @@ __global__ void __launch_bounds__(256)
     constexpr int RPB = 256 / LPR;
     constexpr int N = VPL * VEC;                // entries per lane
     constexpr bool kLds = (N > 8) & !FEWK;      // keys in LDS, in groups
-    constexpr int NG = kLds ? 4 : 1;            // groups per lane
+    constexpr int NG = kLds ? (N > 32 ? 8 : 4) : 1;  // groups per lane
     constexpr int G = N / NG;                   // entries per group
     constexpr int NQ = kLds ? N / 4 : 1;        // 4-key LDS words per lane
-    static_assert(LPR >= 4 && LPR <= 64 && N <= 32, "one row within a wavefront, at most 32 entries per lane");
+    static_assert(LPR >= 4 && LPR <= 64 && N <= 64, "one row within a wavefront, at most 64 entries per lane");
+    static_assert(N <= 32 || !FEWK, "64 entries per lane only with the keys in LDS");
     static_assert(!kLds || G % 4 == 0, "groups of whole 4-key words");
     // lane t's keys 4q..4q+3 at s_keys[q][t]: each lane reads and writes only
     // its own words, with consecutive lanes on consecutive 16 bytes
