@@ -262,8 +262,12 @@ constexpr int resident_min_waves() {
 // row's first element (slot vi holds entries vi * VEC ..), so such rows need
 // only cols / VEC slots, as aligned rows do, and no row pays a partial slot at
 // its front.
-template <bool BF16, int LPR, int VPL, bool ALIGNED, int STAGE>
-__global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR, (resident_min_waves<BF16, LPR, VPL, ALIGNED, STAGE>()))
+//
+// MINW > 0 replaces the waves-per-SIMD request (the same code on a tighter
+// register budget, so the same results bit for bit).
+template <bool BF16, int LPR, int VPL, bool ALIGNED, int STAGE, int MINW = 0>
+__global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR,
+                                  (MINW > 0 ? MINW : resident_min_waves<BF16, LPR, VPL, ALIGNED, STAGE>()))
     k_resident(const void* in, void* out, RowStats st, int64_t rows, int cols, uint32_t gmask) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;

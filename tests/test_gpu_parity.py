@@ -148,6 +148,20 @@ def test_auto_dispatch_edge_columns(ons, orc, bf16):
         assert_parity(run_forward(ons, x, safe=True), ref, bf16, f"safe cols={cols}")
 
 
+@pytest.mark.parametrize("cols,rows", [(32000, 1024), (8000, 2048)], ids=["1024x8", "512x8"])
+def test_dense_small_batches(ons, orc, cols, rows):
+    """fp32 rows on 8-vector shapes: batches of up to two rounds of
+    workgroups take the kernel held to 64 VGPRs, one row more takes the
+    default one; the two must agree bit for bit, and with the oracle."""
+    say(f"dense fp32 rows={rows}/{rows + 1} cols={cols}")
+    x = workloads.normal(rows + 1, cols, seed=cols + rows, scale=2.0)
+    y_big = run_forward(ons, x)
+    y_small = run_forward(ons, x[:rows])
+    assert np.array_equal(y_small.view(np.uint32), y_big[:rows].view(np.uint32)), "dense and default kernels differ"
+    pick = np.r_[0:4, rows // 2, rows - 3:rows + 1]
+    assert_parity(y_big[pick], orc.softmax(x[pick]), False, f"dense cols={cols}")
+
+
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_streaming_two_pass(ons, orc, bf16):
     for rows, cols in [(3, 1), (5, 100), (7, 4096), (9, 32000), (3, 200001), (2, 1 << 20)]:
