@@ -133,6 +133,7 @@ constexpr RowKernel staged_kernel() {
     }
 // fp32 only: 16 vectors of bf16 are 128 fp32 values per lane, more than a
 // 1024-thread workgroup's 128-VGPR budget, so bf16 rows this long stream.
+// No three-pass form: the baseline streams rows this long.
 #define ONORM_RESIDENT_F32(L, V)                                                     \
     {                                                                                \
         L, V,                                                                        \
@@ -141,7 +142,7 @@ constexpr RowKernel staged_kernel() {
                 {nullptr, nullptr},                                                  \
             },                                                                       \
         {                                                                            \
-            {k_safe3_rows<false, L, V, false>, k_safe3_rows<false, L, V, true>},     \
+            {nullptr, nullptr},                                                      \
                 {nullptr, nullptr},                                                  \
         },                                                                           \
         {nullptr, nullptr},                                                          \
@@ -396,10 +397,12 @@ RowKernel hybrid_kernel(int64_t cols, int dtype, bool al) {
     // fp32: the register part grows with the row (measured best: 8 vectors
     // per lane up to 65536 columns, all of it on chip with the LDS copy; 12 up
     // to 110000; 16 beyond, where 12 and 16 measured within 1% on 128256 and
-    // 16 re-reads less)
+    // 16 re-reads less).  Unaligned rows keep 12 beyond 110000: their 16-vector
+    // form spills 2 VGPRs, and 12 measured 0.4-3.7% faster on 5 of 6 lengths
+    // from 110001 to 262143 columns (2.8% slower at 400 x 150001).
     if (cols <= 65536) return al ? k_hybrid<false, 8, 2, true, 4> : k_hybrid<false, 8, 2, false, 4>;
-    if (cols <= 110000) return al ? k_hybrid<false, 12, 2, true, 4> : k_hybrid<false, 12, 2, false, 4>;
-    return al ? k_hybrid<false, 16, 2, true, 4> : k_hybrid<false, 16, 2, false, 4>;
+    if (cols <= 110000 || !al) return al ? k_hybrid<false, 12, 2, true, 4> : k_hybrid<false, 12, 2, false, 4>;
+    return k_hybrid<false, 16, 2, true, 4>;
 }
 
 int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t rows, int64_t cols, int dtype,

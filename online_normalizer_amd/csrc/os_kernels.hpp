@@ -745,9 +745,8 @@ __global__ void __launch_bounds__(W * 64)
 // lanes per row and VPL vectors per lane exactly as k_resident, but every
 // pass reloads the row's slots instead of keeping them in registers.  Pass 1
 // and 2 use plain loads, so re-reads of short rows can hit in cache, which is
-// the regime the pages' benchmark describes for short vectors.  With more than
-// 8 vectors per lane each pass moves them in steps of 4 (all 16 at once would
-// not fit the registers without spilling).
+// the regime the pages' benchmark describes for short vectors.  Shapes of at
+// most 8 vectors per lane; longer rows take the streaming baseline.
 // ---------------------------------------------------------------------------
 template <bool BF16, int LPR, int VPL, bool ALIGNED>
 __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
@@ -776,27 +775,16 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         const Buf bin(si.base, si.bytes);
         const RowAt ri = rows_row<BF16, ALIGNED, (LPR <= 64)>(si.lead + static_cast<uint32_t>(g) * row_bytes, gmask);
         const int nvec = slot_count<BF16>(cols, ri.ph);
-        constexpr int CH = VPL <= 8 ? VPL : 4;  // vectors per lane per step
-        static_assert(VPL % CH == 0, "whole steps");
-        float x[CH][VEC];
+        static_assert(VPL <= 8, "the baseline streams rows past 8 vectors per lane");
+        float x[VPL][VEC];
 
         // pass 1: maximum
         float m = kFloor;
-        if constexpr (CH == VPL) {
-            load_slots<BF16, VPL, ALIGNED, false>(bin, ri, j, LPR, nvec, cols, live, x);
+        load_slots<BF16, VPL, ALIGNED, false>(bin, ri, j, LPR, nvec, cols, live, x);
 #pragma unroll
-            for (int v = 0; v < VPL; ++v)
+        for (int v = 0; v < VPL; ++v)
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[v][k]);
-        } else {
-            for (int c = 0; c < VPL / CH; ++c) {
-                load_slots<BF16, CH, ALIGNED, false>(bin, ri, j + c * CH * LPR, LPR, nvec, cols, live, x);
-#pragma unroll
-                for (int v = 0; v < CH; ++v)
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[v][k]);
-            }
-        }
+            for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[v][k]);
         m = group_max<GROUP>(m);
         if constexpr (W > 1) {
             if ((tid & (kWave - 1)) == 0) lds_m[par][tid / kWave] = m;
@@ -807,21 +795,11 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         }
         // pass 2: sum of e^{x - m}
         float d = 0.0f;
-        if constexpr (CH == VPL) {
-            load_slots<BF16, VPL, ALIGNED, false>(bin, ri, j, LPR, nvec, cols, live, x);
+        load_slots<BF16, VPL, ALIGNED, false>(bin, ri, j, LPR, nvec, cols, live, x);
 #pragma unroll
-            for (int v = 0; v < VPL; ++v)
+        for (int v = 0; v < VPL; ++v)
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) d += exp_e(x[v][k] - m);
-        } else {
-            for (int c = 0; c < VPL / CH; ++c) {
-                load_slots<BF16, CH, ALIGNED, false>(bin, ri, j + c * CH * LPR, LPR, nvec, cols, live, x);
-#pragma unroll
-                for (int v = 0; v < CH; ++v)
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) d += exp_e(x[v][k] - m);
-            }
-        }
+            for (int k = 0; k < VEC; ++k) d += exp_e(x[v][k] - m);
         d = group_sum<GROUP>(d);
         if constexpr (W > 1) {
             if ((tid & (kWave - 1)) == 0) lds_d[par][tid / kWave] = d;
@@ -836,25 +814,12 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         const Span so = rows_span<BF16, ALIGNED, (LPR <= 64)>(out, row0 * cols, nrows * cols, gmask);
         const Buf bout(so.base, so.bytes);
         const RowAt ro = rows_row<BF16, ALIGNED, (LPR <= 64)>(so.lead + static_cast<uint32_t>(g) * row_bytes, gmask);
-        if constexpr (CH == VPL) {
-            load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, nvec, cols, live, x);
+        load_slots<BF16, VPL, ALIGNED, true>(bin, ri, j, LPR, nvec, cols, live, x);
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) {
+        for (int v = 0; v < VPL; ++v) {
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) x[v][k] = exp_e(x[v][k] - m) * inv_d;
-                store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, nvec, cols, live, x[v], v == 0);
-            }
-        } else {
-            for (int c = 0; c < VPL / CH; ++c) {
-                load_slots<BF16, CH, ALIGNED, true>(bin, ri, j + c * CH * LPR, LPR, nvec, cols, live, x);
-#pragma unroll
-                for (int v = 0; v < CH; ++v) {
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) x[v][k] = exp_e(x[v][k] - m) * inv_d;
-                    store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, (c * CH + v) * LPR + j, nvec, cols, live, x[v],
-                                              (c == 0) & (v == 0));
-                }
-            }
+            for (int k = 0; k < VEC; ++k) x[v][k] = exp_e(x[v][k] - m) * inv_d;
+            store_slot<BF16, ALIGNED>(bout, ro, ri.ph, same, v * LPR + j, nvec, cols, live, x[v], v == 0);
         }
     }
 }
