@@ -725,12 +725,22 @@ struct TopkRowsShape {
     int lpr, vpl;
     TopkRowsKernel fn[2][2];  // [K == 1][aligned]
 };
-#define ONORM_TOPK_ROWS(B, L, V)                                                   \
-    {                                                                              \
-        L, V, {                                                                    \
-            {k_topk_rows<B, L, V, false, false>, k_topk_rows<B, L, V, true, false>}, \
-            {k_topk_rows<B, L, V, false, true>, k_topk_rows<B, L, V, true, true>}    \
-        }                                                                          \
+// bf16 rows select on packed (key, column) entries (k_topk_rows_bf16) for
+// K >= 2: 5-74% faster than k_topk_rows on 65536 x 16 .. 4096 x 2048 at
+// K = 2..32 (16384 x 512 K = 32: 14.5 us instead of 23.7; 65536 x 1024 K = 16:
+// 68.5 us instead of 94.6).  At K = 1 it measured -3.6% to +1.3% (its
+// register form holds more VGPRs), so K = 1 keeps k_topk_rows.
+template <bool B, int L, int V, bool AL, bool FEWK>
+constexpr TopkRowsKernel topk_rows_fn() {
+    if constexpr (B && !FEWK) return k_topk_rows_bf16<L, V, AL, false>;
+    else return k_topk_rows<B, L, V, AL, FEWK>;
+}
+#define ONORM_TOPK_ROWS(B, L, V)                                                                       \
+    {                                                                                                  \
+        L, V, {                                                                                        \
+            {topk_rows_fn<B, L, V, false, false>(), topk_rows_fn<B, L, V, true, false>()},             \
+            {topk_rows_fn<B, L, V, false, true>(), topk_rows_fn<B, L, V, true, true>()}                \
+        }                                                                                              \
     }
 const TopkRowsShape kTopkRowsF32[] = {
     ONORM_TOPK_ROWS(false, 4, 1),  ONORM_TOPK_ROWS(false, 4, 2),  ONORM_TOPK_ROWS(false, 4, 4),
@@ -746,7 +756,7 @@ const TopkRowsShape kTopkRowsBF16[] = {
 #define ONORM_TOPK_WIDE(B, L, V)                                                     \
     {                                                                                \
         L, V, {                                                                      \
-            {k_topk_rows<B, L, V, false, false>, k_topk_rows<B, L, V, true, false>}, \
+            {topk_rows_fn<B, L, V, false, false>(), topk_rows_fn<B, L, V, true, false>()}, \
             {nullptr, nullptr}                                                       \
         }                                                                            \
     }
@@ -796,7 +806,22 @@ const TopkRowsShape* topk_rows_shape(int64_t rows, int64_t cols, int K, int dtyp
 // fast or faster (up to 23x at 65536 rows of 16, 4.6x at 65536 x 256 for
 // K = 8, 1.2-1.6x on rows of 1500-2048 for K <= 2, 1.4x at 65536 x 1024 for
 // K = 32), and where it is not it was slower.
+// bf16 rows select on packed entries, which made each round about half as
+// costly; the same comparison then favoured this kernel far more often (e.g.
+// 3000 x 256 at K = 8: 4.8 us against 8.5; 65536 x 1024 at K = 32: 101 us
+// against 215), and the tiled kernel kept only small batches of long rows at
+// large K (64 x 1024 at K = 32: 8.0 us against 10.6) and K = 32 on rows of
+// 1025-2048 columns.
 bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
+    static const int kMaxKBF16[7][4] = {
+        {32, 32, 32, 32},  // <= 16 columns
+        {32, 32, 32, 32},  // <= 64
+        {32, 32, 32, 32},  // <= 128
+        {32, 32, 32, 32},  // <= 256
+        {16, 32, 32, 32},  // <= 512
+        {8, 32, 32, 32},   // <= 1024
+        {4, 32, 16, 16},   // <= 2048
+    };
     static const int kMaxK[7][4] = {
         {32, 32, 32, 32},  // <= 16 columns
         {16, 16, 32, 32},  // <= 64
@@ -815,10 +840,7 @@ bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
                    : cols <= 1024 ? 5
                                   : 6;
     const int rb = rows < 2048 ? 0 : rows < 4096 ? 1 : rows < 8192 ? 2 : 3;
-    // bf16 rows of <= 256 columns: the tiled kernel's one wave per row took
-    // 29 us at 4096 x 256 for K = 32, this kernel 17 us
-    if (dtype == OS_BF16 && cb == 3 && rb == 2) return K <= 32;
-    return K <= kMaxK[cb][rb];
+    return K <= (dtype == OS_BF16 ? kMaxKBF16[cb][rb] : kMaxK[cb][rb]);
 }
 
 int launch_topk(const char* fn, const void* in, int dtype, float* probs, int32_t* idx, int64_t rows, int64_t cols,

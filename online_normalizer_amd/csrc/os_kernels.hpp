@@ -1567,6 +1567,169 @@ __global__ void __launch_bounds__(256)
     }
 }
 
+// bf16 rows: a bf16 value's order key fits in 16 bits, so an entry packs its
+// key and its column into one int, (key << 16) | (0xFFFF - column).  The
+// integer order is then the selection order (larger value first, then lower
+// column), every compare of the selection is one integer max, and the column
+// comes back with the winner.  Columns stay below 2048 here.
+constexpr int kPackedRetired = INT_MIN;  // outside the row, or already output
+
+__device__ __forceinline__ int packed_entry(float x, int col) {
+    // the 32-bit key of a widened bf16 value carries the 16-bit key in its top
+    // half; the all-ones NaN pattern would land on the retired value's key
+    const int k16 = max(order_key(x) >> 16, -32767);
+    return static_cast<int>((static_cast<uint32_t>(k16) << 16) | static_cast<uint32_t>(0xFFFF - col));
+}
+
+__device__ __forceinline__ float packed_value(int p) {
+    const int k16 = p >> 16;
+    return __int_as_float(static_cast<int>(static_cast<uint32_t>(k16 ^ ((k16 >> 31) & 0x7FFF)) << 16));
+}
+
+__device__ __forceinline__ int packed_column(int p) { return 0xFFFF - (p & 0xFFFF); }
+
+// Integer maximum over an aligned group of G lanes, same value in every lane.
+template <int G>
+__device__ __forceinline__ int group_max_i32(int v) {
+    if constexpr (G >= 2) v = max(v, dpp<kDppXor1>(v));
+    if constexpr (G >= 4) v = max(v, dpp<kDppXor2>(v));
+    if constexpr (G >= 8) v = max(v, dpp<kDppHalfMirror>(v));
+    if constexpr (G >= 16) v = max(v, dpp<kDppMirror>(v));
+    if constexpr (G >= 32) {
+        const f32x2 t = swap_rows16(__int_as_float(v));
+        v = max(__float_as_int(t[0]), __float_as_int(t[1]));
+    }
+    if constexpr (G >= 64) {
+        const f32x2 t = swap_rows32(__int_as_float(v));
+        v = max(__float_as_int(t[0]), __float_as_int(t[1]));
+    }
+    return v;
+}
+
+// k_topk_rows for bf16 rows on packed entries: the same state, rounds, groups
+// and LDS layout, with the lane's best a plain maximum and the lane holding
+// the row's winner the one whose best equals it (columns are unique).
+template <int LPR, int VPL, bool ALIGNED, bool FEWK>
+__global__ void __launch_bounds__(256)
+    k_topk_rows_bf16(const void* in, float* probs, int* idx, int64_t rows, int cols, int K) {
+    using E = Elt<true>;
+    constexpr int VEC = E::kVec;
+    constexpr int RPB = 256 / LPR;
+    constexpr int N = VPL * VEC;                     // entries per lane
+    constexpr bool kLds = (N > 8) & !FEWK;           // entries in LDS, in groups
+    constexpr int NG = kLds ? (N > 32 ? 8 : 4) : 1;  // groups per lane
+    constexpr int G = N / NG;                        // entries per group
+    constexpr int NQ = kLds ? N / 4 : 1;             // 4-entry LDS words per lane
+    constexpr int LGL = LPR == 4 ? 2 : LPR == 8 ? 3 : LPR == 16 ? 4 : LPR == 32 ? 5 : 6;
+    static_assert(LPR >= 4 && LPR <= 64 && N <= 64, "one row within a wavefront, at most 64 entries per lane");
+    static_assert(N <= 32 || !FEWK, "64 entries per lane only with the entries in LDS");
+    static_assert(!kLds || G % 4 == 0, "groups of whole 4-entry words");
+    __shared__ int4 s_keys[NQ][kLds ? 256 : 1];
+
+    const int tid = threadIdx.x;
+    const int j = tid % LPR;
+    const int g = tid / LPR;
+    const uint32_t row_bytes = static_cast<uint32_t>(cols) * E::kSize;
+
+    for (int64_t rb = blockIdx.x; rb * RPB < rows; rb += gridDim.x) {
+        const int64_t row0 = rb * RPB;
+        const int64_t nrows = (rows - row0) < RPB ? (rows - row0) : RPB;
+        const int64_t row = row0 + g;
+        const bool live = g < nrows;
+        const Span si = rows_span<true, ALIGNED, true>(in, row0 * cols, nrows * cols, kGrid16);
+        const Buf bin(si.base, si.bytes);
+        const RowAt ri = rows_row<true, ALIGNED, true>(si.lead + static_cast<uint32_t>(g) * row_bytes, kGrid16);
+        const int ns = slot_count<true>(cols, ri.ph);
+
+        float x[VPL][VEC];
+        load_slots<true, VPL, ALIGNED, true>(bin, ri, j, LPR, ns, cols, live, x);
+
+        float ml = kFloor;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) ml = fmaxf(ml, x[v][k]);
+        const float M = group_max<LPR>(ml);
+        float dl = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) dl += exp_e(x[v][k] - M);
+        const float inv_d = rcp(group_sum<LPR>(dl));
+
+        // entry e = v * VEC + k of this lane is column (v * LPR + j) * VEC + k - ph
+        int key[N];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e0 = (v * LPR + j) * VEC - ri.ph;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const bool in_row = live & ((v * LPR + j) < ns) &
+                                    (ALIGNED | (static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols)));
+                key[v * VEC + k] = in_row ? packed_entry(x[v][k], e0 + k) : kPackedRetired;
+            }
+        }
+        int gk[NG];
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            int b = key[q * G];
+#pragma unroll
+            for (int u = 1; u < G; ++u) b = max(b, key[q * G + u]);
+            gk[q] = b;
+        }
+        auto best_of_groups = [&]() {
+            int b = gk[0];
+#pragma unroll
+            for (int q = 1; q < NG; ++q) b = max(b, gk[q]);
+            return b;
+        };
+        int bk = best_of_groups();
+        if constexpr (kLds) {
+            if (K > 1) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    s_keys[q][tid] = int4{key[4 * q], key[4 * q + 1], key[4 * q + 2], key[4 * q + 3]};
+            }
+        }
+
+        for (int r = 0; r < K; ++r) {
+            const int w = group_max_i32<LPR>(bk);
+            if (live & (j == 0)) {
+                probs[row * K + r] = exp_e(packed_value(w) - M) * inv_d;
+                idx[row * K + r] = packed_column(w);
+            }
+            if ((r + 1 < K) & (bk == w) & (w != kPackedRetired)) {
+                // this lane held the row's winner: retire it and refresh its group
+                const int c = packed_column(w) + ri.ph;  // (v * LPR + j) * VEC + k
+                const int e = ((c / VEC) >> LGL) * VEC + (c & (VEC - 1));
+                if constexpr (kLds) {
+                    const int q = e / G;
+                    // the store comes first: one lane's LDS accesses complete
+                    // in order, so the group read below sees it
+                    reinterpret_cast<int*>(&s_keys[e >> 2][tid])[e & 3] = kPackedRetired;
+                    int nk = kPackedRetired;
+#pragma unroll
+                    for (int u = 0; u < G / 4; ++u) {
+                        const int4 kk = s_keys[q * (G / 4) + u][tid];
+                        nk = max(max(nk, kk.x), max(kk.y, max(kk.z, kk.w)));
+                    }
+#pragma unroll
+                    for (int p = 0; p < NG; ++p) gk[p] = p == q ? nk : gk[p];
+                } else {
+                    int b = kPackedRetired;
+#pragma unroll
+                    for (int u = 0; u < N; ++u) {
+                        key[u] = u == e ? kPackedRetired : key[u];
+                        b = max(b, key[u]);
+                    }
+                    gk[0] = b;
+                }
+                bk = best_of_groups();
+            }
+        }
+    }
+}
+
 // Second launch of the split top-K: one wavefront per row folds the S slice
 // states with (+) in slice order and merges the S sorted lists (bitonic, as
 // above), then writes the K probabilities and indices.
