@@ -1374,44 +1374,51 @@ __device__ __forceinline__ int order_key(float x) {
 
 __device__ __forceinline__ float key_value(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return static_cast<uint32_t>(dpp<CTRL>(static_cast<int>(v)));
+// Integer maximum over an aligned group of G lanes, same value in every lane.
+template <int G>
+__device__ __forceinline__ int group_max_i32(int v) {
+    if constexpr (G >= 2) v = max(v, dpp<kDppXor1>(v));
+    if constexpr (G >= 4) v = max(v, dpp<kDppXor2>(v));
+    if constexpr (G >= 8) v = max(v, dpp<kDppHalfMirror>(v));
+    if constexpr (G >= 16) v = max(v, dpp<kDppMirror>(v));
+    if constexpr (G >= 32) {
+        const f32x2 t = swap_rows16(__int_as_float(v));
+        v = max(__float_as_int(t[0]), __float_as_int(t[1]));
+    }
+    if constexpr (G >= 64) {
+        const f32x2 t = swap_rows32(__int_as_float(v));
+        v = max(__float_as_int(t[0]), __float_as_int(t[1]));
+    }
+    return v;
+}
+
+// Integer minimum over an aligned group of G lanes, same value in every lane.
+template <int G>
+__device__ __forceinline__ int group_min_i32(int v) {
+    if constexpr (G >= 2) v = min(v, dpp<kDppXor1>(v));
+    if constexpr (G >= 4) v = min(v, dpp<kDppXor2>(v));
+    if constexpr (G >= 8) v = min(v, dpp<kDppHalfMirror>(v));
+    if constexpr (G >= 16) v = min(v, dpp<kDppMirror>(v));
+    if constexpr (G >= 32) {
+        const f32x2 t = swap_rows16(__int_as_float(v));
+        v = min(__float_as_int(t[0]), __float_as_int(t[1]));
+    }
+    if constexpr (G >= 64) {
+        const f32x2 t = swap_rows32(__int_as_float(v));
+        v = min(__float_as_int(t[0]), __float_as_int(t[1]));
+    }
+    return v;
 }
 
 // Every lane of each aligned group of LPR lanes ends with the group's best
-// (key, column): larger key first, then lower column.  The pair is compared
-// as one unsigned 64-bit number, (key + 2^31) above (2^32 - 1 - column), so a
-// step is two DPP moves, one 64-bit compare and two selects.
+// (key, column): the largest key, then the lowest column among the lanes
+// offering it.  Two integer reductions (a maximum, then a minimum), each step
+// one DPP operand and one max or min.
 template <int LPR>
 __device__ __forceinline__ void group_best_key(int& k, int& c) {
-    uint32_t hi = static_cast<uint32_t>(k) ^ 0x80000000u;
-    uint32_t lo = ~static_cast<uint32_t>(c);
-    auto take = [&](uint32_t ohi, uint32_t olo) {
-        const uint64_t mine = (static_cast<uint64_t>(hi) << 32) | lo;
-        const uint64_t other = (static_cast<uint64_t>(ohi) << 32) | olo;
-        const bool t = other > mine;
-        hi = t ? ohi : hi;
-        lo = t ? olo : lo;
-    };
-    if constexpr (LPR >= 2) take(dpp_u32<kDppXor1>(hi), dpp_u32<kDppXor1>(lo));
-    if constexpr (LPR >= 4) take(dpp_u32<kDppXor2>(hi), dpp_u32<kDppXor2>(lo));
-    if constexpr (LPR >= 8) take(dpp_u32<kDppHalfMirror>(hi), dpp_u32<kDppHalfMirror>(lo));
-    if constexpr (LPR >= 16) take(dpp_u32<kDppMirror>(hi), dpp_u32<kDppMirror>(lo));
-    if constexpr (LPR >= 32) {
-        const f32x2 th = swap_rows16(__uint_as_float(hi)), tl = swap_rows16(__uint_as_float(lo));
-        hi = __float_as_uint(th[0]);
-        lo = __float_as_uint(tl[0]);
-        take(__float_as_uint(th[1]), __float_as_uint(tl[1]));
-    }
-    if constexpr (LPR >= 64) {
-        const f32x2 th = swap_rows32(__uint_as_float(hi)), tl = swap_rows32(__uint_as_float(lo));
-        hi = __float_as_uint(th[0]);
-        lo = __float_as_uint(tl[0]);
-        take(__float_as_uint(th[1]), __float_as_uint(tl[1]));
-    }
-    k = static_cast<int>(hi ^ 0x80000000u);
-    c = static_cast<int>(~lo);
+    const int m = group_max_i32<LPR>(k);
+    c = group_min_i32<LPR>(k == m ? c : INT_MAX);
+    k = m;
 }
 
 template <bool BF16, int LPR, int VPL, bool ALIGNED, bool FEWK>
@@ -1587,24 +1594,6 @@ __device__ __forceinline__ float packed_value(int p) {
 }
 
 __device__ __forceinline__ int packed_column(int p) { return 0xFFFF - (p & 0xFFFF); }
-
-// Integer maximum over an aligned group of G lanes, same value in every lane.
-template <int G>
-__device__ __forceinline__ int group_max_i32(int v) {
-    if constexpr (G >= 2) v = max(v, dpp<kDppXor1>(v));
-    if constexpr (G >= 4) v = max(v, dpp<kDppXor2>(v));
-    if constexpr (G >= 8) v = max(v, dpp<kDppHalfMirror>(v));
-    if constexpr (G >= 16) v = max(v, dpp<kDppMirror>(v));
-    if constexpr (G >= 32) {
-        const f32x2 t = swap_rows16(__int_as_float(v));
-        v = max(__float_as_int(t[0]), __float_as_int(t[1]));
-    }
-    if constexpr (G >= 64) {
-        const f32x2 t = swap_rows32(__int_as_float(v));
-        v = max(__float_as_int(t[0]), __float_as_int(t[1]));
-    }
-    return v;
-}
 
 // k_topk_rows for bf16 rows on packed entries: the same state, rounds, groups
 // and LDS layout, with the lane's best a plain maximum and the lane holding
