@@ -769,13 +769,14 @@ const TopkRowsShape kTopkWideBF16[] = {ONORM_TOPK_WIDE(true, 4, 8), ONORM_TOPK_W
 
 // The short-row shape for these rows, or nullptr when they are too long: the
 // fewest lanes per row that hold it (measured best on rows of 128..512
-// columns against 2..16 times the lanes).  Batches with many rounds (K >= 16
-// for bf16, K >= 32 for fp32) take the 64-entry shape when it has fewer lanes
-// and still gives each SIMD two waves (rows x lanes >= 2 x 256 CUs x 256
-// lanes); measured on MI355X over 256..1024 columns and 4096..65536 rows,
-// those cases ran 2..17% faster (16384 x 512 fp32 K = 32: 24.5 us instead of
-// 28.8 us; 65536 x 1024 bf16 K = 32: 155 us instead of 185 us), and with one
-// wave per SIMD (16384 x 256) they ran up to 28% slower.  Through the tiled
+// columns against 2..16 times the lanes).  Batches with many rounds (K >= 32)
+// take the 64-entry shape when it has fewer lanes and still gives each SIMD
+// two waves (rows x lanes >= 2 x 256 CUs x 256 lanes); measured on MI355X over
+// 256..1024 columns and 4096..65536 rows, those cases ran 2..20% faster
+// (16384 x 512 fp32 K = 32: 24.5 us instead of 28.8 us; bf16 on packed
+// entries 14.3 us instead of 17.1 us), and with one wave per SIMD
+// (16384 x 256) they ran up to 28% slower.  At K = 16 bf16 rows on packed
+// entries measured -7% to +12%, so both dtypes start at K = 32.  Through the tiled
 // kernel before this rule, 65536 x 1024 for K = 32 took 242 us (fp32) and
 // 215 us (bf16); now 169 us and 155 us.
 const TopkRowsShape* topk_rows_shape(int64_t rows, int64_t cols, int K, int dtype, bool al) {
@@ -786,7 +787,7 @@ const TopkRowsShape* topk_rows_shape(int64_t rows, int64_t cols, int K, int dtyp
     const TopkRowsShape* best = nullptr;
     for (int i = 0; i < n && best == nullptr; ++i)
         if (static_cast<int64_t>(t[i].lpr) * t[i].vpl >= need) best = &t[i];
-    if (best == nullptr || K < (bf ? 16 : 32)) return best;
+    if (best == nullptr || K < 32) return best;
     const TopkRowsShape* w = bf ? kTopkWideBF16 : kTopkWideF32;
     const int nw = bf ? sizeof(kTopkWideBF16) / sizeof(kTopkWideBF16[0]) : sizeof(kTopkWideF32) / sizeof(kTopkWideF32[0]);
     for (int i = 0; i < nw; ++i)
