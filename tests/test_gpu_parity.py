@@ -385,8 +385,9 @@ def test_deterministic(ons):
 def test_graph_replays_match_eager(ons):
     """The forward (aligned rows, unaligned rows with direct, LDS-assembled
     and LDS-read stores, and long rows with their LDS copy), the baseline, the
-    top-K (tiled, short-row, and split over two launches) and the split
-    forward captured in a HIP graph: every replay, with eager work and
+    top-K (tiled, short-row on 32 and 64 entries per lane, bf16 short-row on
+    packed entries, and split over two launches) and the split forward
+    captured in a HIP graph: every replay, with eager work and
     synchronisations between replays, equals the eager result bit for bit."""
     x = to_device(workloads.config(2, 0, 512))
     xt = to_device(workloads.config(5, 0, 8))
@@ -403,6 +404,10 @@ def test_graph_replays_match_eager(ons):
     pk_ref, ik_ref = ons.os_softmax_topk_ex(xk, 8, 4, wk)
     xw = to_device(workloads.normal(4200, 512, seed=11, scale=3.0))
     pw_ref, iw_ref = ons.os_softmax_topk_ex(xw, 8, 1, None)
+    xb = to_device(bf16_bits(workloads.normal(4200, 512, seed=15, scale=3.0)))    # bf16, packed entries
+    pb_ref, ib_ref = ons.os_softmax_topk_ex(xb, 8, 1, None)
+    xv = to_device(workloads.normal(16384, 512, seed=16, scale=3.0))              # 64 entries per lane
+    pv_ref, iv_ref = ons.os_softmax_topk_ex(xv, 32, 1, None)
     xu = to_device(workloads.normal(64, 50257, seed=12, scale=3.0))
     yu_ref = ons.os_softmax_forward(xu)
     x1 = to_device(workloads.normal(5000, 127, seed=13, scale=3.0))   # read through LDS
@@ -422,12 +427,14 @@ def test_graph_replays_match_eager(ons):
         ons.os_softmax_forward_split(xs, splits=8, out=sp, workspace=ws)
         pk, ik = ons.os_softmax_topk_ex(xk, 8, 4, wk)
         pw, iw = ons.os_softmax_topk_ex(xw, 8, 1, None)
+        pb, ib = ons.os_softmax_topk_ex(xb, 8, 1, None)
+        pv, iv = ons.os_softmax_topk_ex(xv, 32, 1, None)
         ons.os_softmax_forward(xu, out=yu)
         ons.os_softmax_forward(x1, out=y1)
         ons.os_softmax_forward(x2, out=y2)
         ons.os_softmax_forward(xk, out=yk)
     for rep in range(4):
-        for t in (y, s3, p, i, sp, pk, ik, pw, iw, yu, y1, y2, yk):
+        for t in (y, s3, p, i, sp, pk, ik, pw, iw, pb, ib, pv, iv, yu, y1, y2, yk):
             t.zero_()
         junk = ons.os_softmax_forward(torch.randn(64, 1000, device="cuda"))  # eager work between replays
         torch.cuda.synchronize()
@@ -440,6 +447,8 @@ def test_graph_replays_match_eager(ons):
         assert torch.equal(sp.view(torch.int32), sp_ref.view(torch.int32)), rep
         assert torch.equal(pk, pk_ref) and torch.equal(ik, ik_ref), rep
         assert torch.equal(pw, pw_ref) and torch.equal(iw, iw_ref), rep
+        assert torch.equal(pb, pb_ref) and torch.equal(ib, ib_ref), rep
+        assert torch.equal(pv, pv_ref) and torch.equal(iv, iv_ref), rep
         assert torch.equal(yu.view(torch.int32), yu_ref.view(torch.int32)), rep
         for got, want in ((y1, y1_ref), (y2, y2_ref), (yk, yk_ref)):
             assert torch.equal(got.view(torch.int32), want.view(torch.int32)), rep
