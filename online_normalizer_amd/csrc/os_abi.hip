@@ -823,14 +823,18 @@ bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
         {8, 32, 32, 32},   // <= 1024
         {4, 32, 16, 16},   // <= 2048
     };
+    // fp32, re-measured after the butterfly became two integer reductions
+    // (64..65536 rows x 64..2048 columns, K = 1..32; a limit holds where the
+    // rows kernel was within 2% or faster at the measured batches on both
+    // sides of the bucket's lower edge)
     static const int kMaxK[7][4] = {
         {32, 32, 32, 32},  // <= 16 columns
-        {16, 16, 32, 32},  // <= 64
-        {8, 16, 32, 32},   // <= 128
-        {2, 4, 16, 32},    // <= 256
-        {2, 4, 16, 32},    // <= 512
-        {2, 4, 16, 32},    // <= 1024
-        {2, 4, 4, 4},      // <= 2048
+        {32, 32, 32, 32},  // <= 64
+        {8, 32, 32, 32},   // <= 128
+        {4, 8, 16, 32},    // <= 256
+        {2, 8, 16, 32},    // <= 512
+        {2, 8, 16, 32},    // <= 1024
+        {2, 8, 8, 4},      // <= 2048
     };
     if (cols > 2048 || topk_rows_shape(rows, cols, K, dtype, al) == nullptr) return false;
     const int cb = cols <= 16    ? 0
