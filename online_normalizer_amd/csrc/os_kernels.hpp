@@ -1473,6 +1473,33 @@ __global__ void __launch_bounds__(256)
             for (int k = 0; k < VEC; ++k) dl += exp_e(x[v][k] - M);
         const float inv_d = rcp(group_sum<LPR>(dl));
 
+        if constexpr (FEWK) {
+            // K = 1 (the only K this form is launched for): the row's best is
+            // its maximum M, so the answer is the lowest in-row column holding
+            // M, with no keys at all (-0.0 == +0.0 as the key order has it).
+            // A row of only -inf (or NaN) has no entry equal to M, which starts
+            // at -FLT_MAX; it takes column 0, where the key order puts it too.
+            // Entries are visited from the last, so the lowest column stays.
+            int cl = INT_MAX;
+#pragma unroll
+            for (int v = VPL - 1; v >= 0; --v) {
+                const int e0 = (v * LPR + j) * VEC - ri.ph;
+#pragma unroll
+                for (int k = VEC - 1; k >= 0; --k) {
+                    const bool in_row = live & ((v * LPR + j) < ns) &
+                                        (ALIGNED | (static_cast<uint32_t>(e0 + k) < static_cast<uint32_t>(cols)));
+                    cl = (in_row & (x[v][k] == M)) ? e0 + k : cl;
+                }
+            }
+            const int wc = group_min_i32<LPR>(cl);
+            if (live & (j == 0)) {
+                const bool hit = wc != INT_MAX;
+                probs[row * K] = exp_e((hit ? M : -INFINITY) - M) * inv_d;
+                idx[row * K] = hit ? wc : 0;
+            }
+            continue;
+        }
+
         // keys; entry e = v * VEC + k of this lane is column
         // ((e >> LGV) * LPR + j) * VEC + (e & (VEC - 1)) - ph.  Rows whose
         // length is a whole number of slots hold only in-row entries in
