@@ -211,7 +211,8 @@ int os_forward_split_plan(int64_t rows, int64_t cols, int dtype);
  *   idx     [rows, K] int32 column indices, best first.  Order: larger logit
  *           first; equal logits (including -0.0 == +0.0) by lower index first.
  *   K       1 <= K <= min(cols, OS_TOPK_KMAX).
- *   Rows containing NaN give NaN probabilities and unspecified indices.
+ *   Rows containing NaN give NaN probabilities; their indices are K distinct
+ *   columns of the row, which ones unspecified.
  *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
  */
 int os_softmax_topk(const float *in, float *probs, int32_t *idx, int64_t rows, int64_t cols, int K,

@@ -1269,7 +1269,11 @@ __global__ void __launch_bounds__(W * 64)
                     // entry would pass, so take only in-row entries that rank
                     // ahead of the wave's K-th entry, re-read every round
                     // (once the list holds K entries of -inf, later -inf
-                    // entries of higher index are skipped)
+                    // entries of higher index are skipped).  A NaN entry
+                    // ranks as -inf here, so a row with fewer than K numbers
+                    // still yields K distinct in-row columns.  (A finite T
+                    // has at least K numbers at or above it, so NaN entries
+                    // are never needed once T is finite.)
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int wave_slot0 = base + u * BLOCK + w * kWave;
@@ -1279,7 +1283,7 @@ __global__ void __launch_bounds__(W * 64)
                             const int i_me = my_slot * VEC + k - ph;  // column index
                             const bool in_row =
                                 (my_slot < v1) & (static_cast<uint32_t>(i_me) < static_cast<uint32_t>(cols));
-                            const float xv = x[u][k];
+                            const float xv = (x[u][k] == x[u][k]) ? x[u][k] : -INFINITY;
                             uint64_t mask =
                                 __ballot(in_row & ahead_of(xv, i_me, readlane(L, K - 1), readlane(I, K - 1)));
                             while (mask != 0) {
@@ -1478,7 +1482,11 @@ __global__ void __launch_bounds__(256)
             // its maximum M, so the answer is the lowest in-row column holding
             // M, with no keys at all (-0.0 == +0.0 as the key order has it).
             // A row of only -inf (or NaN) has no entry equal to M, which starts
-            // at -FLT_MAX; it takes column 0, where the key order puts it too.
+            // at -FLT_MAX; it takes column 0, where the key order puts a row
+            // of only -inf too.  On rows without NaN this is the key order's
+            // answer; a row holding NaN takes its lowest column equal to the
+            // largest number (the key order would rank a NaN first), which is
+            // still an in-row column with a NaN probability.
             // Entries are visited from the last, so the lowest column stays.
             int cl = INT_MAX;
 #pragma unroll

@@ -16,6 +16,9 @@ def pytest_configure(config):
 
 
 @pytest.fixture(scope="session")
-def oracle_lib():
+def oracle_lib(tmp_path_factory):
     import oracle
+    from oracle.build import build, sanitizing
+    if sanitizing():  # a sanitizer build of the same source, for this session only
+        return oracle.Oracle(build(out=str(tmp_path_factory.mktemp("oracle_asan") / "liboracle.so")))
     return oracle.load()
