@@ -194,6 +194,30 @@ int os_softmax_forward_lse(const void *in, void *out, float *lse, int64_t rows, 
 int os_softmax_forward_split(const void *in, void *out, int64_t rows, int64_t cols, int dtype, int splits,
                              void *workspace, int64_t workspace_bytes, void *stream);
 
+/* Bytes of the device-resident scratch array os_softmax_forward_split_noalloc
+ * uses on each GPU (1 MiB): rows * splits * 8 must not exceed it. */
+#define OS_STATIC_SCRATCH_BYTES (1LL << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as os_softmax_forward_split, with the slice states kept in a
+ * fixed array inside the library instead of a caller's workspace.  The call
+ * allocates nothing and calls no allocating routine; each GPU the library
+ * runs on holds its own OS_STATIC_SCRATCH_BYTES array until the process ends
+ * (its address is looked up on the first call on that device).
+ *   in, out, rows, cols, dtype, splits, stream   as os_softmax_forward_split.
+ *   The array needs no initialisation (the first launch writes every slice
+ *   state before the second reads any) and keeps the last call's contents.
+ *   Every call on one GPU shares that GPU's array: calls on one stream are
+ *   ordered, but calls that overlap in time on one GPU (different streams)
+ *   race and give wrong results.
+ *   Returns OS_OK, OS_EINVAL (as os_softmax_forward_split, or
+ *   rows * splits * 8 > OS_STATIC_SCRATCH_BYTES), or OS_ELAUNCH.
+ */
+int os_softmax_forward_split_noalloc(const void *in, void *out, int64_t rows, int64_t cols, int dtype, int splits,
+                                     void *stream);
+
 /* Workspace bytes os_softmax_forward_split needs (0 for splits == 1), or
  * OS_EINVAL for rows < 0 or splits outside 1..OS_FWD_MAX_SPLITS.  Host only. */
 int64_t os_softmax_forward_workspace_bytes(int64_t rows, int splits);

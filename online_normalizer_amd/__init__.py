@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
   os_softmax_forward_lse(x, out=None, write_y=True) -> (y, lse)   y and the per-row logsumexp
   os_softmax_forward_split(x, splits=None, out=None, workspace=None)   rows split over workgroups
   os_softmax_forward_workspace_bytes(rows, splits), os_forward_split_plan(rows, cols, dtype)
+  os_softmax_forward_split_noalloc(x, splits=None, out=None)   the same, scratch inside the library
   os_softmax_topk(x, K, splits=None) -> (probs, idx)   fused softmax + top-K (fp32 or bf16 x)
   os_softmax_topk_ex(x, K, splits, workspace) -> (probs, idx)   the same with the dtype passed through
   os_softmax_topk_split(x, K, splits, workspace) -> (probs, idx)
@@ -40,11 +41,13 @@ __all__ = [
     "safe_softmax_forward", "os_device_copy", "os_device_copy_rows", "os_forward_plan", "os_last_error", "os_version",
     "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan", "os_softmax_topk_ex",
     "os_softmax_forward_split", "os_softmax_forward_workspace_bytes", "os_forward_split_plan",
+    "os_softmax_forward_split_noalloc", "OS_STATIC_SCRATCH_BYTES",
 ]
 
 OS_OK, OS_EINVAL, OS_EUNSUPPORTED, OS_ELAUNCH = 0, -1, -2, -3
 OS_F32, OS_BF16 = 0, 1
 OS_TOPK_KMAX = 32
+OS_STATIC_SCRATCH_BYTES = 1 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libonline_softmax.so")
 
@@ -85,6 +88,7 @@ def _load() -> ctypes.CDLL:
         "os_softmax_stats": [vp, vp, vp, i64, i64, i32, vp],
         "os_softmax_forward_lse": [vp, vp, vp, i64, i64, i32, vp],
         "os_softmax_forward_split": [vp, vp, i64, i64, i32, i32, vp, i64, vp],
+        "os_softmax_forward_split_noalloc": [vp, vp, i64, i64, i32, i32, vp],
         "os_forward_split_plan": [i64, i64, i32],
         "os_softmax_topk": [vp, vp, vp, i64, i64, i32, vp],
         "safe_softmax_forward": [vp, vp, i64, i64, i32, vp],
@@ -315,6 +319,21 @@ def os_softmax_forward_split(x: torch.Tensor, splits: int | None = None, out: to
            lib().os_softmax_forward_split(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), splits,
                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                           _stream(x)))
+    return out
+
+
+def os_softmax_forward_split_noalloc(x: torch.Tensor, splits: int | None = None,
+                                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """The split forward on the library's own device-resident scratch (no
+    workspace, no allocation inside the call; pass `out` to allocate nothing
+    here either).  splits=None asks the library's plan."""
+    rows, cols = _rows_cols(x)
+    out = _out_like(x, out)
+    if splits is None:
+        splits = os_forward_split_plan(rows, cols, x.dtype)
+    _check("os_softmax_forward_split_noalloc",
+           lib().os_softmax_forward_split_noalloc(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), splits,
+                                                  _stream(x)))
     return out
 
 

@@ -3,6 +3,8 @@
 // caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -453,6 +455,80 @@ int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t 
 
 }  // namespace
 
+namespace {
+
+// The forward with one workgroup (group) per row: the plan os_softmax_forward uses.
+int forward_unsplit(const char* fn, const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
+    int lpr = 0, vpl = 0;
+    bool staged = false;
+    plan_rows(in, out, cols, dtype, &lpr, &vpl, &staged);
+    return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, true, staged, stream);
+}
+
+// The split forward's two launches over a checked problem, with rows * splits
+// slice states at `states` (device memory, no initialisation needed: the first
+// launch writes every state before the second reads any).
+int forward_split_launch(const char* fn, const void* in, void* out, int64_t rows, int64_t cols, int dtype, int splits,
+                         State* states, void* stream) {
+    const bool al = vector_ok(in, out, cols, dtype);
+    const int64_t seg_vec = (slots_needed(cols, dtype, al) + splits - 1) / splits;
+    const int w = slice_waves(seg_vec);
+    const int block = w * 64;
+    const int64_t units = rows * splits;
+    const int grid = grid_for(units, block, 0);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const SplitFoldKernel kf = w == 1   ? split_fold_w<1>(dtype, al)
+                               : w == 4 ? split_fold_w<4>(dtype, al)
+                               : w == 8 ? split_fold_w<8>(dtype, al)
+                                        : split_fold_w<16>(dtype, al);
+    const SplitNormKernel kn = w == 1   ? split_norm_w<1>(dtype, al)
+                               : w == 4 ? split_norm_w<4>(dtype, al)
+                               : w == 8 ? split_norm_w<8>(dtype, al)
+                                        : split_norm_w<16>(dtype, al);
+    hipLaunchKernelGGL(kf, dim3(grid), dim3(block), 0, st, in, states, rows, static_cast<int>(cols), splits);
+    const int rc = launched(fn);
+    if (rc != OS_OK) return rc;
+    hipLaunchKernelGGL(kn, dim3(grid), dim3(block), 0, st, in, out, states, rows, static_cast<int>(cols), splits);
+    return launched(fn);
+}
+
+// Scratch of os_softmax_forward_split_noalloc: a file-scope device array, so
+// that call never allocates.  Each GPU the library runs on holds its own copy
+// (OS_STATIC_SCRATCH_BYTES) until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// and kept in g_scratch_addr.
+__device__ __align__(256) unsigned char scratch[OS_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of the current device's `scratch`, or an error.
+int static_scratch(const char* fn, void** addr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(OS_ELAUNCH, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(OS_ELAUNCH, "%s: device %d outside [0, %d)", fn, dev, kMaxDevices);
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr)
+                return fail(OS_ELAUNCH, "%s: hipGetSymbolAddress(scratch) on device %d failed: %s", fn, dev,
+                            hipGetErrorString(e));
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *addr = p;
+    return OS_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int os_version(void) { return kVersion; }
@@ -560,12 +636,7 @@ int os_softmax_forward_split(const void* in, void* out, int64_t rows, int64_t co
     int rc = check_problem(fn, in, out, true, rows, cols, dtype);
     if (rc == 1) return ok();
     if (rc != OS_OK) return rc;
-    if (splits == 1) {
-        int lpr = 0, vpl = 0;
-        bool staged = false;
-        plan_rows(in, out, cols, dtype, &lpr, &vpl, &staged);
-        return run_rows(fn, in, out, RowStats{}, rows, cols, dtype, lpr, vpl, 0, true, staged, stream);
-    }
+    if (splits == 1) return forward_unsplit(fn, in, out, rows, cols, dtype, stream);
     if (!workspace_fits(rows, splits * static_cast<int64_t>(sizeof(State))))
         return fail(OS_EINVAL, "%s: rows * splits overflows the workspace size", fn);
     const int64_t need = rows * splits * static_cast<int64_t>(sizeof(State));
@@ -574,28 +645,25 @@ int os_softmax_forward_split(const void* in, void* out, int64_t rows, int64_t co
     if (workspace_bytes < need)
         return fail(OS_EINVAL, "%s: workspace has %lld bytes, needs %lld", fn, (long long)workspace_bytes,
                     (long long)need);
-    const bool al = vector_ok(in, out, cols, dtype);
-    const int64_t seg_vec = (slots_needed(cols, dtype, al) + splits - 1) / splits;
-    const int w = slice_waves(seg_vec);
-    const int block = w * 64;
-    const int64_t units = rows * splits;
-    const int grid = grid_for(units, block, 0);
-    State* states = static_cast<State*>(workspace);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    const SplitFoldKernel kf = w == 1   ? split_fold_w<1>(dtype, al)
-                               : w == 4 ? split_fold_w<4>(dtype, al)
-                               : w == 8 ? split_fold_w<8>(dtype, al)
-                                        : split_fold_w<16>(dtype, al);
-    const SplitNormKernel kn = w == 1   ? split_norm_w<1>(dtype, al)
-                               : w == 4 ? split_norm_w<4>(dtype, al)
-                               : w == 8 ? split_norm_w<8>(dtype, al)
-                                        : split_norm_w<16>(dtype, al);
-    hipLaunchKernelGGL(kf, dim3(grid), dim3(block), 0, st, in, states, rows, static_cast<int>(cols), splits);
-    rc = launched(fn);
+    return forward_split_launch(fn, in, out, rows, cols, dtype, splits, static_cast<State*>(workspace), stream);
+}
+
+int os_softmax_forward_split_noalloc(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int splits,
+                                     void* stream) {
+    const char* fn = "os_softmax_forward_split_noalloc";
+    if (splits < 1 || splits > OS_FWD_MAX_SPLITS)
+        return fail(OS_EINVAL, "%s: splits=%d outside [1, %d]", fn, splits, OS_FWD_MAX_SPLITS);
+    int rc = check_problem(fn, in, out, true, rows, cols, dtype);
+    if (rc == 1) return ok();
     if (rc != OS_OK) return rc;
-    hipLaunchKernelGGL(kn, dim3(grid), dim3(block), 0, st, in, out, states, rows, static_cast<int>(cols), splits);
-    return launched(fn);
+    if (splits == 1) return forward_unsplit(fn, in, out, rows, cols, dtype, stream);
+    if (rows > OS_STATIC_SCRATCH_BYTES / (splits * static_cast<int64_t>(sizeof(State))))
+        return fail(OS_EINVAL, "%s: rows * splits * %d bytes exceeds the %lld-byte static scratch", fn,
+                    (int)sizeof(State), (long long)OS_STATIC_SCRATCH_BYTES);
+    State* states = nullptr;
+    rc = static_scratch(fn, reinterpret_cast<void**>(&states));
+    if (rc != OS_OK) return rc;
+    return forward_split_launch(fn, in, out, rows, cols, dtype, splits, states, stream);
 }
 
 int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {

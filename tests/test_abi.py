@@ -197,6 +197,26 @@ def test_forward_split_validation(L, ons):
     assert ons.os_forward_split_plan(256, 128256) == 1
 
 
+def test_forward_split_noalloc_validation(L, ons):
+    """Argument checks of the no-allocation split forward, all before any HIP
+    call: the static scratch holds OS_STATIC_SCRATCH_BYTES / 8 slice states."""
+    f = L.os_softmax_forward_split_noalloc
+    cap = ons.OS_STATIC_SCRATCH_BYTES // 8
+    assert ons.OS_STATIC_SCRATCH_BYTES == 1 << 20
+    assert f(FAKE, FAKE, cap // 256 + 1, 1 << 20, F32, 256, None) == EINVAL   # beyond the scratch
+    assert "static scratch" in ons.os_last_error()
+    assert f(FAKE, FAKE, cap // 2 + 1, 1 << 20, F32, 2, None) == EINVAL  # beyond the scratch at 2 splits
+    assert f(FAKE, FAKE, 1 << 58, 1, F32, 256, None) == EINVAL
+    assert f(FAKE, FAKE, 10, 1000, F32, 0, None) == EINVAL       # splits < 1
+    assert f(FAKE, FAKE, 10, 1000, F32, 257, None) == EINVAL     # splits > 256
+    assert f(FAKE, None, 10, 1000, F32, 4, None) == EINVAL       # no output
+    assert f(None, FAKE, 10, 1000, F32, 4, None) == EINVAL       # no input
+    assert f(FAKE, FAKE, 10, 1000, 5, 4, None) == EINVAL         # unknown dtype
+    assert f(FAKE + 2, FAKE, 10, 1000, F32, 4, None) == EINVAL   # misaligned input
+    assert f(None, None, 0, 1000, F32, 4, None) == 0             # empty
+    assert f(None, None, 10, 0, F32, 4, None) == 0               # empty rows
+
+
 def test_copy_validation(L):
     assert L.os_device_copy(FAKE, FAKE + 4096, 20, None) == EINVAL      # not a multiple of 16
     assert L.os_device_copy(FAKE + 4, FAKE + 4096, 32, None) == EINVAL  # misaligned
