@@ -22,6 +22,12 @@ with the passages it follows:
 * ``topk`` -- brute-force sort of the whole row under (value desc, index asc),
   probabilities e^{u-m}/d over the whole row (section 4 of the paper summary),
   for fp32 rows or bf16 rows (widened exactly).
+* ``naive_softmax`` -- the unshifted softmax e^{x_i} / sum_j e^{x_j} in two
+  passes, section 2 "Original softmax" of the paper summary, in double with
+  no guard against overflow.
+* ``topk_select`` -- the K largest entries of each row and their columns by
+  the same sort, returned as the entries themselves: the TopK stage of the
+  unfused pipelines in the access table of section 4 of the paper summary.
 
 Rows are independent, so the wrappers may split a batch of rows over host
 threads (each thread runs the same sequential C code on its own rows).
@@ -77,9 +83,13 @@ class Oracle:
         lib.oracle_online_state.restype = None
         lib.oracle_combine.argtypes = [ctypes.c_double] * 4 + [_c_double_p, _c_double_p]
         lib.oracle_combine.restype = None
-        for name in ("oracle_topk_f32", "oracle_topk_bf16"):
+        for name in ("oracle_topk_f32", "oracle_topk_bf16", "oracle_topk_select_f32", "oracle_topk_select_bf16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
+            fn.restype = ctypes.c_int
+        for name in ("oracle_naive_softmax_f32", "oracle_naive_softmax_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, i64, i64, vp]
             fn.restype = ctypes.c_int
         self.lib = lib
 
@@ -105,6 +115,13 @@ class Oracle:
     # -- softmax -----------------------------------------------------------
     def softmax(self, x: np.ndarray, threads: int = 1) -> np.ndarray:
         """Row-wise softmax in double.  ``x``: 2-D float32, or uint16 bf16 bits."""
+        return self._rowwise(x, threads, self.lib.oracle_softmax_f32, self.lib.oracle_softmax_bf16)
+
+    def naive_softmax(self, x: np.ndarray, threads: int = 1) -> np.ndarray:
+        """Row-wise e^{x_i} / sum_j e^{x_j} in double, no maximum subtracted."""
+        return self._rowwise(x, threads, self.lib.oracle_naive_softmax_f32, self.lib.oracle_naive_softmax_bf16)
+
+    def _rowwise(self, x: np.ndarray, threads: int, fn32, fn16) -> np.ndarray:
         x = np.ascontiguousarray(x)
         if x.ndim != 2:
             raise ValueError("x must be 2-D [rows, cols]")
@@ -113,9 +130,9 @@ class Oracle:
         if rows == 0 or cols == 0:
             return y
         if x.dtype == np.float32:
-            fn, esz = self.lib.oracle_softmax_f32, 4
+            fn, esz = fn32, 4
         elif x.dtype == np.uint16:
-            fn, esz = self.lib.oracle_softmax_bf16, 2
+            fn, esz = fn16, 2
         else:
             raise TypeError("x must be float32 or uint16 (bf16 bit patterns)")
         xb, yb = x.ctypes.data, y.ctypes.data
@@ -190,11 +207,19 @@ class Oracle:
     def topk(self, x: np.ndarray, K: int, threads: int = 1):
         """K best entries per row (value desc, index asc) of a float32 array, or
         of a uint16 array of bf16 bit patterns; probabilities over the whole row."""
+        return self._ranked(x, K, threads, self.lib.oracle_topk_f32, self.lib.oracle_topk_bf16)
+
+    def topk_select(self, x: np.ndarray, K: int, threads: int = 1):
+        """K best entries per row (value desc, index asc), returned as the
+        entries themselves (in double) with their columns."""
+        return self._ranked(x, K, threads, self.lib.oracle_topk_select_f32, self.lib.oracle_topk_select_bf16)
+
+    def _ranked(self, x: np.ndarray, K: int, threads: int, fn32, fn16):
         x = np.ascontiguousarray(x)
         if x.dtype == np.float32:
-            fn, esz = self.lib.oracle_topk_f32, 4
+            fn, esz = fn32, 4
         elif x.dtype == np.uint16:
-            fn, esz = self.lib.oracle_topk_bf16, 2
+            fn, esz = fn16, 2
         else:
             raise TypeError("x must be float32 or uint16 (bf16 bit patterns)")
         rows, cols = x.shape

@@ -21,6 +21,13 @@
  *            row).  The oracle does not fuse anything: it sorts the whole row.
  *   [LSE]    "6.2 FlashAttention V2 chi tiết", sections 6.1 and 7.1 (the
  *            per-row logsumexp L = m + log(l) kept in place of m and l).
+ *   [NAIVE]  the paper summary, section 2 "Original softmax", its first
+ *            paragraph: y_i = e^{x_i} / sum_j e^{x_j} in two passes (the sum,
+ *            then the division), no maximum subtracted.
+ *   [SELECT] the paper summary, section 4, the access table: the TopK stage
+ *            of the unfused pipelines reads the probabilities and keeps the K
+ *            largest; here the K largest entries of any row, returned as the
+ *            entries themselves (no exponential, no normaliser).
  *
  * Readings taken where the pages are silent:
  *   - An element equal to -inf contributes e^{-inf} = 0 and leaves the state
@@ -35,6 +42,12 @@
  *   - The logsumexp of a row is log(sum_j e^{x_j}), written as m + log(d)
  *     (an exact identity that keeps the sum finite): -inf for an empty or
  *     all -inf row, NaN for a row holding NaN or +inf, as for the softmax.
+ *   - The naive softmax is the definition computed as printed, in double:
+ *     e^x overflows to +inf past x = 709.78 and underflows to 0 below about
+ *     -745, and the results then follow IEEE (inf/inf and 0/0 are NaN).  That
+ *     is the failure the page describes; the oracle does not guard it.
+ *   - Selection orders entries like the top-K, (value descending, index
+ *     ascending); rows holding NaN have no specified order.
  *
  * Every floating-point step is IEEE double with no reassociation: build with
  * -ffp-contract=off and without -ffast-math.
@@ -317,6 +330,105 @@ int oracle_topk_bf16(const uint16_t *x, int64_t rows, int64_t cols, int K, doubl
     for (int64_t r = 0; r < rows; ++r) {
         widen_row_bf16(x + r * cols, cols, buf);
         topk_row(buf, cols, K, order, probs + r * K, idx + r * K);
+    }
+    free(buf);
+    free(order);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* [NAIVE] y_i = e^{x_i} / sum_j e^{x_j}: pass 1 sums e^{x_j}, pass 2       */
+/* divides; no maximum is subtracted.                                       */
+/* ---------------------------------------------------------------------- */
+static void row_naive_softmax(const double *x, int64_t n, double *y)
+{
+    double d = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        d += exp(x[j]);
+    for (int64_t j = 0; j < n; ++j)
+        y[j] = exp(x[j]) / d;
+}
+
+int oracle_naive_softmax_f32(const float *x, int64_t rows, int64_t cols, double *y)
+{
+    double *buf = (double *)malloc((size_t)(cols > 0 ? cols : 1) * sizeof(double));
+    if (!buf)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        widen_row_f32(x + r * cols, cols, buf);
+        row_naive_softmax(buf, cols, y + r * cols);
+    }
+    free(buf);
+    return 0;
+}
+
+int oracle_naive_softmax_bf16(const uint16_t *x, int64_t rows, int64_t cols, double *y)
+{
+    double *buf = (double *)malloc((size_t)(cols > 0 ? cols : 1) * sizeof(double));
+    if (!buf)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        widen_row_bf16(x + r * cols, cols, buf);
+        row_naive_softmax(buf, cols, y + r * cols);
+    }
+    free(buf);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* [SELECT] brute force: sort the whole row under (value desc, index asc)   */
+/* and keep the first K entries and their columns.                          */
+/* ---------------------------------------------------------------------- */
+static void select_row(const double *buf, int64_t cols, int K, ranked_t *order, double *vals, int32_t *idx)
+{
+    for (int64_t j = 0; j < cols; ++j) {
+        order[j].value = buf[j];
+        order[j].index = j;
+    }
+    qsort(order, (size_t)cols, sizeof(ranked_t), rank_order);
+    for (int k = 0; k < K; ++k) {
+        vals[k] = order[k].value;
+        idx[k] = (int32_t)order[k].index;
+    }
+}
+
+/* vals[r*K + k], idx[r*K + k] for k = 0..K-1, best first, for an fp32 input.
+ * Returns 0, -1 on allocation failure, -2 if K is out of [1, cols]. */
+int oracle_topk_select_f32(const float *x, int64_t rows, int64_t cols, int K, double *vals, int32_t *idx)
+{
+    if (K < 1 || (int64_t)K > cols)
+        return -2;
+    double *buf = (double *)malloc((size_t)cols * sizeof(double));
+    ranked_t *order = (ranked_t *)malloc((size_t)cols * sizeof(ranked_t));
+    if (!buf || !order) {
+        free(buf);
+        free(order);
+        return -1;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        widen_row_f32(x + r * cols, cols, buf);
+        select_row(buf, cols, K, order, vals + r * K, idx + r * K);
+    }
+    free(buf);
+    free(order);
+    return 0;
+}
+
+/* The same for bf16 input given as raw 16-bit patterns (widened exactly). */
+int oracle_topk_select_bf16(const uint16_t *x, int64_t rows, int64_t cols, int K, double *vals, int32_t *idx)
+{
+    if (K < 1 || (int64_t)K > cols)
+        return -2;
+    double *buf = (double *)malloc((size_t)cols * sizeof(double));
+    ranked_t *order = (ranked_t *)malloc((size_t)cols * sizeof(ranked_t));
+    if (!buf || !order) {
+        free(buf);
+        free(order);
+        return -1;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        widen_row_bf16(x + r * cols, cols, buf);
+        select_row(buf, cols, K, order, vals + r * K, idx + r * K);
     }
     free(buf);
     free(order);

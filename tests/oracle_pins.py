@@ -312,6 +312,58 @@ def pin_logsumexp(o):
     assert np.all(np.isnan(o.softmax(z)))
 
 
+def pin_naive_softmax(o):
+    """The unshifted softmax of section 2: closed forms, scipy where e^x stays
+    finite, and the overflow / underflow the page warns of, in double."""
+    from scipy.special import softmax
+    e = math.e
+    y = o.naive_softmax(np.array([[1.0, 2.0, 3.0]], dtype=np.float32))[0]
+    den = e + e * e + e ** 3
+    for k in range(3):
+        assert _rel(y[k], math.exp(k + 1.0) / den) <= 1e-15
+    assert o.naive_softmax(np.array([[7.5]], dtype=np.float32)).tolist() == [[1.0]]
+    a, b = 0.75, -2.5  # two entries: the logistic function of the difference
+    y2 = o.naive_softmax(np.array([[a, b]], dtype=np.float32))[0]
+    assert _rel(y2[0], 1.0 / (1.0 + math.exp(b - a))) <= 1e-15
+    assert _rel(y2[1], 1.0 / (1.0 + math.exp(a - b))) <= 1e-15
+    x = workloads.normal(16, 333, seed=71, scale=4.0)
+    assert np.allclose(o.naive_softmax(x), softmax(x.astype(np.float64), axis=1), rtol=1e-13, atol=0)
+    xb = workloads.f32_to_bf16_bits(workloads.normal(4, 99, seed=72, scale=2.0))
+    wide = workloads.bf16_bits_to_f32(xb).astype(np.float64)
+    assert np.allclose(o.naive_softmax(xb), softmax(wide, axis=1), rtol=1e-13, atol=0)
+    # -inf entries add e^{-inf} = 0
+    xi = np.array([[1.0, -np.inf, 2.0, -np.inf]], dtype=np.float32)
+    yi = o.naive_softmax(xi)[0]
+    assert yi[1] == 0.0 and yi[3] == 0.0 and _rel(yi[2], 1.0 / (1.0 + math.exp(-1.0))) <= 1e-15
+    # overflow: e^1000 is +inf in double, so the maximum's entry is inf/inf
+    yo = o.naive_softmax(np.array([[1000.0, 0.0]], dtype=np.float32))[0]
+    assert math.isnan(yo[0]) and yo[1] == 0.0
+    # underflow: e^{-1000} is 0, so the whole row is 0/0
+    assert np.all(np.isnan(o.naive_softmax(np.array([[-1000.0, -1000.0]], dtype=np.float32))))
+
+
+def pin_topk_select(o):
+    """Selection = numpy's stable argsort of -x (ties to the lowest index),
+    values = the entries themselves; also on bf16 rows and K = cols."""
+    v, i = o.topk_select(np.array([[3, 5, 5, 1, 5]], dtype=np.float32), 5)
+    assert i.tolist() == [[1, 2, 4, 0, 3]] and v.tolist() == [[5.0, 5.0, 5.0, 3.0, 1.0]]
+    rng = np.random.Generator(np.random.PCG64(73))
+    x = rng.integers(-4, 5, size=(32, 301)).astype(np.float32)   # heavy ties
+    x[::4] = workloads.normal(8, 301, seed=74, scale=3.0)
+    x[1, :5] = [-0.0, 0.0, -0.0, 0.0, -0.0]                       # -0.0 ties +0.0
+    x[2, 100:] = -np.inf
+    for K in (1, 7, 32, 301):
+        v, i = o.topk_select(x, K)
+        ref = np.argsort(-x.astype(np.float64), axis=1, kind="stable")[:, :K]
+        assert np.array_equal(i, ref), K
+        assert np.array_equal(v, np.take_along_axis(x, ref, axis=1).astype(np.float64)), K
+    xb = workloads.f32_to_bf16_bits(workloads.normal(6, 200, seed=75, scale=2.0))
+    wide = workloads.bf16_bits_to_f32(xb).astype(np.float64)
+    v, i = o.topk_select(xb, 9)
+    ref = np.argsort(-wide, axis=1, kind="stable")[:, :9]
+    assert np.array_equal(i, ref) and np.array_equal(v, np.take_along_axis(wide, ref, axis=1))
+
+
 PINS = [
     pin_two_shard_worked_example,
     pin_lesson_mock_vector,
@@ -327,6 +379,8 @@ PINS = [
     pin_bf16_widening,
     pin_topk_library,
     pin_logsumexp,
+    pin_naive_softmax,
+    pin_topk_select,
 ]
 
 

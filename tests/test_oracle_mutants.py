@@ -41,6 +41,14 @@ MUTANTS = [
     ("bf16_wrong_shift", "((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
     ("logsumexp_drops_max", "return (d == 0.0) ? -INFINITY : m + log(d);",
      "return (d == 0.0) ? -INFINITY : log(d);"),
+    ("naive_subtracts_a_maximum",  # the safe form: no longer overflows as the page says
+     "        d += exp(x[j]);\n    for (int64_t j = 0; j < n; ++j)\n        y[j] = exp(x[j]) / d;",
+     "        d += exp(x[j] - row_max(x, n));\n    for (int64_t j = 0; j < n; ++j)\n"
+     "        y[j] = exp(x[j] - row_max(x, n)) / d;"),
+    ("naive_sum_skips_first", "    double d = 0.0;\n    for (int64_t j = 0; j < n; ++j)\n        d += exp(x[j]);",
+     "    double d = 0.0;\n    for (int64_t j = 1; j < n; ++j)\n        d += exp(x[j]);"),
+    ("select_returns_reversed", "        vals[k] = order[k].value;", "        vals[k] = order[K - 1 - k].value;"),
+    ("select_returns_probability_like", "        vals[k] = order[k].value;", "        vals[k] = exp(order[k].value);"),
 ]
 
 
