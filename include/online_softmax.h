@@ -298,6 +298,41 @@ int safe_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, 
                          void *stream);
 
 /*
+ * Baseline: the unshifted ("original") softmax y_i = e^{x_i} / sum_j e^{x_j}
+ * of the paper summary, section 2, in two passes over the input in global
+ * memory (the sum of e^x, then normalise and store) with no maximum
+ * subtracted: the third algorithm of the paper summary's section 5
+ * comparison.  Same arguments, layout and geometry as safe_softmax_forward.
+ *   Results match the safe and online forms only where e^x is finite and
+ *   normal in fp32 (about -87 < x < 88.7 for every entry); past that, e^x
+ *   overflows to +inf or underflows to 0 and rows turn to NaN or lose
+ *   accuracy, the failure the page describes.  Not for production use.
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int naive_softmax_forward(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                          void *stream);
+
+/*
+ * Top-K selection alone: the K largest entries of each row under (value desc,
+ * index asc), written as the entries themselves with their columns; no
+ * exponential and no normaliser.  This is the TopK stage of the unfused
+ * pipelines in the paper summary's section 4 access table (softmax written
+ * out, then TopK reading the probabilities), the comparison point of the
+ * fused os_softmax_topk.  One read of the input; the fused kernel's filter,
+ * lists and merge with the fold switched off.
+ *   in      [rows, cols] of `dtype` (OS_F32 or OS_BF16, widened exactly).
+ *   vals    [rows, K] float, best first: the selected entries.
+ *   idx     [rows, K] int32 columns, best first; equal entries (including
+ *           -0.0 == +0.0) by lower column first.
+ *   K       1 <= K <= min(cols, OS_TOPK_KMAX).
+ *   Rows containing NaN give K distinct in-row columns, which ones and their
+ *   values unspecified.
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_topk_select(const void *in, int dtype, float *vals, int32_t *idx, int64_t rows, int64_t cols, int K,
+                   void *stream);
+
+/*
  * Plain device copy of `bytes` bytes with 128-bit accesses: the reference
  * read+write kernel used to calibrate traffic counters and as a bandwidth
  * ceiling.  src and dst must be 16-byte aligned, bytes a multiple of 16,

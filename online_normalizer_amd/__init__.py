@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
   os_softmax_topk_split(x, K, splits, workspace) -> (probs, idx)
   os_softmax_topk_workspace_bytes(rows, K, splits), os_topk_plan(rows, cols, K)
   safe_softmax_forward(x, out=None)            three-pass baseline
+  naive_softmax_forward(x, out=None)           unshifted two-pass baseline (overflows past x = 88.7)
+  os_topk_select(x, K) -> (vals, idx)          top-K of the entries alone (the unfused pipelines' TopK)
   os_device_copy(src, dst)                     plain copy (bandwidth reference)
   os_device_copy_rows(src, dst)                copy with the row-per-workgroup pattern (reference)
   os_forward_plan(cols, dtype) -> (lanes_per_row, vecs_per_lane)
@@ -41,7 +43,7 @@ __all__ = [
     "safe_softmax_forward", "os_device_copy", "os_device_copy_rows", "os_forward_plan", "os_last_error", "os_version",
     "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan", "os_softmax_topk_ex",
     "os_softmax_forward_split", "os_softmax_forward_workspace_bytes", "os_forward_split_plan",
-    "os_softmax_forward_split_noalloc", "OS_STATIC_SCRATCH_BYTES",
+    "os_softmax_forward_split_noalloc", "OS_STATIC_SCRATCH_BYTES", "naive_softmax_forward", "os_topk_select",
 ]
 
 OS_OK, OS_EINVAL, OS_EUNSUPPORTED, OS_ELAUNCH = 0, -1, -2, -3
@@ -92,6 +94,8 @@ def _load() -> ctypes.CDLL:
         "os_forward_split_plan": [i64, i64, i32],
         "os_softmax_topk": [vp, vp, vp, i64, i64, i32, vp],
         "safe_softmax_forward": [vp, vp, i64, i64, i32, vp],
+        "naive_softmax_forward": [vp, vp, i64, i64, i32, vp],
+        "os_topk_select": [vp, i32, vp, vp, i64, i64, i32, vp],
         "os_device_copy": [vp, vp, i64, vp],
         "os_device_copy_rows": [vp, vp, i64, i64, vp],
         "os_version": [],
@@ -359,6 +363,26 @@ def safe_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> to
     _check("safe_softmax_forward",
            lib().safe_softmax_forward(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), _stream(x)))
     return out
+
+
+def naive_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    rows, cols = _rows_cols(x)
+    out = _out_like(x, out)
+    _check("naive_softmax_forward",
+           lib().naive_softmax_forward(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), _stream(x)))
+    return out
+
+
+def os_topk_select(x: torch.Tensor, K: int, vals: torch.Tensor | None = None,
+                   idx: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """The K largest entries of each row (value desc, index asc) and their columns."""
+    rows, cols, v_new, i_new = _topk_out(x, K)
+    vals = v_new if vals is None else vals
+    idx = i_new if idx is None else idx
+    _check("os_topk_select",
+           lib().os_topk_select(x.data_ptr(), _dtype_code(x), vals.data_ptr(), idx.data_ptr(), rows, cols, K,
+                                _stream(x)))
+    return vals, idx
 
 
 def os_device_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:

@@ -80,7 +80,7 @@ int launched(const char* fn) {
 // Register-resident shapes built into the library.
 // ---------------------------------------------------------------------------
 typedef void (*RowKernel)(const void*, void*, RowStats, int64_t, int, uint32_t);
-typedef void (*SafeKernel)(const void*, void*, int64_t, int, uint32_t);
+typedef void (*SafeKernel)(const void*, void*, int64_t, int, uint32_t, int);
 
 struct ResidentShape {
     int lpr, vpl;
@@ -493,6 +493,39 @@ int forward_split_launch(const char* fn, const void* in, void* out, int64_t rows
     return launched(fn);
 }
 
+// The baselines over global memory: safe softmax in three passes (naive = 0)
+// or the unshifted softmax in two (naive = 1), with the lanes-per-row geometry
+// the forward picks when the rows fit it, streaming otherwise.
+int baseline_forward(const char* fn, const void* in, void* out, int64_t rows, int64_t cols, int dtype, int naive,
+                     void* stream) {
+    int rc = check_problem(fn, in, out, true, rows, cols, dtype);
+    if (rc == 1) return ok();
+    if (rc != OS_OK) return rc;
+    const bool al = vector_ok(in, out, cols, dtype);
+    const int bf = dtype == OS_BF16 ? 1 : 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int lpr = 0, vpl = 0;
+    auto_plan(cols, dtype, al, &lpr, &vpl);
+    (void)hipGetLastError();
+    if (lpr != 0) {
+        // rows that fit the register-resident geometry: same lanes and
+        // vectors as the forward, every pass over global memory
+        const ResidentShape* shape = find_shape(lpr, vpl, dtype);
+        const int block = lpr <= 64 ? 256 : lpr;
+        const int rpb = block / lpr;
+        const int grid = grid_for((rows + rpb - 1) / rpb, block, 0);
+        hipLaunchKernelGGL(shape->safe[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, rows,
+                           static_cast<int>(cols), resident_grid(lpr, vpl, cols, dtype, al), naive);
+    } else {
+        const int w = stream_waves(cols, dtype);
+        const int block = w * 64;
+        const int grid = grid_for(rows, block, 0);
+        hipLaunchKernelGGL(safe_kernel(w, dtype, al), dim3(grid), dim3(block), 0, st, in, out, rows,
+                           static_cast<int>(cols), kGrid128, naive);
+    }
+    return launched(fn);
+}
+
 // Scratch of os_softmax_forward_split_noalloc: a file-scope device array, so
 // that call never allocates.  Each GPU the library runs on holds its own copy
 // (OS_STATIC_SCRATCH_BYTES) until the process ends.  In host code `scratch`
@@ -667,33 +700,11 @@ int os_softmax_forward_split_noalloc(const void* in, void* out, int64_t rows, in
 }
 
 int safe_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
-    const char* fn = "safe_softmax_forward";
-    int rc = check_problem(fn, in, out, true, rows, cols, dtype);
-    if (rc == 1) return ok();
-    if (rc != OS_OK) return rc;
-    const bool al = vector_ok(in, out, cols, dtype);
-    const int bf = dtype == OS_BF16 ? 1 : 0;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int lpr = 0, vpl = 0;
-    auto_plan(cols, dtype, al, &lpr, &vpl);
-    (void)hipGetLastError();
-    if (lpr != 0) {
-        // rows that fit the register-resident geometry: same lanes and
-        // vectors as the forward, three passes over global memory
-        const ResidentShape* shape = find_shape(lpr, vpl, dtype);
-        const int block = lpr <= 64 ? 256 : lpr;
-        const int rpb = block / lpr;
-        const int grid = grid_for((rows + rpb - 1) / rpb, block, 0);
-        hipLaunchKernelGGL(shape->safe[bf][al ? 1 : 0], dim3(grid), dim3(block), 0, st, in, out, rows,
-                           static_cast<int>(cols), resident_grid(lpr, vpl, cols, dtype, al));
-    } else {
-        const int w = stream_waves(cols, dtype);
-        const int block = w * 64;
-        const int grid = grid_for(rows, block, 0);
-        hipLaunchKernelGGL(safe_kernel(w, dtype, al), dim3(grid), dim3(block), 0, st, in, out, rows,
-                           static_cast<int>(cols), kGrid128);
-    }
-    return launched(fn);
+    return baseline_forward("safe_softmax_forward", in, out, rows, cols, dtype, 0, stream);
+}
+
+int naive_softmax_forward(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
+    return baseline_forward("naive_softmax_forward", in, out, rows, cols, dtype, 1, stream);
 }
 
 }  // extern "C"
@@ -731,7 +742,7 @@ int check_topk(const char* fn, const void* in, int dtype, const float* probs, co
     return OS_OK;
 }
 
-typedef void (*TopkKernel)(const void*, float*, int*, int64_t, int, int, int, State*, TopkEntry*);
+typedef void (*TopkKernel)(const void*, float*, int*, int64_t, int, int, int, State*, TopkEntry*, int);
 
 // Vectors per lane per tile: 4 for fp32, 2 for bf16 (16 elements either way).
 template <int W, bool BF16>
@@ -917,9 +928,9 @@ bool use_topk_rows(int64_t rows, int64_t cols, int K, int dtype, bool al) {
 }
 
 int launch_topk(const char* fn, const void* in, int dtype, float* probs, int32_t* idx, int64_t rows, int64_t cols,
-                int K, int S, void* workspace, void* stream) {
+                int K, int S, void* workspace, void* stream, int select = 0) {
     const bool al = aligned(in, 16) && ((cols * elt_size(dtype)) % 16) == 0;
-    if (S == 1 && use_topk_rows(rows, cols, K, dtype, al)) {
+    if (S == 1 && !select && use_topk_rows(rows, cols, K, dtype, al)) {
         const TopkRowsShape* sh = topk_rows_shape(rows, cols, K, dtype, al);
         const int rpb = 256 / sh->lpr;
         (void)hipGetLastError();
@@ -950,7 +961,7 @@ int launch_topk(const char* fn, const void* in, int dtype, float* probs, int32_t
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, st, in, probs, idx, rows, static_cast<int>(cols), K, S,
-                       states, lists);
+                       states, lists, select);
     if (S > 1) {
         const int rc = launched(fn);
         if (rc != OS_OK) return rc;
@@ -1030,6 +1041,15 @@ int os_softmax_topk_ex(const void* in, int dtype, float* probs, int32_t* idx, in
                        int splits, void* workspace, int64_t workspace_bytes, void* stream) {
     return topk_split_common("os_softmax_topk_ex", in, dtype, probs, idx, rows, cols, K, splits, workspace,
                              workspace_bytes, stream);
+}
+
+int os_topk_select(const void* in, int dtype, float* vals, int32_t* idx, int64_t rows, int64_t cols, int K,
+                   void* stream) {
+    const char* fn = "os_topk_select";
+    const int rc = check_topk(fn, in, dtype, vals, idx, rows, cols, K);
+    if (rc == 1) return ok();
+    if (rc != OS_OK) return rc;
+    return launch_topk(fn, in, dtype, vals, idx, rows, cols, K, 1, nullptr, stream, 1);
 }
 
 int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {

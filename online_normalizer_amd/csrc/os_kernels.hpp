@@ -665,10 +665,13 @@ __global__ void __launch_bounds__(1024)
 // Baseline: safe softmax in three streaming passes over global memory
 // (maximum; sum of e^{x - m}; normalise and store), same geometry and loads
 // as k_stream so that the two differ only in the passes.
+// naive != 0: the unshifted softmax of the paper summary's section 2 instead,
+// pass 1 skipped and m = 0 (two passes: sum of e^x, then e^x / d); e^x
+// overflows past x = 88.7 and the row then turns to NaN, as the page warns.
 // ---------------------------------------------------------------------------
 template <bool BF16, int W, int U, bool ALIGNED>
 __global__ void __launch_bounds__(W * 64)
-    k_safe3(const void* in, void* out, int64_t rows, int cols, uint32_t gmask) {
+    k_safe3(const void* in, void* out, int64_t rows, int cols, uint32_t gmask, int naive) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int BLOCK = W * 64;
@@ -684,23 +687,26 @@ __global__ void __launch_bounds__(W * 64)
         const Buf bin(si.base, si.bytes);
         const RowAt ri = row_at<BF16>(si.lead, gmask);
         const int nvec = slot_count<BF16>(cols, ri.ph);
-        // pass 1: maximum
-        float m = kFloor;
-        for (int base = 0; base < nvec; base += BLOCK * U) {
-            float x[U][VEC];
-            load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
+        // pass 1: maximum (uniform skip for the naive form)
+        float m = 0.0f;
+        if (!naive) {
+            m = kFloor;
+            for (int base = 0; base < nvec; base += BLOCK * U) {
+                float x[U][VEC];
+                load_slots<BF16, U, ALIGNED, false>(bin, ri, base + tid, BLOCK, nvec, cols, true, x);
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+                for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[u][k]);
-        }
-        m = wave_max(m);
-        if constexpr (W > 1) {
-            if ((tid & (kWave - 1)) == 0) lds_m[par][tid / kWave] = m;
-            __syncthreads();
-            m = lds_m[par][0];
+                    for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[u][k]);
+            }
+            m = wave_max(m);
+            if constexpr (W > 1) {
+                if ((tid & (kWave - 1)) == 0) lds_m[par][tid / kWave] = m;
+                __syncthreads();
+                m = lds_m[par][0];
 #pragma unroll
-            for (int w = 1; w < W; ++w) m = fmaxf(m, lds_m[par][w]);
+                for (int w = 1; w < W; ++w) m = fmaxf(m, lds_m[par][w]);
+            }
         }
         // pass 2: sum of e^{x - m}
         float d = 0.0f;
@@ -747,10 +753,11 @@ __global__ void __launch_bounds__(W * 64)
 // and 2 use plain loads, so re-reads of short rows can hit in cache, which is
 // the regime the pages' benchmark describes for short vectors.  Shapes of at
 // most 8 vectors per lane; longer rows take the streaming baseline.
+// naive != 0: the unshifted two-pass softmax, as in k_safe3.
 // ---------------------------------------------------------------------------
 template <bool BF16, int LPR, int VPL, bool ALIGNED>
 __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
-    k_safe3_rows(const void* in, void* out, int64_t rows, int cols, uint32_t gmask) {
+    k_safe3_rows(const void* in, void* out, int64_t rows, int cols, uint32_t gmask, int naive) {
     using E = Elt<BF16>;
     constexpr int VEC = E::kVec;
     constexpr int BLOCK = LPR <= 64 ? 256 : LPR;
@@ -778,20 +785,23 @@ __global__ void __launch_bounds__(LPR <= 64 ? 256 : LPR)
         static_assert(VPL <= 8, "the baseline streams rows past 8 vectors per lane");
         float x[VPL][VEC];
 
-        // pass 1: maximum
-        float m = kFloor;
-        load_slots<BF16, VPL, ALIGNED, false>(bin, ri, j, LPR, nvec, cols, live, x);
+        // pass 1: maximum (uniform skip for the naive form)
+        float m = 0.0f;
+        if (!naive) {
+            m = kFloor;
+            load_slots<BF16, VPL, ALIGNED, false>(bin, ri, j, LPR, nvec, cols, live, x);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
+            for (int v = 0; v < VPL; ++v)
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[v][k]);
-        m = group_max<GROUP>(m);
-        if constexpr (W > 1) {
-            if ((tid & (kWave - 1)) == 0) lds_m[par][tid / kWave] = m;
-            __syncthreads();
-            m = lds_m[par][0];
+                for (int k = 0; k < VEC; ++k) m = fmaxf(m, x[v][k]);
+            m = group_max<GROUP>(m);
+            if constexpr (W > 1) {
+                if ((tid & (kWave - 1)) == 0) lds_m[par][tid / kWave] = m;
+                __syncthreads();
+                m = lds_m[par][0];
 #pragma unroll
-            for (int w = 1; w < W; ++w) m = fmaxf(m, lds_m[par][w]);
+                for (int w = 1; w < W; ++w) m = fmaxf(m, lds_m[par][w]);
+            }
         }
         // pass 2: sum of e^{x - m}
         float d = 0.0f;
@@ -1135,10 +1145,14 @@ __device__ __forceinline__ void topk_of_lists(int n, int K, int lane, Get get, f
 // row's vector slots, each writing its state (m, d) and its sorted K-list to
 // the workspace; k_topk_merge (the next launch on the stream, so every
 // partial is visible) combines them.
+// select != 0 (SPLIT = false only): top-K selection alone, the TopK stage of
+// the paper summary's unfused pipelines (section 4, the access table): no
+// (m, d) fold, no exponential, and the K entries themselves are written in
+// place of probabilities.
 template <bool BF16, int W, int U, bool ALIGNED, bool SPLIT>
 __global__ void __launch_bounds__(W * 64)
     k_topk(const void* in, float* probs, int* idx, int64_t rows, int cols, int K, int S, State* ws_state,
-           TopkEntry* ws_list) {
+           TopkEntry* ws_list, int select) {
     using E = Elt<BF16>;
     static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16,
                   "the final merge packs W lists of up to 32 entries into at most 8 registers");
@@ -1223,14 +1237,17 @@ __global__ void __launch_bounds__(W * 64)
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) mx = fmaxf(mx, x[u][k]);
-            // (m, d) fold over the tile
+            // (m, d) fold over the tile (the running maximum alone when
+            // selecting: the refreshed bound reads it)
             const float mn = fmaxf(ml, mx);
-            float acc = dl * exp_e(ml - mn);
+            if (!select) {
+                float acc = dl * exp_e(ml - mn);
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+                for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) acc += exp_e(x[u][k] - mn);
-            dl = acc;
+                    for (int k = 0; k < VEC; ++k) acc += exp_e(x[u][k] - mn);
+                dl = acc;
+            }
             ml = mn;
             // candidates
             // every wave of the workgroup runs every tile of the segment (v0,
@@ -1331,7 +1348,7 @@ __global__ void __launch_bounds__(W * 64)
                 out_i);
             if constexpr (!SPLIT) {
                 if (lane < K) {
-                    probs[row * K + lane] = exp_e(out_v - t.m) * rcp(t.d);
+                    probs[row * K + lane] = select ? out_v : exp_e(out_v - t.m) * rcp(t.d);
                     idx[row * K + lane] = out_i;
                 }
             } else {

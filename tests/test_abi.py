@@ -26,12 +26,13 @@ def ons():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:os|safe)_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:os|safe|naive)_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["os_softmax_forward", "os_softmax_topk", "safe_softmax_forward", "os_softmax_stats",
+              "naive_softmax_forward", "os_topk_select", "os_softmax_forward_split_noalloc",
               "os_softmax_forward_lse", "os_softmax_forward_split", "os_softmax_forward_workspace_bytes",
               "os_forward_split_plan", "os_device_copy_rows", "os_softmax_topk_ex", "os_last_error", "os_softmax_forward_tuned", "os_forward_plan", "os_device_copy", "os_version"]:
         assert n in names
@@ -74,7 +75,7 @@ FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced (validati
     ((None, None, 4, 0, BF16), 0),            # empty rows: no-op
 ])
 def test_forward_and_safe_validation(L, ons, args, code):
-    for fn in (L.os_softmax_forward, L.safe_softmax_forward):
+    for fn in (L.os_softmax_forward, L.safe_softmax_forward, L.naive_softmax_forward):
         rc = fn(*args, None)
         assert rc == code, (fn.__name__, ons.os_last_error())
         if code != 0:
@@ -135,6 +136,16 @@ def test_lse_validation(L):
 ])
 def test_topk_validation(L, args, code):
     assert L.os_softmax_topk(*args, None) == code
+    x, p, i, rows, cols, K = args
+    assert L.os_topk_select(x, F32, p, i, rows, cols, K, None) == code
+
+
+def test_topk_select_validation(L):
+    f = L.os_topk_select
+    assert f(FAKE, 7, FAKE, FAKE, 4, 100, 8, None) == EINVAL        # unknown dtype
+    assert f(FAKE + 1, BF16, FAKE, FAKE, 4, 100, 8, None) == EINVAL  # bf16 input not 2-byte aligned
+    assert f(FAKE, BF16, FAKE + 2, FAKE, 4, 100, 8, None) == EINVAL  # misaligned values
+    assert f(None, BF16, None, None, 0, 100, 8, None) == 0           # no rows
 
 
 def test_topk_split_validation(L, ons):
