@@ -15,7 +15,12 @@ duration from HIP events recorded on the launch stream; ``traffic`` is the
 HBM bytes per launch from rocprofv3 counters (``profiles/``), or null when the
 kernels changed since the counters were taken.  ``cpu_baseline`` is the CPU
 oracle timed on this host.  Comparison legs on the same input: the three-pass
-safe-softmax baseline, the streaming two-pass kernel, and a plain copy.
+safe-softmax baseline, the unshifted two-pass baseline, the streaming two-pass
+kernel, and two copies.  ``exp_rate`` is the measured rate of the hardware
+exponential (the arithmetic ceiling beside HBM).  ``workloads`` times all five
+workloads in the launch configuration the parity tests check: kernel time,
+fraction of the HBM peak, rows/s, the same from a flushed cache, the section 5
+baselines, the fused top-K against its unfused pipelines, and the CPU oracle.
 """
 from __future__ import annotations
 
@@ -31,6 +36,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+CUS = 256           # MI355X compute units
+CLOCK_HZ = 2.4e9    # MI355X peak engine clock
 KERNEL_SOURCES = ["online_normalizer_amd/csrc/os_kernels.hpp", "online_normalizer_amd/csrc/os_device.hpp",
                   "online_normalizer_amd/csrc/os_abi.hip"]
 COUNTERS_FILE = "profiles/counters_softmax_fwd_4096x32000_f32.txt"
@@ -66,11 +73,15 @@ def load_traffic(launch_bytes_alg: float):
     return fetch + write, None
 
 
-def time_graph(fn, steps: int, warmup: int, stream):
-    """Capture `steps` calls of fn() in one HIP graph and time a single replay.
+def time_graph(fn, steps: int, warmup: int, stream, replays: int = 1):
+    """Capture `steps` calls of fn() in one HIP graph and time `replays`
+    replays of it, each bracketed by torch.cuda.synchronize().
 
-    Returns (wall seconds of the replay, average seconds per launch from HIP
-    events recorded on the stream around the replay)."""
+    Before the timed replays: `warmup` eager calls, then two untimed replays
+    (the first uploads the graph; the second runs right before the timed ones,
+    so that the GPU is not idle when they start).  Returns (wall seconds,
+    average seconds per launch) of the replay whose average launch is the
+    median, and the list of every replay's average launch."""
     import torch
     for _ in range(warmup):
         fn()
@@ -79,17 +90,23 @@ def time_graph(fn, steps: int, warmup: int, stream):
     with torch.cuda.graph(graph):
         for _ in range(steps):
             fn()
-    graph.replay()  # first replay uploads the graph
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
+    graph.replay()  # uploads the graph
     graph.replay()
-    end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end) * 1e-3 / steps
+    runs = []
+    for _ in range(replays):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        runs.append((wall, start.elapsed_time(end) * 1e-3 / steps))
+    order = sorted(range(len(runs)), key=lambda r: runs[r][1])
+    wall, avg = runs[order[len(order) // 2]]
+    return wall, avg, [a for _, a in runs]
 
 
 def time_launches(fn, steps: int, warmup: int, stream):
@@ -112,29 +129,172 @@ def time_launches(fn, steps: int, warmup: int, stream):
     return wall, per
 
 
-def cpu_baseline(x, bytes_per_row: float, min_cpu_s: float = 10.0, max_wall_s: float = 30.0):
-    """The oracle, as it stands, on every host core; whole-workload passes are
-    repeated until about ``min_cpu_s`` of CPU time has been spent."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_times(fn, reps: int):
+    """Wall seconds of `reps` calls of fn() (the oracle), and their median."""
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return sorted(times)[len(times) // 2], times
+
+
+def cpu_baseline(x, bytes_per_row: float, reps: int = 3):
+    """The oracle, as it stands (three-pass safe softmax in double), on every
+    host core the process may use: the median wall time of `reps` passes over
+    the whole workload."""
     import oracle
     orc = oracle.load()
     cores = len(os.sched_getaffinity(0))
     rows = x.shape[0]
-    passes, wall, cpu = 0, 0.0, 0.0
-    while passes == 0 or (cpu < min_cpu_s and wall < max_wall_s):
-        t0, c0 = time.perf_counter(), time.process_time()
-        orc.softmax(x, threads=cores)
-        wall += time.perf_counter() - t0
-        cpu += time.process_time() - c0
-        passes += 1
+    med, _ = oracle_times(lambda: orc.softmax(x, threads=cores), reps)
     return {
-        "value": round(passes * rows * bytes_per_row / wall / 1e9, 3),
+        "value": round(rows * bytes_per_row / med / 1e9, 3),
         "unit": "GB/s",
-        "rows_per_s": round(passes * rows / wall, 1),
+        "rows_per_s": round(rows / med, 1),
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{passes} pass(es) over all {rows} rows x {x.shape[1]} cols of the workload "
-                  f"(3-pass safe softmax in double): {cpu:.1f} s CPU over {wall:.2f} s wall",
+        "cpu_model": cpu_model(),
+        "sample": f"the whole workload, {rows} rows x {x.shape[1]} cols (3-pass safe softmax in double, "
+                  f"std::thread over rows): median of {reps} passes, {med:.3f} s wall each",
     }
+
+
+def exp_rate(ons, stream):
+    """Measured rate of the hardware exponential: 2048 workgroups (8 waves per
+    SIMD), 2048 rounds of one exponential + one fused multiply-add per chain."""
+    import torch
+    wgs, iters = 2048, 2048
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for chains, name in ((8, "independent"), (1, "dependent")):
+        _, avg, _ = time_graph(lambda: ons.os_bench_exp(out, wgs, iters, chains), 5, 2, stream, replays=3)
+        rate = wgs * 256 * iters * chains / avg
+        res[name] = {"Gexp_per_s": round(rate / 1e9, 1),
+                     "per_CU_per_clock": round(rate / (CUS * CLOCK_HZ), 2), "us": round(avg * 1e6, 2)}
+    return res
+
+
+def flushed_us(fn, stream, scratch, reps: int = 10):
+    """Median single launch with L2 and the Infinity Cache flushed first (a
+    1 GiB fill runs before each launch, outside the HIP events)."""
+    import torch
+    times = []
+    for _ in range(reps):
+        scratch.zero_()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) * 1e-3)
+    return sorted(times)[len(times) // 2] * 1e6
+
+
+def per_workload(ons, stream, exp_per_s: float, x2=None, y2=None):
+    """Every workload in the launch configuration the benchmark times: kernel
+    time (median of 3 graph replays of 20 launches), bandwidth on the
+    algorithmic bytes as a fraction of the 8 TB/s peak, rows/s, the same with
+    caches flushed, the [OS] section 5 baselines on the same input (3-pass
+    safe, unshifted 2-pass), and the CPU oracle on the whole workload (median
+    of 3 passes; workload 1: of 100, plus one thread)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    orc = oracle.load()
+    cores = len(os.sched_getaffinity(0))
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+
+    def gus(fn, reps=20):
+        _, avg, _ = time_graph(fn, reps, 3, stream, replays=3)
+        return avg * 1e6
+
+    table = {}
+    for n in (1, 2, 3, 4):
+        if n == 2 and x2 is not None:
+            xh, x, y = None, x2, y2
+        else:
+            xh = workloads.config(n)
+            x = (torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16) if xh.dtype == np.uint16
+                 else torch.from_numpy(xh)).cuda()
+            y = torch.empty_like(x)
+        rows, cols = x.shape
+        nb = rows * cols * x.element_size() * 2
+        t = gus(lambda: ons.os_softmax_forward(x, out=y), 200 if n == 1 else 20)
+        tf = flushed_us(lambda: ons.os_softmax_forward(x, out=y), stream, scratch)
+        ts = gus(lambda: ons.safe_softmax_forward(x, out=y))
+        tn = gus(lambda: ons.naive_softmax_forward(x, out=y))
+        e = {"rows": rows, "cols": cols, "dtype": str(x.dtype).replace("torch.", ""),
+             "algorithmic_bytes": nb, "kernel_us": round(t, 2), "GBs": round(nb / t / 1e3, 1),
+             "frac": round(nb / t / 1e3 / PEAK_HBM_GBS, 4), "rows_per_s": round(rows / t * 1e6, 1),
+             "flushed_us": round(tf, 2), "flushed_frac": round(nb / tf / 1e3 / PEAK_HBM_GBS, 4),
+             "safe_3pass_us": round(ts, 2), "naive_2pass_us": round(tn, 2),
+             "speedup_vs_safe_3pass": round(ts / t, 3)}
+        if xh is None:
+            xh = x.cpu().numpy()
+        if n == 1:
+            med, _ = oracle_times(lambda: orc.softmax(xh, threads=cores), 100)
+            med1, _ = oracle_times(lambda: orc.softmax(xh, threads=1), 100)
+            e["cpu_oracle"] = {"s": round(med, 6), "s_one_thread": round(med1, 6), "cores": cores,
+                               "rows_per_s": round(rows / med, 1), "GBs": round(nb / med / 1e9, 3)}
+        else:
+            med, _ = oracle_times(lambda: orc.softmax(xh, threads=cores), 3)
+            e["cpu_oracle"] = {"s": round(med, 4), "cores": cores, "rows_per_s": round(rows / med, 1),
+                               "GBs": round(nb / med / 1e9, 3)}
+        table[str(n)] = e
+        del x, y, xh
+    # workload 5: the fused top-K, its unfused pipelines, and the same logits in bf16
+    xh = workloads.config(5)
+    K = workloads.TOPK_K
+    x = torch.from_numpy(xh).cuda()
+    rows, cols = x.shape
+    nb = rows * cols * 4 + rows * K * 8
+    t = gus(lambda: ons.os_softmax_topk(x, K), 200)
+    tf = flushed_us(lambda: ons.os_softmax_topk(x, K), stream, scratch)
+    yt = torch.empty_like(x)
+    legs = {}
+    for name, fwd in (("unfused_online", ons.os_softmax_forward), ("unfused_safe", ons.safe_softmax_forward),
+                      ("unfused_naive", ons.naive_softmax_forward)):
+        def pipeline(fwd=fwd):
+            fwd(x, out=yt)
+            ons.os_topk_select(yt, K)
+        tu = gus(pipeline, 50)
+        tuf = flushed_us(pipeline, stream, scratch)
+        legs[name] = {"us": round(tu, 2), "fused_speedup": round(tu / t, 2), "flushed_us": round(tuf, 2),
+                      "fused_speedup_flushed": round(tuf / tf, 2)}
+    tsel = gus(lambda: ons.os_topk_select(x, K), 200)
+    xb = x.to(torch.bfloat16)
+    nb16 = rows * cols * 2 + rows * K * 8
+    tb = gus(lambda: ons.os_softmax_topk(xb, K), 200)
+    tbf = flushed_us(lambda: ons.os_softmax_topk(xb, K), stream, scratch)
+    floor_b = max(nb16 / PEAK_HBM_GBS / 1e3, rows * cols / exp_per_s * 1e6)  # us
+    med, _ = oracle_times(lambda: orc.topk(xh, K, threads=cores), 3)
+    table["5"] = {"rows": rows, "cols": cols, "dtype": "float32", "K": K, "algorithmic_bytes": nb,
+                  "kernel_us": round(t, 2), "GBs": round(nb / t / 1e3, 1),
+                  "frac": round(nb / t / 1e3 / PEAK_HBM_GBS, 4), "rows_per_s": round(rows / t * 1e6, 1),
+                  "flushed_us": round(tf, 2), "flushed_frac": round(nb / tf / 1e3 / PEAK_HBM_GBS, 4),
+                  "select_only_us": round(tsel, 2), **legs,
+                  "bf16": {"kernel_us": round(tb, 2), "algorithmic_bytes": nb16,
+                           "frac": round(nb16 / tb / 1e3 / PEAK_HBM_GBS, 4), "flushed_us": round(tbf, 2),
+                           "flushed_frac": round(nb16 / tbf / 1e3 / PEAK_HBM_GBS, 4),
+                           "floor_us_max_hbm_exp": round(floor_b, 2), "frac_vs_max_hbm_exp": round(floor_b / tb, 4)},
+                  "cpu_oracle": {"s": round(med, 4), "cores": cores, "rows_per_s": round(rows / med, 1)}}
+    del x, xb, yt, scratch
+    return table
 
 
 def main(argv=None) -> int:
@@ -142,13 +302,16 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replays", type=int, default=5,
+                    help="timed replays of the K-step graph; the median one is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
-                    help="time the steps as individual launches instead of one HIP graph replay")
+                    help="time the steps as individual launches instead of HIP graph replays")
     ap.add_argument("--no-compare", action="store_true", help="skip the comparison legs")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload section")
     ap.add_argument("--all-configs", metavar="FILE", default=None,
-                    help="also time every workload (forward, three-pass baseline, copy; top-K for the "
-                         "top-K workload) and write the table to FILE as JSON")
+                    help="also time the extended table (every workload, split, unaligned and router cases) "
+                         "and write it to FILE as JSON")
     ap.add_argument("--perf-map", metavar="FILE", default=None,
                     help="also time the forward over row lengths from 64 to 2^20 (16-byte aligned and not, "
                          "fp32 and bf16) and the top-K over batches, row lengths and K; write a text table to FILE")
@@ -159,7 +322,6 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import online_normalizer_amd as ons
@@ -181,8 +343,10 @@ def main(argv=None) -> int:
     if args.eager:
         wall, per = time_launches(step, args.steps, args.warmup, stream)
         avg = sum(per) / len(per)
+        replay_us = None
     else:
-        wall, avg = time_graph(step, args.steps, args.warmup, stream)
+        wall, avg, reps = time_graph(step, args.steps, args.warmup, stream, replays=args.replays)
+        replay_us = [round(a * 1e6, 2) for a in reps]
     value = bytes_alg * args.steps / wall / 1e9
     achieved = bytes_alg / avg / 1e9
     traffic, traffic_note = load_traffic(bytes_alg)
@@ -218,8 +382,10 @@ def main(argv=None) -> int:
             "algorithmic_bytes": bytes_alg,
         },
         "timing": ("K steps as individual launches, HIP events around each" if args.eager else
-                   "K steps captured in one HIP graph, one replay timed; HIP events around the replay "
-                   "give the average launch duration"),
+                   f"K steps captured in one HIP graph, replayed twice untimed, then {args.replays} timed "
+                   "replays (each bracketed by synchronize, HIP events on the launch stream); the replay "
+                   "with the median average launch is reported"),
+        "replays_kernel_us": replay_us,
         "kernel_us_eager_median": round(eager_us, 2),
     }
     if traffic_note:
@@ -227,39 +393,31 @@ def main(argv=None) -> int:
 
     if not args.no_compare:
         legs = {}
-        _, per3 = time_launches(lambda: ons.safe_softmax_forward(x, out=y), 20, 3, stream)
-        a3 = sum(per3) / len(per3)
-        legs["safe_3pass"] = {"kernel_us": round(a3 * 1e6, 2), "effective_GBs": round(bytes_alg / a3 / 1e9, 2)}
-        _, per2 = time_launches(lambda: ons.os_softmax_forward_tuned(x, 0, 0, 0, out=y), 20, 3, stream)
-        a2 = sum(per2) / len(per2)
-        legs["online_stream_2pass"] = {"kernel_us": round(a2 * 1e6, 2),
-                                       "effective_GBs": round(bytes_alg / a2 / 1e9, 2)}
-        _, perc = time_launches(lambda: ons.os_device_copy(x, y), 20, 3, stream)
-        ac = sum(perc) / len(perc)
+        for name, fn in (("safe_3pass", lambda: ons.safe_softmax_forward(x, out=y)),
+                         ("naive_2pass", lambda: ons.naive_softmax_forward(x, out=y)),
+                         ("online_stream_2pass", lambda: ons.os_softmax_forward_tuned(x, 0, 0, 0, out=y))):
+            _, a, _ = time_graph(fn, 20, 3, stream, replays=3)
+            legs[name] = {"kernel_us": round(a * 1e6, 2), "effective_GBs": round(bytes_alg / a / 1e9, 2)}
+        _, ac, _ = time_graph(lambda: ons.os_device_copy(x, y), 20, 3, stream, replays=3)
         legs["copy"] = {"kernel_us": round(ac * 1e6, 2), "GBs": round(bytes_alg / ac / 1e9, 2)}
         # the same copy with the forward's own access pattern (one 1024-lane
         # workgroup per 128 KB row, all loads before the stores)
-        _, perr = time_launches(lambda: ons.os_device_copy_rows(x, y), 20, 3, stream)
-        ar = sum(perr) / len(perr)
+        _, ar, _ = time_graph(lambda: ons.os_device_copy_rows(x, y), 20, 3, stream, replays=3)
         legs["copy_row_pattern"] = {"kernel_us": round(ar * 1e6, 2), "GBs": round(bytes_alg / ar / 1e9, 2)}
-        # the headline kernel with L2 / Infinity Cache flushed before each launch
         scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-        times = []
-        for _ in range(10):
-            scratch.zero_()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            ons.os_softmax_forward(x, out=y)
-            e.record(stream)
-            torch.cuda.synchronize()
-            times.append(s.elapsed_time(e) * 1e-3)
+        af = flushed_us(step, stream, scratch)
         del scratch
-        af = sorted(times)[len(times) // 2]
-        legs["online_flushed"] = {"kernel_us": round(af * 1e6, 2), "effective_GBs": round(bytes_alg / af / 1e9, 2)}
-        legs["speedup_vs_safe_3pass"] = round(a3 / avg, 3)
+        legs["online_flushed"] = {"kernel_us": round(af, 2), "effective_GBs": round(bytes_alg / af / 1e3, 2)}
+        legs["speedup_vs_safe_3pass"] = round(legs["safe_3pass"]["kernel_us"] / (avg * 1e6), 3)
+        legs["speedup_vs_naive_2pass"] = round(legs["naive_2pass"]["kernel_us"] / (avg * 1e6), 3)
         legs["pct_of_copy"] = round(100.0 * ac / avg, 2)
         legs["pct_of_row_pattern_copy"] = round(100.0 * ar / avg, 2)
         out["compare"] = legs
+
+    ex = exp_rate(ons, stream)
+    out["exp_rate"] = ex
+    if not args.no_workloads:
+        out["workloads"] = per_workload(ons, stream, ex["independent"]["Gexp_per_s"] * 1e9, x, y)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_host, cols * 8)
@@ -285,7 +443,7 @@ def perf_map(ons, stream) -> str:
     import torch
 
     def graph_us(fn):
-        _, avg = time_graph(fn, 20, 3, stream)
+        _, avg, _ = time_graph(fn, 20, 3, stream)
         return avg * 1e6
 
     lines = ["# Forward and fused top-K across shapes on MI355X (gfx950), from:",
@@ -340,7 +498,7 @@ def all_configs(ons, stream):
     events around each ("us_eager", which adds the launch ramp)."""
 
     def measure(fn, reps):
-        _, avg = time_graph(fn, reps, 5, stream)
+        _, avg, _ = time_graph(fn, reps, 5, stream)
         _, per = time_launches(fn, reps, 5, stream)
         return avg, sorted(per)[len(per) // 2]
 
@@ -414,12 +572,14 @@ def all_configs(ons, stream):
                           "us_flushed": round(tbf * 1e6, 2), "algorithmic_bytes": nb16}
     del xb
     # the unfused pipelines of the fusion comparison: softmax written out, then
-    # top-K over the probabilities (online: 2R+1W then 1R; safe: 3R+1W then 1R)
+    # top-K selection over the probabilities (online: 2R+1W then 1R; safe:
+    # 3R+1W then 1R; naive: 2R+1W then 1R)
     yt = torch.empty_like(xt)
-    for name, fwd in (("unfused_online", ons.os_softmax_forward), ("unfused_safe", ons.safe_softmax_forward)):
+    for name, fwd in (("unfused_online", ons.os_softmax_forward), ("unfused_safe", ons.safe_softmax_forward),
+                      ("unfused_naive", ons.naive_softmax_forward)):
         def pipeline(fwd=fwd):
             fwd(xt, out=yt)
-            ons.os_softmax_topk(yt, workloads.TOPK_K)
+            ons.os_topk_select(yt, workloads.TOPK_K)
         tu, tue = measure(pipeline, 100)
         tuf = flushed(pipeline)
         entry[name] = {"us": round(tu * 1e6, 2), "fused_speedup": round(tu / t, 2), "us_eager": round(tue * 1e6, 2),

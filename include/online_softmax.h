@@ -351,6 +351,23 @@ int os_device_copy(const void *src, void *dst, int64_t bytes, void *stream);
  */
 int os_device_copy_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes, void *stream);
 
+/*
+ * Microbenchmark of the hardware exponential (v_exp_f32), the arithmetic
+ * ceiling beside HBM bandwidth: every element of a fold costs one (the paper
+ * summary's section 3 counts the recurrence's extra work per element; "5.2
+ * Hiện thực và tối ưu CUDA Online Softmax", section 4.4, weighs the extra
+ * exponentials against the bytes saved).  `workgroups` 256-thread workgroups;
+ * every lane runs `iters` rounds of one exponential and one fused
+ * multiply-add on each of `chains` values (1: one dependent chain, latency;
+ * 8: independent chains, throughput), so a launch performs
+ * workgroups * 256 * iters * chains exponentials.
+ *   out         [workgroups * 256] float, one result per lane (kept so that
+ *               no work is dropped; its values carry no meaning).
+ *   workgroups  1..2^20;  iters >= 1;  chains 1 or 8.
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_bench_exp(float *out, int64_t workgroups, int iters, int chains, void *stream);
+
 /* Message for the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call on the same thread. */
 const char *os_last_error(void);

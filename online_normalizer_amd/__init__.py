@@ -24,6 +24,7 @@ Entry points (same names as the C ABI):
   os_topk_select(x, K) -> (vals, idx)          top-K of the entries alone (the unfused pipelines' TopK)
   os_device_copy(src, dst)                     plain copy (bandwidth reference)
   os_device_copy_rows(src, dst)                copy with the row-per-workgroup pattern (reference)
+  os_bench_exp(out, workgroups, iters, chains) exponential-rate microbenchmark
   os_forward_plan(cols, dtype) -> (lanes_per_row, vecs_per_lane)
   os_last_error(), os_version()
 
@@ -44,6 +45,7 @@ __all__ = [
     "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan", "os_softmax_topk_ex",
     "os_softmax_forward_split", "os_softmax_forward_workspace_bytes", "os_forward_split_plan",
     "os_softmax_forward_split_noalloc", "OS_STATIC_SCRATCH_BYTES", "naive_softmax_forward", "os_topk_select",
+    "os_bench_exp",
 ]
 
 OS_OK, OS_EINVAL, OS_EUNSUPPORTED, OS_ELAUNCH = 0, -1, -2, -3
@@ -98,6 +100,7 @@ def _load() -> ctypes.CDLL:
         "os_topk_select": [vp, i32, vp, vp, i64, i64, i32, vp],
         "os_device_copy": [vp, vp, i64, vp],
         "os_device_copy_rows": [vp, vp, i64, i64, vp],
+        "os_bench_exp": [vp, i64, i32, i32, vp],
         "os_version": [],
         "os_softmax_topk_split": [vp, vp, vp, i64, i64, i32, i32, vp, i64, vp],
         "os_topk_plan": [i64, i64, i32],
@@ -383,6 +386,15 @@ def os_topk_select(x: torch.Tensor, K: int, vals: torch.Tensor | None = None,
            lib().os_topk_select(x.data_ptr(), _dtype_code(x), vals.data_ptr(), idx.data_ptr(), rows, cols, K,
                                 _stream(x)))
     return vals, idx
+
+
+def os_bench_exp(out: torch.Tensor, workgroups: int, iters: int, chains: int) -> torch.Tensor:
+    """Launch the exponential-rate microbenchmark (workgroups * 256 * iters *
+    chains exponentials); out: float32 with at least workgroups * 256 elements."""
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < workgroups * 256:
+        raise ValueError("out must be a float32 GPU tensor of at least workgroups * 256 elements")
+    _check("os_bench_exp", lib().os_bench_exp(out.data_ptr(), workgroups, iters, chains, _stream(out)))
+    return out
 
 
 def os_device_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:

@@ -1068,6 +1068,18 @@ int os_device_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     return launched(fn);
 }
 
+int os_bench_exp(float* out, int64_t workgroups, int iters, int chains, void* stream) {
+    const char* fn = "os_bench_exp";
+    if (chains != 1 && chains != 8) return fail(OS_EINVAL, "%s: chains must be 1 or 8", fn);
+    if (workgroups < 1 || workgroups > (int64_t(1) << 20) || iters < 1)
+        return fail(OS_EINVAL, "%s: workgroups must be in [1, 2^20] and iters >= 1", fn);
+    if (out == nullptr || !aligned(out, 4)) return fail(OS_EINVAL, "%s: out must be a 4-byte aligned pointer", fn);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(chains == 1 ? k_exp_rate<1> : k_exp_rate<8>, dim3(static_cast<uint32_t>(workgroups)), dim3(256),
+                       0, static_cast<hipStream_t>(stream), out, iters);
+    return launched(fn);
+}
+
 int os_device_copy_rows(const void* src, void* dst, int64_t rows, int64_t row_bytes, void* stream) {
     const char* fn = "os_device_copy_rows";
     if (rows < 0 || row_bytes < 0 || row_bytes % 16 != 0 || row_bytes > 131072)

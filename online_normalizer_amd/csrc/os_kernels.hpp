@@ -1837,4 +1837,29 @@ __global__ void __launch_bounds__(1024) k_copy_rows(const char* src, char* dst, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Rate of the hardware base-2 exponential (v_exp_f32), the second ceiling of
+// the per-element work beside HBM (every element of a fold costs one).  Each
+// lane runs `iters` rounds over CHAINS values; a round is one v_exp_f32 and
+// one fused multiply-add per value, v <- 2^v * 0.5 - 0.5, which keeps v in
+// [-0.15, 0.21).  CHAINS = 1: one dependent chain per lane (latency bound);
+// CHAINS = 8: eight independent chains (throughput).  One float per lane is
+// written so that no round can be dropped.
+// ---------------------------------------------------------------------------
+template <int CHAINS>
+__global__ void __launch_bounds__(256) k_exp_rate(float* out, int iters) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    float v[CHAINS];
+#pragma unroll
+    for (int c = 0; c < CHAINS; ++c) v[c] = static_cast<float>(gid & 255) * (1.0f / 1024.0f) + c * (1.0f / 64.0f) - 0.25f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < CHAINS; ++c) v[c] = fmaf(__builtin_amdgcn_exp2f(v[c]), 0.5f, -0.5f);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CHAINS; ++c) s += v[c];
+    out[gid] = s;
+}
+
 }  // namespace onorm

@@ -228,6 +228,16 @@ def test_forward_split_noalloc_validation(L, ons):
     assert f(None, None, 10, 0, F32, 4, None) == 0               # empty rows
 
 
+def test_bench_exp_validation(L):
+    f = L.os_bench_exp
+    assert f(FAKE, 4, 10, 2, None) == EINVAL          # chains 1 or 8
+    assert f(FAKE, 0, 10, 8, None) == EINVAL          # no workgroups
+    assert f(FAKE, (1 << 20) + 1, 10, 8, None) == EINVAL
+    assert f(FAKE, 4, 0, 8, None) == EINVAL           # no rounds
+    assert f(None, 4, 10, 8, None) == EINVAL
+    assert f(FAKE + 2, 4, 10, 8, None) == EINVAL      # misaligned
+
+
 def test_copy_validation(L):
     assert L.os_device_copy(FAKE, FAKE + 4096, 20, None) == EINVAL      # not a multiple of 16
     assert L.os_device_copy(FAKE + 4, FAKE + 4096, 32, None) == EINVAL  # misaligned

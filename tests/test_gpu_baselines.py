@@ -161,3 +161,23 @@ def test_unfused_pipelines_workload5(ons, orc):
         # where the probabilities are separated, the columns are the fused ones
         assert np.array_equal(i[separated], ir[separated]), name
     assert separated.sum() >= 200  # most rows; the rest hold duplicated maxima
+
+
+# -- the exponential-rate microbenchmark -----------------------------------------------
+
+@pytest.mark.parametrize("chains", [1, 8])
+def test_bench_exp_computes_its_recurrence(ons, chains):
+    """Every lane's result is the recurrence v <- 2^v / 2 - 1/2 run `iters`
+    times from its start value (numpy in float64; the hardware exponential is
+    within a few ulp, and the map contracts, so errors stay ~1e-6)."""
+    wgs, iters = 3, 50
+    out = torch.full((wgs * 256,), np.nan, dtype=torch.float32, device="cuda")
+    say(f"os_bench_exp chains={chains}")
+    ons.os_bench_exp(out, wgs, iters, chains)
+    torch.cuda.synchronize()
+    gid = np.arange(wgs * 256)
+    v = np.stack([(gid & 255) / 1024.0 + c / 64.0 - 0.25 for c in range(chains)])
+    for _ in range(iters):
+        v = np.exp2(v) * 0.5 - 0.5
+    ref = v.sum(axis=0)
+    assert np.max(np.abs(to_host(out).astype(np.float64) - ref)) <= 1e-5 * chains
