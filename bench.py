@@ -277,6 +277,11 @@ def per_workload(ons, stream, exp_per_s: float, x2=None, y2=None):
         legs[name] = {"us": round(tu, 2), "fused_speedup": round(tu / t, 2), "flushed_us": round(tuf, 2),
                       "fused_speedup_flushed": round(tuf / tf, 2)}
     tsel = gus(lambda: ons.os_topk_select(x, K), 200)
+    # the read-only reference over the same bytes: the ceiling of a kernel
+    # that only reads this much
+    sink = torch.empty(4 * 2048, dtype=torch.float32, device="cuda")
+    trd = gus(lambda: ons.os_device_read(x, sink), 200)
+    trdf = flushed_us(lambda: ons.os_device_read(x, sink), stream, scratch)
     xb = x.to(torch.bfloat16)
     nb16 = rows * cols * 2 + rows * K * 8
     tb = gus(lambda: ons.os_softmax_topk(xb, K), 200)
@@ -287,7 +292,10 @@ def per_workload(ons, stream, exp_per_s: float, x2=None, y2=None):
                   "kernel_us": round(t, 2), "GBs": round(nb / t / 1e3, 1),
                   "frac": round(nb / t / 1e3 / PEAK_HBM_GBS, 4), "rows_per_s": round(rows / t * 1e6, 1),
                   "flushed_us": round(tf, 2), "flushed_frac": round(nb / tf / 1e3 / PEAK_HBM_GBS, 4),
-                  "select_only_us": round(tsel, 2), **legs,
+                  "select_only_us": round(tsel, 2),
+                  "read_only_reference": {"us": round(trd, 2), "flushed_us": round(trdf, 2),
+                                          "frac_of_it": round(trd / t, 4), "flushed_frac_of_it": round(trdf / tf, 4)},
+                  **legs,
                   "bf16": {"kernel_us": round(tb, 2), "algorithmic_bytes": nb16,
                            "frac": round(nb16 / tb / 1e3 / PEAK_HBM_GBS, 4), "flushed_us": round(tbf, 2),
                            "flushed_frac": round(nb16 / tbf / 1e3 / PEAK_HBM_GBS, 4),

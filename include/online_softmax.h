@@ -341,6 +341,18 @@ int os_topk_select(const void *in, int dtype, float *vals, int32_t *idx, int64_t
 int os_device_copy(const void *src, void *dst, int64_t bytes, void *stream);
 
 /*
+ * Plain device read of `bytes` bytes with 128-bit accesses (4 KiB tiles,
+ * 256-thread workgroups striding over them, at most 2048 workgroups): the
+ * read-only bandwidth reference for kernels that only read, such as the fused
+ * top-K.  src 16-byte aligned, bytes a multiple of 16.
+ *   sink         device floats receiving one sum per wave (values carry no
+ *                meaning; they keep the loads from being dropped).
+ *   sink_floats  capacity of sink: at least 4 * min(2048, ceil(bytes / 4096)).
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_device_read(const void *src, int64_t bytes, float *sink, int64_t sink_floats, void *stream);
+
+/*
  * Device copy of `rows` rows of `row_bytes` bytes each with the access pattern
  * of the register-resident forward on rows up to 128 KiB: one 1024-lane
  * workgroup per row, eight 16-byte vectors per lane, every load of a row

@@ -25,6 +25,7 @@ Entry points (same names as the C ABI):
   os_device_copy(src, dst)                     plain copy (bandwidth reference)
   os_device_copy_rows(src, dst)                copy with the row-per-workgroup pattern (reference)
   os_bench_exp(out, workgroups, iters, chains) exponential-rate microbenchmark
+  os_device_read(src, sink)                    plain read (read-only bandwidth reference)
   os_forward_plan(cols, dtype) -> (lanes_per_row, vecs_per_lane)
   os_last_error(), os_version()
 
@@ -45,7 +46,7 @@ __all__ = [
     "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan", "os_softmax_topk_ex",
     "os_softmax_forward_split", "os_softmax_forward_workspace_bytes", "os_forward_split_plan",
     "os_softmax_forward_split_noalloc", "OS_STATIC_SCRATCH_BYTES", "naive_softmax_forward", "os_topk_select",
-    "os_bench_exp",
+    "os_bench_exp", "os_device_read",
 ]
 
 OS_OK, OS_EINVAL, OS_EUNSUPPORTED, OS_ELAUNCH = 0, -1, -2, -3
@@ -101,6 +102,7 @@ def _load() -> ctypes.CDLL:
         "os_device_copy": [vp, vp, i64, vp],
         "os_device_copy_rows": [vp, vp, i64, i64, vp],
         "os_bench_exp": [vp, i64, i32, i32, vp],
+        "os_device_read": [vp, i64, vp, i64, vp],
         "os_version": [],
         "os_softmax_topk_split": [vp, vp, vp, i64, i64, i32, i32, vp, i64, vp],
         "os_topk_plan": [i64, i64, i32],
@@ -395,6 +397,16 @@ def os_bench_exp(out: torch.Tensor, workgroups: int, iters: int, chains: int) ->
         raise ValueError("out must be a float32 GPU tensor of at least workgroups * 256 elements")
     _check("os_bench_exp", lib().os_bench_exp(out.data_ptr(), workgroups, iters, chains, _stream(out)))
     return out
+
+
+def os_device_read(src: torch.Tensor, sink: torch.Tensor) -> torch.Tensor:
+    """Read all of src (a plain read, the read-only bandwidth reference); sink:
+    float32, at least 4 * min(2048, ceil(bytes / 4096)) elements."""
+    if sink.dtype != torch.float32 or not sink.is_cuda:
+        raise ValueError("sink must be a float32 GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    _check("os_device_read", lib().os_device_read(src.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), _stream(src)))
+    return sink
 
 
 def os_device_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:

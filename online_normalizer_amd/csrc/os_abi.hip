@@ -457,6 +457,10 @@ int run_rows(const char* fn, const void* in, void* out, RowStats stats, int64_t 
 
 namespace {
 
+// Workgroups of the read reference (8 per CU; on a 131 MB read this pattern
+// measured fastest of the tile and row patterns tried, cold and warm).
+constexpr int64_t kReadGrid = 2048;
+
 // The forward with one workgroup (group) per row: the plan os_softmax_forward uses.
 int forward_unsplit(const char* fn, const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
     int lpr = 0, vpl = 0;
@@ -1077,6 +1081,22 @@ int os_bench_exp(float* out, int64_t workgroups, int iters, int chains, void* st
     (void)hipGetLastError();
     hipLaunchKernelGGL(chains == 1 ? k_exp_rate<1> : k_exp_rate<8>, dim3(static_cast<uint32_t>(workgroups)), dim3(256),
                        0, static_cast<hipStream_t>(stream), out, iters);
+    return launched(fn);
+}
+
+int os_device_read(const void* src, int64_t bytes, float* sink, int64_t sink_floats, void* stream) {
+    const char* fn = "os_device_read";
+    if (bytes < 0 || bytes % 16 != 0) return fail(OS_EINVAL, "%s: bytes must be a non-negative multiple of 16", fn);
+    if (bytes == 0) return ok();
+    if (src == nullptr || sink == nullptr) return fail(OS_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(src, 16) || !aligned(sink, 4)) return fail(OS_EINVAL, "%s: src must be 16-byte and sink 4-byte aligned", fn);
+    const int64_t tiles = (bytes + 4095) / 4096;
+    const int grid = static_cast<int>(tiles < kReadGrid ? tiles : kReadGrid);
+    if (sink_floats < static_cast<int64_t>(grid) * 4)
+        return fail(OS_EINVAL, "%s: sink holds %lld floats, needs %lld", fn, (long long)sink_floats, (long long)grid * 4);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_read, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), static_cast<const char*>(src),
+                       bytes, sink);
     return launched(fn);
 }
 

@@ -1818,6 +1818,26 @@ __global__ void __launch_bounds__(256) k_copy(const char* src, char* dst, int64_
 }
 
 // ---------------------------------------------------------------------------
+// Plain 128-bit read (the read-only bandwidth reference, for kernels that only
+// read, such as the fused top-K): each thread reads one 16-byte vector per
+// 4 KiB tile, 256-thread workgroups striding over the tiles; each wave writes
+// one float (its sum) to sink[workgroup * 4 + wave], so no load is dropped.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_read(const char* src, int64_t bytes, float* sink) {
+    const uint32_t off = threadIdx.x * 16u;
+    float acc = 0.0f;
+    for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * 4096; t0 < bytes; t0 += static_cast<int64_t>(gridDim.x) * 4096) {
+        const int64_t left = bytes - t0;
+        const Buf bs(src + t0, static_cast<uint32_t>(left < 4096 ? left : 4096));
+        float x[4];
+        Elt<false>::unpack(bs.load16<true>(off), x);
+        acc += (x[0] + x[1]) + (x[2] + x[3]);
+    }
+    acc = wave_sum(acc);
+    if ((threadIdx.x & (kWave - 1)) == 0) sink[static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave] = acc;
+}
+
+// ---------------------------------------------------------------------------
 // Copy with the register-resident forward's access pattern on rows of up to
 // 128 KiB: one 1024-lane workgroup per row, 8 vectors per lane (slot
 // v * 1024 + lane), every load issued before any store.  It is the bandwidth

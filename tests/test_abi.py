@@ -238,6 +238,17 @@ def test_bench_exp_validation(L):
     assert f(FAKE + 2, 4, 10, 8, None) == EINVAL      # misaligned
 
 
+def test_read_validation(L):
+    f = L.os_device_read
+    assert f(FAKE, 20, FAKE, 8192, None) == EINVAL          # not a multiple of 16
+    assert f(FAKE + 4, 32, FAKE, 8192, None) == EINVAL      # misaligned source
+    assert f(None, 32, FAKE, 8192, None) == EINVAL
+    assert f(FAKE, 32, None, 8192, None) == EINVAL
+    assert f(FAKE, 1 << 30, FAKE, 8191, None) == EINVAL     # sink too small (2048 workgroups x 4)
+    assert f(FAKE, 8192, FAKE, 7, None) == EINVAL           # 2 tiles need 8 floats
+    assert f(None, 0, None, 0, None) == 0                   # nothing to read
+
+
 def test_copy_validation(L):
     assert L.os_device_copy(FAKE, FAKE + 4096, 20, None) == EINVAL      # not a multiple of 16
     assert L.os_device_copy(FAKE + 4, FAKE + 4096, 32, None) == EINVAL  # misaligned

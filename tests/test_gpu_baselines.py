@@ -181,3 +181,15 @@ def test_bench_exp_computes_its_recurrence(ons, chains):
         v = np.exp2(v) * 0.5 - 0.5
     ref = v.sum(axis=0)
     assert np.max(np.abs(to_host(out).astype(np.float64) - ref)) <= 1e-5 * chains
+
+
+def test_device_read_sums(ons):
+    """The read reference reads every byte: its per-wave sums add up to the sum
+    of the input (small integers, exact in fp32), also with a partial last tile."""
+    for n in (4, 1 << 20, (1 << 22) + 12, 10 << 20):
+        src = torch.arange(n, device="cuda", dtype=torch.int64).remainder(7).float()
+        sink = torch.zeros(4 * 2048, device="cuda")
+        say(f"os_device_read {n * 4} bytes")
+        ons.os_device_read(src, sink)
+        torch.cuda.synchronize()
+        assert float(sink.double().sum()) == float(src.double().sum())
