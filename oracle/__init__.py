@@ -28,6 +28,13 @@ with the passages it follows:
 * ``topk_select`` -- the K largest entries of each row and their columns by
   the same sort, returned as the entries themselves: the TopK stage of the
   unfused pipelines in the access table of section 4 of the paper summary.
+* ``attention`` -- O = softmax(scale Q K^T) V by the definition (section 7.1
+  of the paper summary), optional causal mask, and the per-row logsumexp L =
+  m + log(l) ("6.2 FlashAttention V2 chi tiết", sections 5, 6.1, 7.1), for
+  bf16 Q, K, V of shape [heads, n, d].
+* ``attention_tiled`` -- the same by the tiled (m, l, o~) recurrence with
+  delayed rescaling (section 7.2.3 of the paper summary; "6.2 ...", sections
+  3.2 and 6.1), tiles of b keys.
 
 Rows are independent, so the wrappers may split a batch of rows over host
 threads (each thread runs the same sequential C code on its own rows).
@@ -87,6 +94,12 @@ class Oracle:
             fn = getattr(lib, name)
             fn.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
             fn.restype = ctypes.c_int
+        lib.oracle_attention_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int, i64,
+                                              vp, vp, vp]
+        lib.oracle_attention_bf16.restype = ctypes.c_int
+        lib.oracle_attention_tiled_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
+                                                    i64, i64, vp, vp]
+        lib.oracle_attention_tiled_bf16.restype = ctypes.c_int
         for name in ("oracle_naive_softmax_f32", "oracle_naive_softmax_bf16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp, i64, i64, vp]
@@ -235,6 +248,53 @@ class Oracle:
 
         self._run_rows(part, rows, threads)
         return probs, idx
+
+
+    # -- attention -----------------------------------------------------------
+    @staticmethod
+    def _attn_args(q, k, v, causal, q_off):
+        q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+        for a in (q, k, v):
+            if a.dtype != np.uint16 or a.ndim != 3:
+                raise TypeError("q, k, v must be uint16 (bf16 bit patterns) of shape [heads, n, d]")
+        heads, nq, d = q.shape
+        if k.shape != v.shape or k.shape[0] != heads or k.shape[2] != d:
+            raise ValueError("k and v must be [heads, nk, d] with q's heads and d")
+        if causal and q_off + nq > k.shape[1]:
+            raise ValueError("causal attention needs q_off + nq <= nk")
+        return q, k, v, heads, nq, k.shape[1], d
+
+    def attention(self, q, k, v, scale: float, causal: bool = False, q_off: int = 0, threads: int = 1,
+                  want_abs: bool = False):
+        """(O, L[, O_abs]) in double: O [heads, nq, d], L [heads, nq]; q holds
+        query rows q_off .. q_off + nq - 1 of each head.  O_abs = the same
+        weights applied to |V|."""
+        q, k, v, heads, nq, nk, d = self._attn_args(q, k, v, causal, q_off)
+        o = np.empty((heads, nq, d), dtype=np.float64)
+        lse = np.empty((heads, nq), dtype=np.float64)
+        oabs = np.empty((heads, nq, d), dtype=np.float64) if want_abs else None
+        fn = self.lib.oracle_attention_bf16
+
+        def part(h0, h1):
+            n = h1 - h0
+            return fn(ctypes.c_void_p(q[h0:].ctypes.data), ctypes.c_void_p(k[h0:].ctypes.data),
+                      ctypes.c_void_p(v[h0:].ctypes.data), n, nq, nk, d, float(scale), int(bool(causal)), q_off,
+                      ctypes.c_void_p(o[h0:].ctypes.data), ctypes.c_void_p(lse[h0:].ctypes.data),
+                      None if oabs is None else ctypes.c_void_p(oabs[h0:].ctypes.data))
+
+        if heads:
+            self._run_rows(part, heads, threads)
+        return (o, lse, oabs) if want_abs else (o, lse)
+
+    def attention_tiled(self, q, k, v, scale: float, tile: int, causal: bool = False, q_off: int = 0):
+        q, k, v, heads, nq, nk, d = self._attn_args(q, k, v, causal, q_off)
+        o = np.empty((heads, nq, d), dtype=np.float64)
+        lse = np.empty((heads, nq), dtype=np.float64)
+        rc = self.lib.oracle_attention_tiled_bf16(_ptr(q), _ptr(k), _ptr(v), heads, nq, nk, d, float(scale),
+                                                  int(bool(causal)), q_off, tile, _ptr(o), _ptr(lse))
+        if rc != 0:
+            raise RuntimeError(f"oracle call failed with status {rc}")
+        return o, lse
 
 
 _DEFAULT: Oracle | None = None

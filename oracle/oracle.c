@@ -28,6 +28,17 @@
  *            of the unfused pipelines reads the probabilities and keeps the K
  *            largest; here the K largest entries of any row, returned as the
  *            entries themselves (no exponential, no normaliser).
+ *   [ATTN]   the paper summary, section 7.1: O = softmax(Q K^T) V row by row
+ *            (the logits X = Q K^T, A = softmax(X) over each row, O = A V),
+ *            with the scale 1/sqrt(d) and the causal mask (key j visible to
+ *            query i when j <= i) of "6.2 FlashAttention V2 chi tiết",
+ *            sections 5.1 and 6.1, and the per-row logsumexp L = m + log(l)
+ *            of its section 7.1.
+ *   [TILED]  the paper summary, section 7.2.3 (the tiled recurrence of
+ *            (m, d', o')) in the delayed-rescaling form of "6.2 FlashAttention
+ *            V2 chi tiết", sections 3.2 and 6.1: per tile of b keys,
+ *            m_new = max(m, rowmax S), l = e^{m - m_new} l + rowsum e^{S - m_new},
+ *            o~ = e^{m - m_new} o~ + e^{S - m_new} V, and O = o~ / l at the end.
  *
  * Readings taken where the pages are silent:
  *   - An element equal to -inf contributes e^{-inf} = 0 and leaves the state
@@ -48,6 +59,12 @@
  *     is the failure the page describes; the oracle does not guard it.
  *   - Selection orders entries like the top-K, (value descending, index
  *     ascending); rows holding NaN have no specified order.
+ *   - Attention takes bf16 Q, K, V (widened exactly) laid out [heads, n, d],
+ *     logits s_ij = scale * sum_k Q[i,k] K[j,k] in double; `scale` is passed
+ *     in (1/sqrt(d) on the pages).  The causal mask needs as many queries as
+ *     keys and hides key j from query i when j > i, so no row is fully
+ *     masked.  `oabs` (optional) receives sum_j a_ij |V[j,:]|, the same
+ *     weights on |V|: the scale of the rounding error of O.
  *
  * Every floating-point step is IEEE double with no reassociation: build with
  * -ffp-contract=off and without -ffast-math.
@@ -432,5 +449,166 @@ int oracle_topk_select_bf16(const uint16_t *x, int64_t rows, int64_t cols, int K
     }
     free(buf);
     free(order);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* [ATTN] O = softmax(scale * Q K^T) V, row by row, by the definition:     */
+/* the row of logits, its maximum, the sum of e^{s - m}, the weights       */
+/* a_j = e^{s_j - m} / l, then O[i,:] = sum_j a_j V[j,:];                 */
+/* L[i] = m + log(l).                                                      */
+/* ---------------------------------------------------------------------- */
+static void widen_mat_bf16(const uint16_t *src, int64_t n, double *dst)
+{
+    for (int64_t j = 0; j < n; ++j)
+        dst[j] = bf16_bits_to_double(src[j]);
+}
+
+/* q [heads, nq, d], k and v [heads, nk, d] (bf16 bits); o [heads, nq, d],
+ * lse [heads, nq] and oabs [heads, nq, d] (double; lse and oabs may be NULL).
+ * The nq query rows are rows q_off .. q_off + nq - 1 of each head (so a test
+ * may take a subset of rows); with `causal`, query row r sees keys j <= r,
+ * which needs q_off + nq <= nk.  Returns 0, -1 on allocation failure, -2 for
+ * bad sizes. */
+int oracle_attention_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t heads, int64_t nq,
+                          int64_t nk, int64_t d, double scale, int causal, int64_t q_off, double *o, double *lse,
+                          double *oabs)
+{
+    if (heads < 0 || nq < 0 || nk < 1 || d < 1 || q_off < 0 || (causal && q_off + nq > nk))
+        return -2;
+    double *qr = (double *)malloc((size_t)d * sizeof(double));
+    double *kv = (double *)malloc((size_t)(nk * d) * sizeof(double));
+    double *vv = (double *)malloc((size_t)(nk * d) * sizeof(double));
+    double *s = (double *)malloc((size_t)nk * sizeof(double));
+    double *a = (double *)malloc((size_t)nk * sizeof(double));
+    if (!qr || !kv || !vv || !s || !a) {
+        free(qr);
+        free(kv);
+        free(vv);
+        free(s);
+        free(a);
+        return -1;
+    }
+    for (int64_t h = 0; h < heads; ++h) {
+        widen_mat_bf16(k + h * nk * d, nk * d, kv);
+        widen_mat_bf16(v + h * nk * d, nk * d, vv);
+        for (int64_t i = 0; i < nq; ++i) {
+            widen_mat_bf16(q + (h * nq + i) * d, d, qr);
+            const int64_t nvis = causal ? q_off + i + 1 : nk; /* keys 0 .. nvis-1 are visible */
+            /* logits */
+            for (int64_t j = 0; j < nvis; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += qr[c] * kv[j * d + c];
+                s[j] = scale * dot;
+            }
+            /* softmax of the row: maximum, sum, weights */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nvis; ++j)
+                if (s[j] > m)
+                    m = s[j];
+            double l = 0.0;
+            for (int64_t j = 0; j < nvis; ++j)
+                l += exp(s[j] - m);
+            for (int64_t j = 0; j < nvis; ++j)
+                a[j] = exp(s[j] - m) / l;
+            /* O = A V */
+            double *orow = o + (h * nq + i) * d;
+            double *arow = oabs ? oabs + (h * nq + i) * d : NULL;
+            for (int64_t c = 0; c < d; ++c)
+                orow[c] = 0.0;
+            if (arow)
+                for (int64_t c = 0; c < d; ++c)
+                    arow[c] = 0.0;
+            for (int64_t j = 0; j < nvis; ++j) {
+                for (int64_t c = 0; c < d; ++c)
+                    orow[c] += a[j] * vv[j * d + c];
+                if (arow)
+                    for (int64_t c = 0; c < d; ++c)
+                        arow[c] += a[j] * fabs(vv[j * d + c]);
+            }
+            if (lse)
+                lse[h * nq + i] = m + log(l);
+        }
+    }
+    free(qr);
+    free(kv);
+    free(vv);
+    free(s);
+    free(a);
+    return 0;
+}
+
+/* [TILED] the same result by the pages' tiled recurrence, tiles of `tile`
+ * keys in order, the output kept unnormalised and divided once at the end.
+ * The state starts at (m, l, o~) = (-inf, 0, 0).  Same arguments as
+ * oracle_attention_bf16 (no oabs). */
+int oracle_attention_tiled_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t heads, int64_t nq,
+                                int64_t nk, int64_t d, double scale, int causal, int64_t q_off, int64_t tile,
+                                double *o, double *lse)
+{
+    if (heads < 0 || nq < 0 || nk < 1 || d < 1 || tile < 1 || q_off < 0 || (causal && q_off + nq > nk))
+        return -2;
+    double *qr = (double *)malloc((size_t)d * sizeof(double));
+    double *kv = (double *)malloc((size_t)(nk * d) * sizeof(double));
+    double *vv = (double *)malloc((size_t)(nk * d) * sizeof(double));
+    double *s = (double *)malloc((size_t)tile * sizeof(double));
+    double *acc = (double *)malloc((size_t)d * sizeof(double));
+    if (!qr || !kv || !vv || !s || !acc) {
+        free(qr);
+        free(kv);
+        free(vv);
+        free(s);
+        free(acc);
+        return -1;
+    }
+    for (int64_t h = 0; h < heads; ++h) {
+        widen_mat_bf16(k + h * nk * d, nk * d, kv);
+        widen_mat_bf16(v + h * nk * d, nk * d, vv);
+        for (int64_t i = 0; i < nq; ++i) {
+            widen_mat_bf16(q + (h * nq + i) * d, d, qr);
+            const int64_t nvis = causal ? q_off + i + 1 : nk;
+            double m = -INFINITY, l = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                acc[c] = 0.0;
+            for (int64_t j0 = 0; j0 < nvis; j0 += tile) {
+                const int64_t nt = (nvis - j0) < tile ? (nvis - j0) : tile;
+                /* the tile's logits and their maximum */
+                double m_tile = -INFINITY;
+                for (int64_t t = 0; t < nt; ++t) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c)
+                        dot += qr[c] * kv[(j0 + t) * d + c];
+                    s[t] = scale * dot;
+                    if (s[t] > m_tile)
+                        m_tile = s[t];
+                }
+                /* rescale the state to the new maximum, then add the tile */
+                const double m_new = m > m_tile ? m : m_tile;
+                const double alpha = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+                double rowsum = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    acc[c] *= alpha;
+                for (int64_t t = 0; t < nt; ++t) {
+                    const double p = exp(s[t] - m_new);
+                    rowsum += p;
+                    for (int64_t c = 0; c < d; ++c)
+                        acc[c] += p * vv[(j0 + t) * d + c];
+                }
+                l = alpha * l + rowsum;
+                m = m_new;
+            }
+            double *orow = o + (h * nq + i) * d;
+            for (int64_t c = 0; c < d; ++c)
+                orow[c] = acc[c] / l;
+            if (lse)
+                lse[h * nq + i] = m + log(l);
+        }
+    }
+    free(qr);
+    free(kv);
+    free(vv);
+    free(s);
+    free(acc);
     return 0;
 }

@@ -364,6 +364,89 @@ def pin_topk_select(o):
     assert np.array_equal(i, ref) and np.array_equal(v, np.take_along_axis(wide, ref, axis=1))
 
 
+def _attn_inputs(heads, nq, nk, d, seed, scale_q=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = workloads.f32_to_bf16_bits((rng.standard_normal((heads, nq, d)) * scale_q).astype(np.float32))
+    k = workloads.f32_to_bf16_bits(rng.standard_normal((heads, nk, d)).astype(np.float32))
+    v = workloads.f32_to_bf16_bits(rng.standard_normal((heads, nk, d)).astype(np.float32))
+    return q, k, v
+
+
+def _wide(b):
+    return workloads.bf16_bits_to_f32(b).astype(np.float64)
+
+
+def pin_attention_library(o):
+    """O = softmax(scale Q K^T) V and L = logsumexp by scipy in float64 (the
+    three stages of section 7.1 written with library routines), with and
+    without the causal mask; a subset of query rows equals those rows."""
+    from scipy.special import logsumexp, softmax
+    q, k, v = _attn_inputs(3, 37, 53, 24, seed=81)
+    scale = 1.0 / math.sqrt(24)
+    O, L = o.attention(q, k, v, scale)
+    X = np.einsum("hic,hjc->hij", _wide(q), _wide(k)) * scale
+    assert np.allclose(O, softmax(X, axis=-1) @ _wide(v), rtol=0, atol=1e-12)
+    assert np.allclose(L, logsumexp(X, axis=-1), rtol=1e-13, atol=0)
+    qs, ks, vs = _attn_inputs(2, 40, 40, 16, seed=82)
+    Oc, Lc = o.attention(qs, ks, vs, 0.3, causal=True)
+    Xc = np.einsum("hic,hjc->hij", _wide(qs), _wide(ks)) * 0.3
+    Xc = np.where(np.tril(np.ones((40, 40), dtype=bool)), Xc, -np.inf)  # key j hidden from query i when j > i
+    assert np.allclose(Oc, softmax(Xc, axis=-1) @ _wide(vs), rtol=0, atol=1e-12)
+    assert np.allclose(Lc, logsumexp(Xc, axis=-1), rtol=1e-13, atol=0)
+    Os, Ls = o.attention(np.ascontiguousarray(qs[:, 11:29]), ks, vs, 0.3, causal=True, q_off=11)
+    assert np.array_equal(Os, Oc[:, 11:29]) and np.array_equal(Ls, Lc[:, 11:29])
+
+
+def pin_attention_closed_forms(o):
+    """Equal keys: the mean of V; one key: V itself; V of ones: ones; two keys:
+    the logistic mix; causal row 0: V[0]; a huge scale: the argmax key's V;
+    the |V| weights equal O for V >= 0."""
+    bits = workloads.f32_to_bf16_bits
+    q, k, v = _attn_inputs(2, 9, 6, 8, seed=83)
+    k_eq = np.ascontiguousarray(np.broadcast_to(k[:, :1], k.shape))
+    O, L = o.attention(q, k_eq, v, 0.7)
+    assert np.allclose(O, _wide(v).mean(axis=1, keepdims=True), rtol=0, atol=1e-15)
+    s0 = 0.7 * np.einsum("hic,hc->hi", _wide(q), _wide(k)[:, 0])
+    assert np.allclose(L, s0 + math.log(6), rtol=1e-15, atol=1e-14)
+    O1, L1 = o.attention(q, k[:, :1].copy(), v[:, :1].copy(), 0.7)
+    assert np.array_equal(O1, np.broadcast_to(_wide(v)[:, :1], O1.shape))
+    assert np.allclose(L1, s0, rtol=1e-15, atol=0)
+    ones = bits(np.ones(v.shape, dtype=np.float32))
+    assert np.allclose(o.attention(q, k, ones, 0.7)[0], 1.0, rtol=0, atol=1e-15)
+    O2 = o.attention(q, k[:, :2].copy(), v[:, :2].copy(), 0.7)[0]
+    s = 0.7 * np.einsum("hic,hjc->hij", _wide(q), _wide(k)[:, :2])
+    w0 = 1.0 / (1.0 + np.exp(s[..., 1] - s[..., 0]))
+    ref = w0[..., None] * _wide(v)[:, None, 0] + (1 - w0)[..., None] * _wide(v)[:, None, 1]
+    assert np.allclose(O2, ref, rtol=0, atol=1e-14)
+    qc, kc, vc = _attn_inputs(1, 5, 5, 8, seed=84)
+    Oc = o.attention(qc, kc, vc, 0.5, causal=True)[0]
+    assert np.array_equal(Oc[0, 0], _wide(vc)[0, 0])
+    # a very large scale: all weight on the largest logit (distinct logits)
+    X = np.einsum("hic,hjc->hij", _wide(q), _wide(k))
+    Oh = o.attention(q, k, v, 1.0e6)[0]
+    assert np.allclose(Oh, np.take_along_axis(_wide(v), X.argmax(axis=-1)[..., None], axis=1), rtol=0, atol=1e-15)
+    va = bits(np.abs(workloads.bf16_bits_to_f32(v)))
+    Op, _, Oa = o.attention(q, k, va, 0.7, want_abs=True)
+    assert np.allclose(Oa, Op, rtol=1e-15, atol=0)
+    _, _, Oa2 = o.attention(q, k, v, 0.7, want_abs=True)
+    assert np.array_equal(Oa2, Oa)
+
+
+def pin_attention_tiled_recurrence(o):
+    """The tiled (m, l, o~) recurrence with delayed rescaling reaches the
+    definition for any tile size (the induction of section 3.2 carried to o),
+    with and without the mask, also when a later tile raises the maximum."""
+    q, k, v = _attn_inputs(2, 33, 70, 16, seed=85, scale_q=3.0)
+    k[:, 66] = workloads.f32_to_bf16_bits(np.full((2, 16), 4.0, dtype=np.float32))  # a late, large logit
+    for causal, nk in ((False, 70), (True, 33)):
+        kk, vv = np.ascontiguousarray(k[:, :nk]), np.ascontiguousarray(v[:, :nk])
+        O, L = o.attention(q, kk, vv, 0.25, causal=causal)
+        for tile in (1, 3, 16, 64, nk):
+            Ot, Lt = o.attention_tiled(q, kk, vv, 0.25, tile, causal=causal)
+            assert np.allclose(Ot, O, rtol=0, atol=1e-13), (causal, tile)
+            assert np.allclose(Lt, L, rtol=1e-14, atol=0), (causal, tile)
+
+
 PINS = [
     pin_two_shard_worked_example,
     pin_lesson_mock_vector,
@@ -381,6 +464,9 @@ PINS = [
     pin_logsumexp,
     pin_naive_softmax,
     pin_topk_select,
+    pin_attention_library,
+    pin_attention_closed_forms,
+    pin_attention_tiled_recurrence,
 ]
 
 

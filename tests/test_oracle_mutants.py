@@ -47,6 +47,14 @@ MUTANTS = [
      "        y[j] = exp(x[j] - row_max(x, n)) / d;"),
     ("naive_sum_skips_first", "    double d = 0.0;\n    for (int64_t j = 0; j < n; ++j)\n        d += exp(x[j]);",
      "    double d = 0.0;\n    for (int64_t j = 1; j < n; ++j)\n        d += exp(x[j]);"),
+    ("attention_drops_scale", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("attention_causal_hides_diagonal", "const int64_t nvis = causal ? q_off + i + 1 : nk; /* keys",
+     "const int64_t nvis = causal ? q_off + i : nk; /* keys"),
+    ("attention_weights_unnormalised", "a[j] = exp(s[j] - m) / l;", "a[j] = exp(s[j] - m);"),
+    ("attention_lse_drops_max", "            if (lse)\n                lse[h * nq + i] = m + log(l);\n        }\n    }\n    free(qr);\n    free(kv);\n    free(vv);\n    free(s);\n    free(a);",
+     "            if (lse)\n                lse[h * nq + i] = log(l);\n        }\n    }\n    free(qr);\n    free(kv);\n    free(vv);\n    free(s);\n    free(a);"),
+    ("tiled_forgets_rescale", "acc[c] *= alpha;", "acc[c] *= 1.0;"),
+    ("tiled_sum_not_rescaled", "l = alpha * l + rowsum;", "l = l + rowsum;"),
     ("select_returns_reversed", "        vals[k] = order[k].value;", "        vals[k] = order[K - 1 - k].value;"),
     ("select_returns_probability_like", "        vals[k] = order[k].value;", "        vals[k] = exp(order[k].value);"),
 ]
