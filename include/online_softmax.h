@@ -363,6 +363,36 @@ int os_device_read(const void *src, int64_t bytes, float *sink, int64_t sink_flo
  */
 int os_device_copy_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes, void *stream);
 
+/* longest query or key sequence accepted by os_attention_forward: 2^22 */
+#define OS_ATTN_MAX_SEQ (1LL << 22)
+
+/*
+ * Attention forward with the online normalizer: per head,
+ *     O = softmax(scale * Q K^T) V,   L = m + ln l  (the row's logsumexp),
+ * the self-attention of the paper summary's section 7.1, computed without
+ * forming Q K^T in memory by the tiled (m, l, o~) recurrence of its section
+ * 7.2.3 in the delayed-rescaling form of "6.2 FlashAttention V2 chi tiết"
+ * (sections 3.2 and 6.1: the running output is rescaled by e^{m_old - m_new}
+ * per key tile and divided by l once at the end; the logsumexp is the
+ * statistic of its section 7.1).  The two products run on the bf16 matrix
+ * cores with fp32 accumulation; the softmax state is fp32.
+ *   q        [heads, nq, head_dim] bf16 (raw 16-bit patterns).
+ *   k, v     [heads, nk, head_dim] bf16.
+ *   o        [heads, nq, head_dim] bf16, written (rounded to nearest-even).
+ *            o may be q itself; no other overlap.
+ *   lse      [heads, nq] float, or NULL: L = scale * max_j (q.k_j) + ln l.
+ *   head_dim 128 (the only one built).
+ *   scale    > 0 and finite (1/sqrt(head_dim) on the pages).
+ *   causal   non-zero: key j is hidden from query row i when j > i ("6.2
+ *            FlashAttention V2 chi tiết", section 5; key tiles wholly above
+ *            the diagonal are skipped); needs nq == nk.
+ *   heads == 0 or nq == 0 is a no-op; otherwise 1 <= nk, and nq, nk <=
+ *   OS_ATTN_MAX_SEQ.  q, k, v, o 16-byte aligned.
+ *   Returns OS_OK, OS_EINVAL, or OS_ELAUNCH.
+ */
+int os_attention_forward(const void *q, const void *k, const void *v, void *o, float *lse, int64_t heads,
+                         int64_t nq, int64_t nk, int head_dim, float scale, int causal, void *stream);
+
 /*
  * Microbenchmark of the hardware exponential (v_exp_f32), the arithmetic
  * ceiling beside HBM bandwidth: every element of a fold costs one (the paper

@@ -26,6 +26,8 @@ Entry points (same names as the C ABI):
   os_device_copy_rows(src, dst)                copy with the row-per-workgroup pattern (reference)
   os_bench_exp(out, workgroups, iters, chains) exponential-rate microbenchmark
   os_device_read(src, sink)                    plain read (read-only bandwidth reference)
+  os_attention_forward(q, k, v, scale=None, causal=False, out=None, lse=True) -> (o, lse)
+                                               attention forward on the online normalizer (bf16, d = 128)
   os_forward_plan(cols, dtype) -> (lanes_per_row, vecs_per_lane)
   os_last_error(), os_version()
 
@@ -46,7 +48,7 @@ __all__ = [
     "os_softmax_topk_split", "os_softmax_topk_workspace_bytes", "os_topk_plan", "os_softmax_topk_ex",
     "os_softmax_forward_split", "os_softmax_forward_workspace_bytes", "os_forward_split_plan",
     "os_softmax_forward_split_noalloc", "OS_STATIC_SCRATCH_BYTES", "naive_softmax_forward", "os_topk_select",
-    "os_bench_exp", "os_device_read",
+    "os_bench_exp", "os_device_read", "os_attention_forward",
 ]
 
 OS_OK, OS_EINVAL, OS_EUNSUPPORTED, OS_ELAUNCH = 0, -1, -2, -3
@@ -103,6 +105,7 @@ def _load() -> ctypes.CDLL:
         "os_device_copy_rows": [vp, vp, i64, i64, vp],
         "os_bench_exp": [vp, i64, i32, i32, vp],
         "os_device_read": [vp, i64, vp, i64, vp],
+        "os_attention_forward": [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_float, i32, vp],
         "os_version": [],
         "os_softmax_topk_split": [vp, vp, vp, i64, i64, i32, i32, vp, i64, vp],
         "os_topk_plan": [i64, i64, i32],
@@ -407,6 +410,32 @@ def os_device_read(src: torch.Tensor, sink: torch.Tensor) -> torch.Tensor:
     nbytes = src.numel() * src.element_size()
     _check("os_device_read", lib().os_device_read(src.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), _stream(src)))
     return sink
+
+
+def os_attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                         causal: bool = False, out: torch.Tensor | None = None,
+                         lse: bool = True) -> tuple[torch.Tensor, torch.Tensor | None]:
+    """O = softmax(scale Q K^T) V per head for bf16 q [..., nq, d], k and v
+    [..., nk, d] (contiguous; the leading dimensions are the heads), and the
+    per-row logsumexp (float32 [..., nq]) when lse is true.  scale defaults to
+    1/sqrt(d)."""
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() < 2:
+            raise TypeError("q, k, v must be contiguous bfloat16 GPU tensors [..., n, d]")
+    d = q.shape[-1]
+    if k.shape != v.shape or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != d:
+        raise ValueError("k and v must be [..., nk, d] with q's leading dimensions and d")
+    heads = q.numel() // max(1, q.shape[-2] * d) if q.shape[-2] * d else 0
+    nq, nk = q.shape[-2], k.shape[-2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = _out_like(q, out)
+    L = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if lse else None
+    _check("os_attention_forward",
+           lib().os_attention_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      None if L is None else L.data_ptr(), heads, nq, nk, d, float(scale),
+                                      int(bool(causal)), _stream(q)))
+    return out, L
 
 
 def os_device_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:

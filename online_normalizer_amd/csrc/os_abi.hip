@@ -13,6 +13,7 @@
 
 #include "../../include/online_softmax.h"
 #include "os_kernels.hpp"
+#include "os_attention.hpp"
 
 using namespace onorm;
 
@@ -1081,6 +1082,33 @@ int os_bench_exp(float* out, int64_t workgroups, int iters, int chains, void* st
     (void)hipGetLastError();
     hipLaunchKernelGGL(chains == 1 ? k_exp_rate<1> : k_exp_rate<8>, dim3(static_cast<uint32_t>(workgroups)), dim3(256),
                        0, static_cast<hipStream_t>(stream), out, iters);
+    return launched(fn);
+}
+
+int os_attention_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t heads, int64_t nq,
+                         int64_t nk, int head_dim, float scale, int causal, void* stream) {
+    const char* fn = "os_attention_forward";
+    if (head_dim != kAttnD) return fail(OS_EINVAL, "%s: head_dim %d is not supported (128 only)", fn, head_dim);
+    if (heads < 0 || nq < 0 || nk < 0) return fail(OS_EINVAL, "%s: heads, nq and nk must be >= 0", fn);
+    if (heads == 0 || nq == 0) return ok();
+    if (nk < 1) return fail(OS_EINVAL, "%s: nk must be >= 1 when there are query rows", fn);
+    if (nq > OS_ATTN_MAX_SEQ || nk > OS_ATTN_MAX_SEQ)
+        return fail(OS_EINVAL, "%s: nq and nk must be <= %lld", fn, (long long)OS_ATTN_MAX_SEQ);
+    if (causal && nq != nk) return fail(OS_EINVAL, "%s: the causal mask needs nq == nk", fn);
+    if (!(scale > 0.0f) || !(scale < INFINITY)) return fail(OS_EINVAL, "%s: scale must be finite and > 0", fn);
+    const int64_t nqb = (nq + kAttnBr - 1) / kAttnBr;
+    if (heads > INT64_MAX / (nq > nk ? nq : nk) / kAttnD / 2 || heads > INT64_MAX / nqb)
+        return fail(OS_EINVAL, "%s: heads * rows * head_dim overflows", fn);
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return fail(OS_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return fail(OS_EINVAL, "%s: q, k, v, o must be 16-byte aligned and lse 4-byte aligned", fn);
+    const int64_t units = heads * nqb;
+    const int grid = grid_for(units, 256, 0);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(causal ? k_attn_fwd<true> : k_attn_fwd<false>, dim3(grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                       heads, static_cast<int>(nq), static_cast<int>(nk), scale);
     return launched(fn);
 }
 

@@ -1,0 +1,131 @@
+"""GPU parity of the attention forward (os_attention_forward), through the C
+ABI, against the oracle's definition O = softmax(scale Q K^T) V with its
+per-row logsumexp, on seeded bf16 inputs.
+
+Bar, derived from the arithmetic (no tolerance is stated for this path):
+  - O: the kernel rounds each weight e^{(s - m) scale} to bf16 before the
+    second product (relative error <= 2^-9 per weight, so <= 2^-9 * sum_j
+    a_j |V_j| on an output), accumulates in fp32 (error ~1e-4 relative at
+    most) and rounds O to bf16 (2^-9 |O|):
+        |O - O_ref| <= 2^-8 * (sum_j a_j |V_j| + |O_ref|)     (2x margin).
+  - L = m scale + ln l: the fp32 dot products of the first product are off by
+    at most 128 * 2^-24 * sum_c |q_c k_c| before the scale, and l by at most
+    nk * 2^-24 relative (fp32 summation) plus a few ulp of exp2:
+        |L - L_ref| <= scale * 128 * 2^-24 * max_j sum_c |q_c k_c| + 2 nk 2^-24
+                       + 2^-22 |L_ref| + 1e-6.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ons():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_normalizer_amd
+    return online_normalizer_amd
+
+
+def dev(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def wide(bits: np.ndarray) -> np.ndarray:
+    return workloads.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def check(ons, orc, q, k, v, causal: bool, what: str, scale=None, threads: int = 16):
+    heads, nq, d = q.shape
+    nk = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    say(f"attention {what}: heads={heads} nq={nq} nk={nk} causal={causal}")
+    O, L = ons.os_attention_forward(dev(q), dev(k), dev(v), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy().astype(np.float64)
+    L = L.cpu().numpy().astype(np.float64)
+    Or, Lr, Oa = orc.attention(q, k, v, scale, causal=causal, threads=threads, want_abs=True)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L)), what
+    err = np.abs(O - Or) - 2.0 ** -8 * (Oa + np.abs(Or))
+    assert float(err.max()) <= 0.0, f"{what}: O off by {float(np.abs(O - Or).max()):.3e} beyond the bound"
+    # the logsumexp bound needs max_j sum_c |q_c k_c| per row
+    qa, ka = np.abs(wide(q)), np.abs(wide(k))
+    dots = np.einsum("hic,hjc->hij", qa, ka)
+    if causal:
+        dots = np.where(np.tril(np.ones((nq, nk), dtype=bool)), dots, 0.0)
+    bound_s = scale * d * 2.0 ** -24 * dots.max(axis=2)
+    tol = bound_s + 2 * nk * 2.0 ** -24 + 2.0 ** -22 * np.abs(Lr) + 1e-6
+    assert np.all(np.abs(L - Lr) <= tol), f"{what}: L off by {float(np.abs(L - Lr).max()):.3e}"
+    return float(np.abs(O - Or).max()), float(np.abs(L - Lr).max())
+
+
+# query and key lengths around the tile sizes (128 query rows per workgroup,
+# 64 keys per tile): one row, ragged tails, exact multiples
+SHAPES = [(1, 1), (1, 64), (31, 63), (128, 64), (129, 65), (200, 300), (64, 1), (257, 130)]
+
+
+@pytest.mark.parametrize("nq,nk", SHAPES, ids=[f"{a}x{b}" for a, b in SHAPES])
+def test_attention_small(ons, oracle_lib, nq, nk):
+    q, k, v = workloads.attention_qkv(3, nq, nk, 128, seed=2000 + nq * 7 + nk)
+    check(ons, oracle_lib, q, k, v, False, f"{nq}x{nk}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 128, 129, 300])
+def test_attention_causal(ons, oracle_lib, n):
+    q, k, v = workloads.attention_qkv(3, n, n, 128, seed=3000 + n)
+    check(ons, oracle_lib, q, k, v, True, f"causal n={n}")
+
+
+def test_attention_special_inputs(ons, oracle_lib):
+    """Large logits (scale 1, |q.k| up to ~hundreds: exercises the running
+    maximum's rescaling), equal keys (uniform weights), and a key that wins
+    every row late in the sequence."""
+    q, k, v = workloads.attention_qkv(2, 150, 260, 128, seed=4000)
+    check(ons, oracle_lib, q, k, v, False, "scale 1", scale=1.0)
+    keq = np.ascontiguousarray(np.broadcast_to(k[:, :1], k.shape))
+    check(ons, oracle_lib, q, keq, v, False, "equal keys")
+    kl = k.copy()
+    kl[:, 250] = workloads.f32_to_bf16_bits(np.sign(workloads.bf16_bits_to_f32(q[:, 0])) * 3.0)
+    check(ons, oracle_lib, q, kl, v, False, "late winning key")
+
+
+def test_attention_in_place_and_deterministic(ons):
+    q, k, v = workloads.attention_qkv(2, 300, 300, 128, seed=5000)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o1, l1 = ons.os_attention_forward(qd, kd, vd)
+    o2, l2 = ons.os_attention_forward(qd, kd, vd)
+    o3, _ = ons.os_attention_forward(qd, kd, vd, out=qd)  # o == q
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    assert o3.data_ptr() == qd.data_ptr() and torch.equal(qd.view(torch.int16), o1.view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_attention_workload_full(ons, oracle_lib, causal):
+    """The attention workload (256 heads x 2048 x 128, bf16) in the launch the
+    benchmark times, every output against the oracle."""
+    q, k, v = workloads.attention_workload()
+    heads = q.shape[0]
+    say(f"attention workload causal={causal}")
+    O, L = ons.os_attention_forward(dev(q), dev(k), dev(v), causal=causal)
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy()
+    L = L.cpu().numpy()
+    scale = 1.0 / math.sqrt(128)
+    for h0 in range(0, heads, 32):  # in head blocks: bounded host memory
+        sl = slice(h0, h0 + 32)
+        Or, Lr, Oa = oracle_lib.attention(q[sl], k[sl], v[sl], scale, causal=causal, threads=16, want_abs=True)
+        err = np.abs(O[sl].astype(np.float64) - Or) - 2.0 ** -8 * (Oa + np.abs(Or))
+        assert float(err.max()) <= 0.0, f"heads {h0}..: O beyond the bound"
+        # the L bound of the module docstring, with sum_c |q_c k_c| <= max|k| * sum_c |q_c|
+        bound_s = scale * 128 * 2.0 ** -24 * np.abs(wide(q[sl])).sum(axis=2) * np.abs(wide(k[sl])).max(axis=(1, 2))[:, None]
+        tol = bound_s + 2 * k.shape[1] * 2.0 ** -24 + 2.0 ** -22 * np.abs(Lr) + 1e-6
+        assert np.all(np.abs(L[sl] - Lr) <= tol), f"heads {h0}..: L off by {float(np.abs(L[sl] - Lr).max())}"

@@ -206,6 +206,31 @@ def dup_rows_cfg5() -> np.ndarray:
     return _dup_maxima(x, SEED_BASE + 5)
 
 
+# -- attention inputs ---------------------------------------------------------------
+#
+# The attention forward's workload takes workload 3's shape as an attention
+# problem: 8 batch x 32 heads = 256 heads of 2048 queries and 2048 keys, head
+# dimension 128 (the 1/sqrt(128) scale of workload 3), Q, K and V drawn
+# N(0, 1) in fp32 and rounded to bf16 nearest-even, seeds 1006 (Q), 1007 (K),
+# 1008 (V), laid out [heads, n, d].
+ATTN_HEADS, ATTN_N, ATTN_D = 8 * 32, 2048, 128
+ATTN_SEED = 1006
+
+
+def attention_qkv(heads: int, nq: int, nk: int, d: int, seed: int):
+    """Seeded bf16 Q [heads, nq, d], K and V [heads, nk, d] (uint16 bit patterns),
+    each N(0, 1) rounded to nearest-even, from seeds seed, seed + 1, seed + 2."""
+    def draw(n, s):
+        x = _blocked(heads * n, d, s, lambda g, m: g.standard_normal((m, d), dtype=np.float32), np.float32)
+        return f32_to_bf16_bits(x).reshape(heads, n, d)
+    return draw(nq, seed), draw(nk, seed + 1), draw(nk, seed + 2)
+
+
+def attention_workload():
+    """The attention workload: (q, k, v) of 256 heads x 2048 x 128."""
+    return attention_qkv(ATTN_HEADS, ATTN_N, ATTN_N, ATTN_D, ATTN_SEED)
+
+
 def two_shard_row() -> np.ndarray:
     """The worked example's row: shard A = [1, 2], shard B = [3]."""
     return np.array([[1.0, 2.0, 3.0]], dtype=np.float32)
