@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 CUS = 256           # MI355X compute units
 CLOCK_HZ = 2.4e9    # MI355X peak engine clock
 KERNEL_SOURCES = ["online_normalizer_amd/csrc/os_kernels.hpp", "online_normalizer_amd/csrc/os_device.hpp",
@@ -301,8 +302,49 @@ def per_workload(ons, stream, exp_per_s: float, x2=None, y2=None):
                            "flushed_frac": round(nb16 / tbf / 1e3 / PEAK_HBM_GBS, 4),
                            "floor_us_max_hbm_exp": round(floor_b, 2), "frac_vs_max_hbm_exp": round(floor_b / tb, 4)},
                   "cpu_oracle": {"s": round(med, 4), "cores": cores, "rows_per_s": round(rows / med, 1)}}
-    del x, xb, yt, scratch
+    del x, xb, yt
+    table["attention"] = attention_entry(ons, stream, gus, scratch)
+    del scratch
     return table
+
+
+def attention_entry(ons, stream, gus, scratch):
+    """The attention forward on the online normalizer (NEXT to the row
+    softmax: the (m, l, o~) state carried through Q K^T and P V on the matrix
+    cores), on workload 3's shape taken as attention: 256 heads x 2048 x 128,
+    bf16, full and causal.  FLOPs are the two products' 4 d per visible
+    (query, key) pair; the roofline is the 2.5 PFLOP/s dense bf16 peak.  The
+    CPU oracle is timed on 8 of the 256 heads."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    q, k, v = workloads.attention_workload()
+    H, N, D = q.shape
+    dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o = torch.empty_like(qd)
+    entry = {"heads": H, "seq": N, "head_dim": D, "dtype": "bf16", "peak_TFLOPs": PEAK_BF16_TFLOPS}
+    for causal in (False, True):
+        pairs = N * (N + 1) // 2 if causal else N * N
+        flops = 4.0 * D * pairs * H
+        t = gus(lambda: ons.os_attention_forward(qd, kd, vd, causal=causal, out=o), 10)
+        tf = flushed_us(lambda: ons.os_attention_forward(qd, kd, vd, causal=causal, out=o), stream, scratch, 5)
+        entry["causal" if causal else "full"] = {
+            "flops": flops, "kernel_us": round(t, 2), "TFLOPs": round(flops / t / 1e6, 1),
+            "frac": round(flops / t / 1e6 / PEAK_BF16_TFLOPS, 4), "flushed_us": round(tf, 2)}
+    orc = oracle.load()
+    cores = len(os.sched_getaffinity(0))
+    hs = 8
+    med, _ = oracle_times(lambda: orc.attention(q[:hs], k[:hs], v[:hs], 1.0 / math.sqrt(D), threads=cores), 3)
+    entry["cpu_oracle"] = {"s_for_8_heads": round(med, 3), "cores": cores,
+                           "TFLOPs": round(4.0 * D * N * N * hs / med / 1e12, 4)}
+    del qd, kd, vd, o
+    return entry
 
 
 def main(argv=None) -> int:
