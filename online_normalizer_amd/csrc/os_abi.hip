@@ -1103,9 +1103,9 @@ int os_attention_forward(const void* q, const void* k, const void* v, void* o, f
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return fail(OS_EINVAL, "%s: q, k, v, o must be 16-byte aligned and lse 4-byte aligned", fn);
     const int64_t units = heads * nqb;
-    const int grid = grid_for(units, 256, 0);
+    const int grid = grid_for(units, kAttnWaves * 64, 0);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(causal ? k_attn_fwd<true> : k_attn_fwd<false>, dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL(causal ? k_attn_fwd<true> : k_attn_fwd<false>, dim3(grid), dim3(kAttnWaves * 64), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
                        heads, static_cast<int>(nq), static_cast<int>(nk), scale);

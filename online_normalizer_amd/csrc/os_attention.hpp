@@ -10,7 +10,7 @@
 // Layout: bf16 Q [heads, nq, 128], K and V [heads, nk, 128], O like Q; the
 // per-row logsumexp L = m + ln l in fp32 [heads, nq].
 //
-// One workgroup = 4 waves = 128 query rows of one head (the outer loop over
+// One workgroup = 8 waves = 256 query rows of one head (the outer loop over
 // query blocks of "6.2 FlashAttention V2 chi tiết", section 2.2); each wave
 // owns 32 query rows (its section 4.2: no exchange between waves), walks the
 // key tiles of 64 keys in order, and keeps its rows' (m, l) and o~ in
@@ -41,7 +41,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnD = 128;                // head dimension
 constexpr int kAttnBc = 64;                // keys per tile
-constexpr int kAttnWaves = 4;              // waves per workgroup
+// 8 waves = 256 query rows per workgroup, one workgroup per CU at 2 waves per
+// SIMD: each staged K/V tile feeds twice the products of a 4-wave workgroup
+// (measured 870 -> 719 us on the 256-head 2048 x 128 workload; 16 waves
+// would cap a lane at 128 VGPRs and spill)
+constexpr int kAttnWaves = 8;              // waves per workgroup
 constexpr int kAttnBr = 32 * kAttnWaves;   // query rows per workgroup
 constexpr int kAttnKStride = kAttnD + 8;   // LDS row stride of a K tile (elements; +16 B against bank conflicts)
 constexpr int kAttnVStride = kAttnBc + 8;  // LDS row stride of a V^T tile
@@ -61,9 +65,12 @@ __device__ __forceinline__ int vt_pos(int kk) {
 }
 
 template <bool CAUSAL>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAttnWaves * 64), amdgpu_waves_per_eu(2)))
     k_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                uint16_t* __restrict__ o, float* __restrict__ lse, int64_t heads, int nq, int nk, float scale) {
+    constexpr int NT = kAttnWaves * 64;        // threads
+    constexpr int KV = kAttnBc * kAttnD / 8 / NT;  // K vectors per thread per tile
+    constexpr int VK = kAttnBc * kAttnD / 8 / NT;  // V keys per thread per tile (one 8-dim chunk each)
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][kAttnBc * kAttnKStride];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][kAttnD * kAttnVStride];
 
@@ -76,6 +83,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
     const int nqb = (nq + kAttnBr - 1) / kAttnBr;
     const int64_t units = heads * nqb;
 
+    static_assert(KV * NT * 8 == kAttnBc * kAttnD && (VK == 1 || VK == 2 || VK == 4), "staging shape");
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         // Workgroups go to the 8 XCDs in turn (unit % 8), and each XCD has its
         // own L2.  When the heads split evenly, all query blocks of a head run
@@ -107,38 +115,42 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
         for (int ks = 0; ks < kAttnD / 16; ++ks)
             qb8[ks] = as_bf16x8(bq.load16<true>((static_cast<uint32_t>(qrow) * kAttnD + ks * 16 + h * 8) * 2u));
 
-        // tile staging: thread tid moves K vectors tid + 256 r (key (tid + 256 r) / 16,
-        // dims 8 ((tid + 256 r) % 16)), and V keys 4 (tid / 16) .. + 3, dims 8 (tid % 16)
-        u32x4 kr[4], vr[4];
-        const int vkey0 = (tid >> 4) * 4, vchunk = tid & 15;
+        // tile staging: thread tid moves K vectors tid + NT r, and V keys
+        // VK (tid / 16) .. + VK - 1, dims 8 (tid % 16)
+        u32x4 kr[KV], vr[VK];
+        const int vkey0 = (tid >> 4) * VK, vchunk = tid & 15;
         auto load_tile = [&](int t) {
             const int key0 = t * kAttnBc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int idx = tid + 256 * r;
+            for (int r = 0; r < KV; ++r) {
+                const int idx = tid + NT * r;
                 kr[r] = bk.load16<true>((static_cast<uint32_t>(key0 + (idx >> 4)) * kAttnD + (idx & 15) * 8) * 2u);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < VK; ++r)
                 vr[r] = bv.load16<true>((static_cast<uint32_t>(key0 + vkey0 + r) * kAttnD + vchunk * 8) * 2u);
         };
         auto store_tile = [&](int buf) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int idx = tid + 256 * r;
+            for (int r = 0; r < KV; ++r) {
+                const int idx = tid + NT * r;
                 *reinterpret_cast<u32x4*>(&sK[buf][(idx >> 4) * kAttnKStride + (idx & 15) * 8]) = kr[r];
             }
-            // transpose 4 keys x 8 dims: dim dd of the 4 keys becomes 4 consecutive V^T entries
+            // transpose VK keys x 8 dims: dim dd of the keys becomes VK consecutive V^T entries
             const int pos = vt_pos(vkey0);
 #pragma unroll
             for (int dd = 0; dd < 8; ++dd) {
                 const int word = dd >> 1, hi = dd & 1;
-                const uint32_t e0 = hi ? (vr[0][word] >> 16) : (vr[0][word] & 0xFFFFu);
-                const uint32_t e1 = hi ? (vr[1][word] >> 16) : (vr[1][word] & 0xFFFFu);
-                const uint32_t e2 = hi ? (vr[2][word] >> 16) : (vr[2][word] & 0xFFFFu);
-                const uint32_t e3 = hi ? (vr[3][word] >> 16) : (vr[3][word] & 0xFFFFu);
-                *reinterpret_cast<u32x2*>(&sV[buf][(vchunk * 8 + dd) * kAttnVStride + pos]) =
-                    u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+                uint32_t e[VK];
+#pragma unroll
+                for (int r = 0; r < VK; ++r) e[r] = hi ? (vr[r][word] >> 16) : (vr[r][word] & 0xFFFFu);
+                if constexpr (VK == 4)
+                    *reinterpret_cast<u32x2*>(&sV[buf][(vchunk * 8 + dd) * kAttnVStride + pos]) =
+                        u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+                else if constexpr (VK == 2)
+                    *reinterpret_cast<uint32_t*>(&sV[buf][(vchunk * 8 + dd) * kAttnVStride + pos]) = e[0] | (e[1] << 16);
+                else
+                    sV[buf][(vchunk * 8 + dd) * kAttnVStride + pos] = static_cast<uint16_t>(e[0]);
             }
         };
 
@@ -161,6 +173,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
             const int buf = t & 1;
             if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's products
 
+            // causal: a tile whose first key lies past this wave's last row adds nothing to it
+            const bool wave_live = !CAUSAL || (t * kAttnBc <= q0 + w * 32 + 31);
+            if (wave_live) {
             // S^T = K Q^T for the tile's two 32-key blocks
             f32x16 s[2];
 #pragma unroll
@@ -234,6 +249,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
                         &sV[buf][(db * 32 + col) * kAttnVStride + (kk >> 1) * 32 + (kk & 1) * 16 + h * 8]));
                     oacc[db] = mfma32(a, pb[kk], oacc[db]);
                 }
+            }  // wave_live
             if (t + 1 < ntiles) {
                 store_tile(buf ^ 1);
                 __syncthreads();
