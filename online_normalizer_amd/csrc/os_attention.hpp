@@ -116,25 +116,35 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
             qb8[ks] = as_bf16x8(bq.load16<true>((static_cast<uint32_t>(qrow) * kAttnD + ks * 16 + h * 8) * 2u));
 
         // tile staging: thread tid moves K vectors tid + NT r, and V keys
-        // VK (tid / 16) .. + VK - 1, dims 8 (tid % 16)
-        u32x4 kr[KV], vr[VK];
-        const int vkey0 = (tid >> 4) * VK, vchunk = tid & 15;
-        auto load_tile = [&](int t) {
+        // VK (tid % (64 / VK)) .. + VK - 1, dims 8 (tid / (64 / VK)), through one of two
+        // register sets: tile j's loads go to set j % 2 two tiles before its
+        // LDS store, so their latency hides behind two tiles of products
+        struct Stage {
+            u32x4 k[KV], v[VK];
+        };
+        Stage st0, st1;
+        // Consecutive lanes take consecutive keys of one dim chunk, so a V^T
+        // store instruction fills one LDS row across the banks (with the
+        // chunk in the low lane bits, the 16 chunks' rows, 1152 bytes apart,
+        // fell on the same banks)
+        constexpr int VGROUPS = kAttnBc / VK;  // key groups per tile
+        const int vkey0 = (tid % VGROUPS) * VK, vchunk = tid / VGROUPS;
+        auto load_tile = [&](int t, Stage& sg) {
             const int key0 = t * kAttnBc;
 #pragma unroll
             for (int r = 0; r < KV; ++r) {
                 const int idx = tid + NT * r;
-                kr[r] = bk.load16<true>((static_cast<uint32_t>(key0 + (idx >> 4)) * kAttnD + (idx & 15) * 8) * 2u);
+                sg.k[r] = bk.load16<true>((static_cast<uint32_t>(key0 + (idx >> 4)) * kAttnD + (idx & 15) * 8) * 2u);
             }
 #pragma unroll
             for (int r = 0; r < VK; ++r)
-                vr[r] = bv.load16<true>((static_cast<uint32_t>(key0 + vkey0 + r) * kAttnD + vchunk * 8) * 2u);
+                sg.v[r] = bv.load16<true>((static_cast<uint32_t>(key0 + vkey0 + r) * kAttnD + vchunk * 8) * 2u);
         };
-        auto store_tile = [&](int buf) {
+        auto store_tile = [&](const Stage& sg, int buf) {
 #pragma unroll
             for (int r = 0; r < KV; ++r) {
                 const int idx = tid + NT * r;
-                *reinterpret_cast<u32x4*>(&sK[buf][(idx >> 4) * kAttnKStride + (idx & 15) * 8]) = kr[r];
+                *reinterpret_cast<u32x4*>(&sK[buf][(idx >> 4) * kAttnKStride + (idx & 15) * 8]) = sg.k[r];
             }
             // transpose VK keys x 8 dims: dim dd of the keys becomes VK consecutive V^T entries
             const int pos = vt_pos(vkey0);
@@ -143,7 +153,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
                 const int word = dd >> 1, hi = dd & 1;
                 uint32_t e[VK];
 #pragma unroll
-                for (int r = 0; r < VK; ++r) e[r] = hi ? (vr[r][word] >> 16) : (vr[r][word] & 0xFFFFu);
+                for (int r = 0; r < VK; ++r) e[r] = hi ? (sg.v[r][word] >> 16) : (sg.v[r][word] & 0xFFFFu);
                 if constexpr (VK == 4)
                     *reinterpret_cast<u32x2*>(&sV[buf][(vchunk * 8 + dd) * kAttnVStride + pos]) =
                         u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
@@ -162,16 +172,24 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
         float m = -INFINITY;  // running maximum of this row's raw logits q.k
         float l = 0.0f;       // this lane's share of sum e^{(s - m) scale} (its half of the keys)
 
-        load_tile(0);
-        store_tile(0);
+        load_tile(0, st0);
+        store_tile(st0, 0);
         __syncthreads();
         // Q must be in registers before the loop: otherwise the compiler's
         // wait for Q's loads inside the first product also waits for the
-        // next tile's loads, every tile (measured 1018 -> 963 us)
+        // next tiles' loads, every tile (measured 1018 -> 963 us)
         __builtin_amdgcn_s_waitcnt(0);
-        for (int t = 0; t < ntiles; ++t) {
+        load_tile(1, st1);
+        // One tile: issue tile t + 2's loads into `cur` (free: it held tile t,
+        // stored before this tile began), the products on LDS buffer t % 2,
+        // then tile t + 1 from `nxt` into the other buffer.  The loads are
+        // issued even past the last tile (keys past nk read nothing: the
+        // buffer range check; causal tiles past the diagonal are real keys,
+        // unused): a conditional load would make the compiler wait for it
+        // together with `nxt`'s loads before the store.
+        auto tile = [&](const int t, Stage& cur, const Stage& nxt) {
             const int buf = t & 1;
-            if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's products
+            load_tile(t + 2, cur);
 
             // causal: a tile whose first key lies past this wave's last row adds nothing to it
             const bool wave_live = !CAUSAL || (t * kAttnBc <= q0 + w * 32 + 31);
@@ -251,9 +269,13 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
                 }
             }  // wave_live
             if (t + 1 < ntiles) {
-                store_tile(buf ^ 1);
+                store_tile(nxt, buf ^ 1);
                 __syncthreads();
             }
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            tile(t, st0, st1);
+            if (t + 1 < ntiles) tile(t + 1, st1, st0);
         }
         // the row's sum over both halves; O = o~ / l
         {
