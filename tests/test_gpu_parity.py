@@ -458,6 +458,52 @@ def test_graph_replays_match_eager(ons):
         del junk
 
 
+def test_graph_replays_more_entries(ons):
+    """The naive two-pass forward, the value selection, the split forward on
+    the library's static scratch, and the attention forward (full and causal,
+    with a ragged key tail) captured in one HIP graph: every replay, with eager
+    calls of the same entry points on other inputs between replays, equals the
+    eager result bit for bit."""
+    x = to_device(workloads.config(2, 0, 256))
+    xs = to_device(workloads.normal(8, 100003, seed=21, scale=3.0))
+    xt = to_device(bf16_bits(workloads.normal(64, 32000, seed=22, scale=3.0)))
+    q, k, v = (to_device(a) for a in workloads.attention_qkv(4, 320, 320, 128, 23))
+    say("graph capture (naive, select, no-alloc split, attention)")
+    n_ref = ons.naive_softmax_forward(x)
+    sv_ref, si_ref = ons.os_topk_select(xt, 8)
+    ns_ref = ons.os_softmax_forward_split_noalloc(xs, splits=8)
+    o_ref, l_ref = ons.os_attention_forward(q, k, v)
+    oc_ref, lc_ref = ons.os_attention_forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    n, ns = torch.empty_like(x), torch.empty_like(xs)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ons.naive_softmax_forward(x, out=n)
+        sv, si = ons.os_topk_select(xt, 8)
+        ons.os_softmax_forward_split_noalloc(xs, splits=8, out=ns)
+        o, l = ons.os_attention_forward(q, k, v)
+        oc, lc = ons.os_attention_forward(q, k, v, causal=True)
+    other = to_device(workloads.normal(4, 70001, seed=24, scale=3.0))
+    for rep in range(4):
+        for t in (n, sv, si, ns, o, l, oc, lc):
+            t.zero_()
+        # eager calls between replays, the no-allocation one on the same static scratch
+        junk = [ons.os_softmax_forward_split_noalloc(other, splits=4), ons.naive_softmax_forward(other),
+                ons.os_attention_forward(k, q, v)]
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(n.view(torch.int32), n_ref.view(torch.int32)), rep
+        assert torch.equal(sv, sv_ref) and torch.equal(si, si_ref), rep
+        assert torch.equal(ns.view(torch.int32), ns_ref.view(torch.int32)), rep
+        for got, want in ((o, o_ref), (oc, oc_ref)):
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), rep
+        for got, want in ((l, l_ref), (lc, lc_ref)):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32)), rep
+        del junk
+
+
 def test_stats_invariants(ons, orc):
     """1 <= d <= N (up to fp32 rounding), m is the exact row maximum, d matches the oracle."""
     for n in (1, 2, 4):
