@@ -1182,6 +1182,11 @@ __global__ void __launch_bounds__(W * 64)
         const Slice sl = slice_of(seg, SPLIT ? S : 1, slot_count<BF16>(cols, ph), si.bytes, 1);
         const int v0 = sl.v0, v1 = sl.v1;
         const Buf bin(si.base, sl.bytes);
+        // the first tile's loads go out before the barrier below, which
+        // waits for every wave of the workgroup to start
+        u32x4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(v0 + u * BLOCK + tid) * 16u);
         if (tid == 0) s_thr = ordered_bits(-INFINITY);
         if (tid < 128) s_rank[tid / 64][tid % 64] = 0;
         __syncthreads();
@@ -1324,9 +1329,6 @@ __global__ void __launch_bounds__(W * 64)
         // Software pipeline over the segment's tiles: the loads of the next
         // tile are in flight while one is folded.  Loads past the end of the
         // segment touch no memory (buffer range check).
-        u32x4 raw[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = bin.load16<true>(static_cast<uint32_t>(v0 + u * BLOCK + tid) * 16u);
         for (int base = v0; base < v1; base += STEP) tile(raw, base);
 
         const State st = group_merge<64>(State{ml, dl});
