@@ -183,6 +183,13 @@ def _out_like(x, out):
     return out
 
 
+def _whole(t: torch.Tensor, what: str, like: torch.Tensor | None = None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous GPU tensor")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{what} must be on the input's device")
+
+
 def os_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     rows, cols = _rows_cols(x)
     out = _out_like(x, out)
@@ -257,19 +264,27 @@ def _split_workspace(x: torch.Tensor, nbytes: int) -> torch.Tensor:
     return ws
 
 
-def _topk_out(x, K):
+def _topk_out(x, K, probs=None, idx=None):
+    """rows, cols and the (probs or values, indices) outputs: new tensors, or
+    the caller's, checked to be contiguous [..., K] float32 / int32 tensors on
+    x's device (the library writes rows * K entries through their pointers)."""
     rows, cols = _rows_cols(x)
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("top-K takes float32 or bfloat16 input")
     shape = (*x.shape[:-1], K)
-    probs = torch.empty(shape, dtype=torch.float32, device=x.device)
-    idx = torch.empty(shape, dtype=torch.int32, device=x.device)
+    for name, t, dt in (("probs", probs, torch.float32), ("idx", idx, torch.int32)):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != dt or t.device != x.device
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape} on {x.device}")
+    probs = torch.empty(shape, dtype=torch.float32, device=x.device) if probs is None else probs
+    idx = torch.empty(shape, dtype=torch.int32, device=x.device) if idx is None else idx
     return rows, cols, probs, idx
 
 
 def os_softmax_topk_split(x: torch.Tensor, K: int, splits: int,
                           workspace: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     rows, cols, probs, idx = _topk_out(x, K)
+    _whole(workspace, "workspace", x)
     _check("os_softmax_topk_split",
            lib().os_softmax_topk_split(x.data_ptr(), probs.data_ptr(), idx.data_ptr(), rows, cols, K, splits,
                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -298,8 +313,8 @@ def os_device_copy_rows(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
     """Copy src (rows x row_bytes, row_bytes <= 128 KiB) with the register-resident
     forward's access pattern (a bandwidth reference)."""
     rows, cols = _rows_cols(src)
-    if dst.shape != src.shape or dst.dtype != src.dtype or not dst.is_contiguous():
-        raise ValueError("dst must be a contiguous tensor like src")
+    if dst.shape != src.shape or dst.dtype != src.dtype or not dst.is_contiguous() or dst.device != src.device:
+        raise ValueError("dst must be a contiguous tensor like src, on its device")
     _check("os_device_copy_rows", lib().os_device_copy_rows(src.data_ptr(), dst.data_ptr(), rows,
                                                             cols * src.element_size(), _stream(src)))
     return dst
@@ -327,6 +342,7 @@ def os_softmax_forward_split(x: torch.Tensor, splits: int | None = None, out: to
         splits = os_forward_split_plan(rows, cols, x.dtype)
     if workspace is None:
         workspace = _split_workspace(x, os_softmax_forward_workspace_bytes(rows, splits))
+    _whole(workspace, "workspace", x)
     _check("os_softmax_forward_split",
            lib().os_softmax_forward_split(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), splits,
                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -354,9 +370,9 @@ def os_softmax_topk_ex(x: torch.Tensor, K: int, splits: int, workspace: torch.Te
                        idx: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
     """Fused softmax + top-K for float32 or bfloat16 input (dtype from the tensor).
     workspace may be None when splits == 1."""
-    rows, cols, p_new, i_new = _topk_out(x, K)
-    probs = p_new if probs is None else probs
-    idx = i_new if idx is None else idx
+    rows, cols, probs, idx = _topk_out(x, K, probs, idx)
+    if workspace is not None:
+        _whole(workspace, "workspace", x)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("os_softmax_topk_ex",
@@ -384,9 +400,7 @@ def naive_softmax_forward(x: torch.Tensor, out: torch.Tensor | None = None) -> t
 def os_topk_select(x: torch.Tensor, K: int, vals: torch.Tensor | None = None,
                    idx: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
     """The K largest entries of each row (value desc, index asc) and their columns."""
-    rows, cols, v_new, i_new = _topk_out(x, K)
-    vals = v_new if vals is None else vals
-    idx = i_new if idx is None else idx
+    rows, cols, vals, idx = _topk_out(x, K, vals, idx)
     _check("os_topk_select",
            lib().os_topk_select(x.data_ptr(), _dtype_code(x), vals.data_ptr(), idx.data_ptr(), rows, cols, K,
                                 _stream(x)))
@@ -396,7 +410,7 @@ def os_topk_select(x: torch.Tensor, K: int, vals: torch.Tensor | None = None,
 def os_bench_exp(out: torch.Tensor, workgroups: int, iters: int, chains: int) -> torch.Tensor:
     """Launch the exponential-rate microbenchmark (workgroups * 256 * iters *
     chains exponentials); out: float32 with at least workgroups * 256 elements."""
-    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < workgroups * 256:
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or out.numel() < workgroups * 256:
         raise ValueError("out must be a float32 GPU tensor of at least workgroups * 256 elements")
     _check("os_bench_exp", lib().os_bench_exp(out.data_ptr(), workgroups, iters, chains, _stream(out)))
     return out
@@ -405,8 +419,9 @@ def os_bench_exp(out: torch.Tensor, workgroups: int, iters: int, chains: int) ->
 def os_device_read(src: torch.Tensor, sink: torch.Tensor) -> torch.Tensor:
     """Read all of src (a plain read, the read-only bandwidth reference); sink:
     float32, at least 4 * min(2048, ceil(bytes / 4096)) elements."""
-    if sink.dtype != torch.float32 or not sink.is_cuda:
-        raise ValueError("sink must be a float32 GPU tensor")
+    if sink.dtype != torch.float32 or not sink.is_cuda or not sink.is_contiguous() or sink.device != src.device:
+        raise ValueError("sink must be a contiguous float32 tensor on src's device")
+    _whole(src, "src")
     nbytes = src.numel() * src.element_size()
     _check("os_device_read", lib().os_device_read(src.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), _stream(src)))
     return sink
@@ -422,6 +437,8 @@ def os_attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scal
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() < 2:
             raise TypeError("q, k, v must be contiguous bfloat16 GPU tensors [..., n, d]")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     d = q.shape[-1]
     if k.shape != v.shape or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != d:
         raise ValueError("k and v must be [..., nk, d] with q's leading dimensions and d")
@@ -439,6 +456,8 @@ def os_attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scal
 
 
 def os_device_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    _whole(src, "src")
+    _whole(dst, "dst", src)
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst is smaller than src")

@@ -504,6 +504,37 @@ def test_graph_replays_more_entries(ons):
         del junk
 
 
+def test_binding_rejects_bad_outputs(ons):
+    """Caller-supplied outputs and workspaces of the wrong shape, dtype or
+    layout are refused by the binding before any launch (the library writes
+    rows * K entries through their pointers)."""
+    x = to_device(workloads.normal(16, 1000, seed=31, scale=3.0))
+    say("binding output checks")
+    good_v = torch.empty(16, 8, device="cuda")
+    good_i = torch.empty(16, 8, dtype=torch.int32, device="cuda")
+    bad = [
+        dict(vals=torch.empty(16, 4, device="cuda")),                        # too few columns
+        dict(vals=torch.empty(8, 8, device="cuda")),                         # too few rows
+        dict(idx=torch.empty(16, 8, dtype=torch.int64, device="cuda")),      # wrong dtype
+        dict(idx=torch.empty(8, 16, dtype=torch.int32, device="cuda").t()),  # not contiguous
+        dict(vals=torch.empty(16, 8)),                                       # host memory
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            ons.os_topk_select(x, 8, **kw)
+        kwp = {"probs" if k == "vals" else k: v for k, v in kw.items()}
+        with pytest.raises(ValueError):
+            ons.os_softmax_topk_ex(x, 8, 1, None, **kwp)
+    with pytest.raises(ValueError):
+        ons.os_softmax_forward_split(x, splits=2, workspace=torch.empty(4096, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        ons.os_device_copy(x.t(), torch.empty_like(x))
+    v, i = ons.os_topk_select(x, 8, good_v, good_i)
+    p, j = ons.os_softmax_topk_ex(x, 8, 1, None, torch.empty_like(good_v), torch.empty_like(good_i))
+    torch.cuda.synchronize()
+    assert v.data_ptr() == good_v.data_ptr() and torch.equal(i, j)
+
+
 def test_stats_invariants(ons, orc):
     """1 <= d <= N (up to fp32 rounding), m is the exact row maximum, d matches the oracle."""
     for n in (1, 2, 4):
