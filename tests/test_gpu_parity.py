@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import (TOPK_PROB_ABS, assert_fp32_parity, assert_parity, say, to_device, to_host)
+from gpu_util import (FP32_MAX_ABS, FP32_ROW_SUM, TOPK_PROB_ABS, assert_fp32_parity, assert_parity, say, to_device,
+                      to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -630,6 +631,39 @@ def test_split_launches_past_the_grid_cap(ons, orc):
     pr, ir = orc.topk(xm, 1, threads=16)
     assert np.array_equal(to_host(i), ir)
     assert np.max(np.abs(to_host(p).astype(np.float64) - pr)) <= TOPK_PROB_ABS
+
+
+def test_maximum_row_length(ons, orc):
+    """One row of the longest length the library takes (OS_MAX_COLS = 2^28
+    entries: 1 GiB in fp32, 512 MiB in bf16), through the forward (one
+    workgroup streaming the row) and the planned split forward, every output
+    against the oracle in blocks of 2^24, and the fp32 row's sum."""
+    n = 1 << 28
+    x32 = workloads.normal(1, n, seed=28, scale=3.0)
+    x32[0, n - 7] = 40.0  # the maximum near the end: every earlier part is rescaled
+    for bf16 in (False, True):
+        x = bf16_bits(x32) if bf16 else x32
+        ref = orc.softmax(x)[0]
+        xd = to_device(x)
+        for name in ("forward", "split forward"):
+            say(f"maximum row length 2^28, bf16={bf16}, {name}")
+            y = ons.os_softmax_forward(xd) if name == "forward" else ons.os_softmax_forward_split(xd)
+            torch.cuda.synchronize()
+            yh = to_host(y)[0]
+            del y
+            blk = 1 << 24
+            for b0 in range(0, n, blk):
+                got, want = yh[b0:b0 + blk], ref[b0:b0 + blk]
+                if bf16:
+                    assert_parity(got[None], want[None], True, f"{name} bf16 block {b0}")
+                else:
+                    err = float(np.max(np.abs(got.astype(np.float64) - want)))
+                    assert err <= FP32_MAX_ABS, f"{name} block {b0}: max abs error {err:.3e}"
+            if not bf16:
+                total = float(np.sum(yh, dtype=np.float64))
+                assert abs(total - 1.0) <= FP32_ROW_SUM, f"{name}: row sum {total}"
+            del yh
+        del xd, ref
 
 
 def test_split_forward_reuses_workspace(ons, orc):
