@@ -108,6 +108,28 @@ def test_attention_in_place_and_deterministic(ons):
     assert o3.data_ptr() == qd.data_ptr() and torch.equal(qd.view(torch.int16), o1.view(torch.int16))
 
 
+def test_attention_longest_key_sequence(ons, oracle_lib):
+    """The longest key sequence the library takes (OS_ATTN_MAX_SEQ = 2^22
+    keys: 1 GiB of K and of V for one head) against a few query rows, every
+    output against the oracle (with the bound of the module docstring, the
+    dot-product term taken as max|k| * sum|q|)."""
+    nk = 1 << 22
+    q, k, v = workloads.attention_qkv(1, 5, nk, 128, seed=4200)
+    scale = 1.0 / math.sqrt(128)
+    say(f"attention: 1 head, 5 queries, {nk} keys")
+    O, L = ons.os_attention_forward(dev(q), dev(k), dev(v))
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy().astype(np.float64)
+    L = L.cpu().numpy().astype(np.float64)
+    Or, Lr, Oa = oracle_lib.attention(q, k, v, scale, want_abs=True)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    err = np.abs(O - Or) - 2.0 ** -8 * (Oa + np.abs(Or))
+    assert float(err.max()) <= 0.0, f"O off by {float(np.abs(O - Or).max()):.3e} beyond the bound"
+    bound_s = scale * 128 * 2.0 ** -24 * np.abs(wide(q)).sum(axis=2) * float(np.abs(wide(k)).max())
+    tol = bound_s + 2 * nk * 2.0 ** -24 + 2.0 ** -22 * np.abs(Lr) + 1e-6
+    assert np.all(np.abs(L - Lr) <= tol), f"L off by {float(np.abs(L - Lr).max())}"
+
+
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_attention_workload_full(ons, oracle_lib, causal):
     """The attention workload (256 heads x 2048 x 128, bf16) in the launch the
