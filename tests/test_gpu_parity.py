@@ -938,6 +938,44 @@ def test_topk_split_rows(ons, orc, splits):
     check_topk(ons, orc, xl, 8, f"split {splits} long rows", splits=splits)
 
 
+def test_topk_maximum_row_length(ons, orc):
+    """Top-32 of one row of OS_MAX_COLS = 2^28 fp32 entries (1 GiB), one
+    workgroup and the planned split.  The oracle's full sort of such a row is
+    out of reach, so the result is checked by properties that fix it: 32
+    distinct in-row columns whose values rank first under (value desc, index
+    asc) -- fewer than 32 entries lie above the 32nd value, and every entry
+    equal to it that is not selected has a higher column than the selected
+    ones -- and probabilities e^{x - m} / d from the oracle's (m, d) of the row.
+    A planted duplicate of the maximum exercises the tie rule."""
+    n, K = 1 << 28, 32
+    x = workloads.normal(1, n, seed=2828, scale=3.0)
+    x[0, n - 11] = 40.0   # far above the row's natural maximum (about 19)
+    x[0, 12345] = 40.0    # a tie at the top: the lower column ranks first
+    x[0, n - 2] = 39.5
+    m, d = orc.stats(x)
+    xd = to_device(x)
+    row = x[0]
+    for splits in (1, None):
+        say(f"top-K maximum row length 2^28, K={K}, splits={splits}")
+        p, i = ons.os_softmax_topk(xd, K, splits=splits)
+        torch.cuda.synchronize()
+        i = to_host(i)[0].astype(np.int64)
+        p = to_host(p)[0].astype(np.float64)
+        assert np.all((i >= 0) & (i < n)) and np.unique(i).size == K
+        vals = row[i]
+        assert i[0] == 12345 and i[1] == n - 11 and i[2] == n - 2
+        order_ok = (vals[:-1] > vals[1:]) | ((vals[:-1] == vals[1:]) & (i[:-1] < i[1:]))
+        assert np.all(order_ok), "selected entries are not in (value desc, index asc) order"
+        vk = vals[-1]
+        assert int(np.count_nonzero(row > vk)) < K
+        ties = np.flatnonzero(row == vk)
+        chosen = np.sort(i[vals == vk])
+        assert np.array_equal(ties[:chosen.size], chosen), "a lower column equal to the K-th value was skipped"
+        want = np.exp(vals.astype(np.float64) - m[0]) / d[0]
+        assert float(np.max(np.abs(p - want))) <= TOPK_PROB_ABS
+    del xd
+
+
 def test_topk_split_reuses_workspace(ons):
     """Back-to-back split calls on one (uninitialised) workspace give identical results."""
     x = to_device(workloads.config(5, 0, 64))
