@@ -15,6 +15,7 @@ Bar, derived from the arithmetic (no tolerance is stated for this path):
                        + 2^-22 |L_ref| + 1e-6.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -82,6 +83,24 @@ def test_attention_small(ons, oracle_lib, nq, nk):
 def test_attention_causal(ons, oracle_lib, n):
     q, k, v = workloads.attention_qkv(3, n, n, 128, seed=3000 + n)
     check(ons, oracle_lib, q, k, v, True, f"causal n={n}")
+
+
+RANDOM_CASES = int(os.environ.get("ONORM_RANDOM_ATTN_CASES", "24"))
+
+
+@pytest.mark.parametrize("case", range(RANDOM_CASES))
+def test_attention_random(ons, oracle_lib, case):
+    """A seeded random draw of heads (1-4), query and key lengths around the
+    tile sizes, the causal mask and the scale (ONORM_RANDOM_ATTN_CASES sets the
+    number of cases, 24 by default)."""
+    rng = np.random.Generator(np.random.PCG64(77000 + case))
+    heads = int(rng.integers(1, 5))
+    causal = bool(rng.random() < 0.4)
+    nq = int(rng.choice([1, 2, 31, 32, 33, 63, 64, 65, 127, 200, 255, 256, 257, 300, 511, 513, 700]))
+    nk = nq if causal else int(rng.choice([1, 3, 63, 64, 65, 100, 128, 129, 255, 256, 300, 640, 1000]))
+    scale = float(rng.choice([1.0 / math.sqrt(128), 0.01, 0.3, 1.0]))
+    q, k, v = workloads.attention_qkv(heads, nq, nk, 128, seed=77000 + 3 * case)
+    check(ons, oracle_lib, q, k, v, causal, f"random case {case} (scale {scale})", scale=scale, threads=4)
 
 
 def test_attention_special_inputs(ons, oracle_lib):

@@ -4,9 +4,14 @@ Each case draws a shape (1 to 64 rows, 1 to 200003 columns), a dtype, a value
 scale and a mix of special entries (-inf runs, all -inf rows, NaN, +-80
 outliers, copied maxima for ties), and sometimes a base pointer that is only
 element-aligned.  The forward, the 3-pass baseline, the logsumexp, the
-split-row forward (random slice count) and, for inputs without NaN, the top-K
-(random K and slice count) must each meet the parity bars.
+split-row forward (random slice count) and its no-allocation form, the
+unshifted baseline (on inputs whose exponentials stay finite in fp32), and,
+for inputs without NaN, the top-K (random K and slice count) and the
+selection must each meet the parity bars.  ONORM_RANDOM_CASES sets the number
+of cases (48 by default).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -17,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-N_CASES = 48
+N_CASES = int(os.environ.get("ONORM_RANDOM_CASES", "48"))
 COLS = [1, 2, 3, 5, 8, 17, 63, 64, 100, 127, 255, 511, 1000, 2047, 4096, 4099, 8193, 16384, 32000, 40000, 65536,
         65537, 81920, 131072, 200003]
 
@@ -92,10 +97,23 @@ def test_random_case(ons, oracle_lib, case):
     assert np.all(np.abs(lse[fin] - lse_ref[fin]) <= 1e-5 + 2.0 ** -22 * np.abs(lse_ref[fin])), what
 
     S = int(rng.choice([1, 2, 3, 7, 16, 64, 256]))
-    say(f"{what}: split forward S={S}")
+    say(f"{what}: split forward S={S}, and on the static scratch")
     ys = ons.os_softmax_forward_split(xd, splits=S)
+    Sn = min(S, 16)
+    yn = ons.os_softmax_forward_split_noalloc(xd, splits=Sn) if rows * Sn * 8 <= ons.OS_STATIC_SCRATCH_BYTES else None
     torch.cuda.synchronize()
     assert_parity(to_host(ys), ref, bf16, f"{what} split S={S}")
+    if yn is not None:
+        assert_parity(to_host(yn), ref, bf16, f"{what} split on the static scratch S={Sn}")
+
+    # the unshifted form, where no e^x overflows or underflows to zero sum in fp32
+    finite = x32[np.isfinite(x32)]
+    if not nan and finite.size and float(finite.max()) < 80.0 and float(finite.min()) > -80.0:
+        say(f"{what}: naive")
+        yv = ons.naive_softmax_forward(xd)
+        torch.cuda.synchronize()
+        rn = oracle_lib.naive_softmax(x, threads=8)
+        assert_parity(to_host(yv), rn, bf16, f"{what} naive")
 
     if not nan:
         K = int(rng.integers(1, min(cols, 32) + 1))
@@ -109,3 +127,9 @@ def test_random_case(ons, oracle_lib, case):
         assert np.array_equal(np.isnan(p), np.isnan(pr))
         ok = ~np.isnan(pr)
         assert np.max(np.abs(p[ok] - pr[ok]), initial=0.0) <= TOPK_PROB_ABS, what
+        say(f"{what}: selection K={K}")
+        sv, si = ons.os_topk_select(xd, K)
+        torch.cuda.synchronize()
+        vr, jr = oracle_lib.topk_select(x, K, threads=8)
+        assert np.array_equal(to_host(si), jr), f"{what} selection K={K}: indices differ"
+        assert np.array_equal(to_host(sv).astype(np.float64), vr), f"{what} selection K={K}: values differ"
