@@ -53,6 +53,9 @@ MUTANTS = [
     ("attention_weights_unnormalised", "a[j] = exp(s[j] - m) / l;", "a[j] = exp(s[j] - m);"),
     ("attention_lse_drops_max", "            if (lse)\n                lse[h * nq + i] = m + log(l);\n        }\n    }\n    free(qr);\n    free(kv);\n    free(vv);\n    free(s);\n    free(a);",
      "            if (lse)\n                lse[h * nq + i] = log(l);\n        }\n    }\n    free(qr);\n    free(kv);\n    free(vv);\n    free(s);\n    free(a);"),
+    ("attention_multiplies_k_not_v", "orow[c] += a[j] * vv[j * d + c];", "orow[c] += a[j] * kv[j * d + c];"),
+    ("attention_logits_use_key_zero", "dot += qr[c] * kv[j * d + c];", "dot += qr[c] * kv[c];"),
+    ("attention_scale_applied_twice", "s[j] = scale * dot;", "s[j] = scale * scale * dot;"),
     ("tiled_forgets_rescale", "acc[c] *= alpha;", "acc[c] *= 1.0;"),
     ("tiled_sum_not_rescaled", "l = alpha * l + rowsum;", "l = l + rowsum;"),
     ("select_returns_reversed", "        vals[k] = order[k].value;", "        vals[k] = order[K - 1 - k].value;"),
