@@ -164,7 +164,7 @@ constexpr ResidentShape kResident[] = {
     ONORM_RESIDENT(1024, 1),  ONORM_RESIDENT(1024, 2),  ONORM_RESIDENT(1024, 4),  ONORM_RESIDENT(1024, 8),
     // rows just past a power of two in slots (a lane at 5 or 6 vectors)
     ONORM_RESIDENT(256, 5),   ONORM_RESIDENT(512, 5),   ONORM_RESIDENT(512, 6),   ONORM_RESIDENT(1024, 5),
-    ONORM_RESIDENT(1024, 6),
+    ONORM_RESIDENT(1024, 6),  ONORM_RESIDENT(1024, 7),
     ONORM_RESIDENT_F32(1024, 16),
 };
 constexpr int kNumResident = sizeof(kResident) / sizeof(kResident[0]);
@@ -182,30 +182,33 @@ constexpr int kNumResident = sizeof(kResident) / sizeof(kResident[0]);
 // or 6 vectors per lane on 256, 512 or 1024 lanes (measured 2-20% faster on
 // rows of 1-25% past the power of two, e.g. 32776 bf16 columns in 100.6 us
 // against 114.9 us on 1024 x 8, 8193 bf16 columns in 86.3 us against 96.9 us
-// on 256 x 8).
+// on 256 x 8), and rows of 6145-7168 slots 7 vectors on 1024 lanes (1-7%
+// faster than 1024 x 8 at ~0.25 GiB per launch, e.g. 55000 bf16 columns in
+// 90.5 us against 94.4 us, the 50257-column rows in 96.8 us against 99.7 us).
 struct PlanEntry {
     int max_slots, lpr, vpl;
 };
 constexpr PlanEntry kPlanF32[] = {
     {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {24, 16, 2},      {32, 32, 1},      {48, 32, 2},
     {64, 64, 1},     {128, 64, 2},     {256, 128, 2},    {512, 256, 2},    {640, 256, 4},    {1024, 512, 2},
-    {1536, 512, 4},  {2560, 512, 8},   {4096, 1024, 4},  {5120, 1024, 5},  {6144, 1024, 6},  {8192, 1024, 8}};
+    {1536, 512, 4},  {2560, 512, 8},   {4096, 1024, 4},  {5120, 1024, 5},  {6144, 1024, 6},  {7168, 1024, 7},
+    {8192, 1024, 8}};
 constexpr PlanEntry kPlanF32Unaligned[] = {
     {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {32, 32, 1},      {40, 32, 2},      {64, 64, 1},
     {128, 64, 2},    {256, 64, 4},     {320, 128, 4},    {512, 256, 2},    {640, 256, 4},    {1024, 512, 2},
     {1280, 256, 5},  {2048, 512, 4},   {2560, 512, 5},   {4096, 1024, 4},  {5120, 1024, 5},  {6144, 1024, 6},
-    {8192, 1024, 8}};
+    {7168, 1024, 7}, {8192, 1024, 8}};
 constexpr PlanEntry kPlanBF16[] = {
     {4, 4, 1},       {8, 8, 1},        {10, 8, 2},       {16, 16, 1},      {32, 16, 2},      {64, 32, 2},
     {128, 64, 2},    {192, 64, 4},     {256, 128, 2},    {384, 64, 8},     {512, 256, 2},    {1024, 256, 4},
     {1280, 256, 5},  {2048, 256, 8},   {2560, 512, 5},   {3072, 512, 6},   {4096, 1024, 4},  {5120, 1024, 5},  {6144, 1024, 6},
-    {8192, 1024, 8}};
+    {7168, 1024, 7}, {8192, 1024, 8}};
 constexpr PlanEntry kPlanBF16Unaligned[] = {
     {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {32, 32, 1},      {48, 32, 2},      {64, 64, 1},
     {80, 32, 4},     {128, 64, 2},     {256, 64, 4},     {320, 128, 4},    {512, 256, 2},    {640, 256, 4},
     {1024, 512, 2},  {1280, 256, 5},   {2048, 256, 8},   {2560, 512, 5},   {3072, 512, 6},   {4096, 512, 8},
     {5120, 1024, 5},
-    {6144, 1024, 6}, {8192, 1024, 8}};
+    {6144, 1024, 6}, {7168, 1024, 7}, {8192, 1024, 8}};
 
 const ResidentShape* find_shape(int lpr, int vpl, int dtype) {
     const int bf = dtype == OS_BF16 ? 1 : 0;

@@ -104,7 +104,7 @@ def test_config1(ons, orc):
 
 SHAPES = [(lanes, vecs) for lanes in (4, 8, 16, 32) for vecs in (1, 2, 4)] + \
     [(lanes, vecs) for lanes in (64, 128, 256, 512, 1024) for vecs in (1, 2, 4, 8)] + \
-    [(256, 5), (512, 5), (512, 6), (1024, 5), (1024, 6), (1024, 16)]
+    [(256, 5), (512, 5), (512, 6), (1024, 5), (1024, 6), (1024, 7), (1024, 16)]
 
 
 # (1024 x 16 is built for fp32 only)
@@ -141,7 +141,8 @@ def test_every_resident_shape(ons, orc, lanes, vecs, bf16):
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_auto_dispatch_edge_columns(ons, orc, bf16):
     cols_list = [1, 2, 3, 5, 7, 8, 9, 31, 32, 33, 63, 64, 65, 127, 128, 129, 257, 1000, 1023, 1024, 1025,
-                 2047, 2048, 2049, 4097, 8191, 8193, 16385, 32000, 32768, 32769, 65536, 65537, 100003]
+                 2047, 2048, 2049, 4097, 8191, 8193, 16385, 26001, 28000, 32000, 32768, 32769, 53001, 56000, 65536,
+                 65537, 100003]
     for cols in cols_list:
         rows = 19 if cols < 20000 else 5
         say(f"auto bf16={bf16} rows={rows} cols={cols}")
