@@ -108,8 +108,8 @@ constexpr RowKernel dense_kernel() {
 // them over MI355X's 256 CUs at 32 waves per CU.
 constexpr int64_t dense_rows(int block) { return 2 * 256 * (32 * 64 / block); }
 
-// Multi-row shapes read rows that are not 16-byte aligned through LDS when
-// that lets a smaller shape hold them (see plan_rows).
+// Multi-row shapes may read rows that are not 16-byte aligned through LDS
+// (where the plan says so: see the plan tables and plan_for).
 template <bool BF16, int L, int V>
 constexpr RowKernel staged_kernel() {
     if constexpr (L <= 64) return k_resident<BF16, L, V, false, 2>;
@@ -170,45 +170,51 @@ constexpr ResidentShape kResident[] = {
 constexpr int kNumResident = sizeof(kResident) / sizeof(kResident[0]);
 
 // Automatic choice, by the number of 16-byte slots a row spans, from sweeps
-// of every built shape on MI355X at ~0.5 GiB per launch, with rows at both
-// ends and in the middle of every power-of-two bucket of slots, aligned and
-// not.  Entry {n, l, v} serves rows of up to n slots with l lanes of v
-// vectors.  A row just past a power of two runs fastest on half the lanes
-// with twice the vectors (its workgroups are smaller, or its wavefronts carry
-// more rows); unaligned rows (rows whose starts are not all 16-byte aligned)
-// favour shapes whose partial first and last slots fall in fewer vector steps.
-// Past 1024 slots (bf16, and unaligned fp32), 2048 slots (the same) and
-// 4096 slots, rows that left most of the next power-of-two shape idle take 5
-// or 6 vectors per lane on 256, 512 or 1024 lanes (measured 2-20% faster on
-// rows of 1-25% past the power of two, e.g. 32776 bf16 columns in 100.6 us
-// against 114.9 us on 1024 x 8, 8193 bf16 columns in 86.3 us against 96.9 us
-// on 256 x 8), and rows of 6145-7168 slots 7 vectors on 1024 lanes (1-7%
-// faster than 1024 x 8 at ~0.25 GiB per launch, e.g. 55000 bf16 columns in
-// 90.5 us against 94.4 us, the 50257-column rows in 96.8 us against 99.7 us).
+// of every built shape on MI355X at ~0.5 GiB per launch: 90 lengths per
+// table (rows at both ends and in the middle of every power-of-two bucket of
+// slots, and lengths that leave 0-7 slots spare on 256-1024 lanes), 96 rows
+// one element short of a whole number of blocks and 96 random lengths.
+// Entry {n, l, v, s} serves rows of up to n slots with l lanes of v vectors,
+// read through LDS when s is set.  Over those 552 lengths the choice (with
+// plan_for's rule) averages 0.2-0.4% above the best shape for each length (a
+// geometric mean; the worst single length is 6% above it).
+//  - A row just past a power of two often runs fastest on half the lanes with
+//    twice the vectors (smaller workgroups, or more rows per wavefront), and
+//    past 1024, 2048 and 4096 slots on 5, 6 or 7 vectors per lane (rows of
+//    1-25% past the power of two measured 2-20% faster than on 8 vectors).
+//  - One-row shapes (over 64 lanes) keep 8 or more slots spare on rows that
+//    are not 16-byte aligned, and fp32 rows past 4096 slots, so that the
+//    workgroup may start at the 128-byte line holding the row: at 0-7 spare
+//    slots it starts at the row's 16-byte block, measured 3-8% slower (e.g.
+//    16381 fp32 columns on 1024 x 4 in 184.7 us against 175 us on 1024 x 5).
+//  - Short fp32 rows that are not 16-byte aligned run fastest read through
+//    LDS (5-32 slots: 166-173 us against 174-262 us for the best direct
+//    loads, 9 slots 1.5x); bf16 rows measured faster with direct loads at
+//    every length but one, and keep them.
 struct PlanEntry {
     int max_slots, lpr, vpl;
+    bool staged;
 };
 constexpr PlanEntry kPlanF32[] = {
-    {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {24, 16, 2},      {32, 32, 1},      {48, 32, 2},
-    {64, 64, 1},     {128, 64, 2},     {256, 128, 2},    {512, 256, 2},    {640, 256, 4},    {1024, 512, 2},
-    {1536, 512, 4},  {2560, 512, 8},   {4096, 1024, 4},  {5120, 1024, 5},  {6144, 1024, 6},  {7168, 1024, 7},
-    {8192, 1024, 8}};
+    {4, 4, 1},        {8, 8, 1},        {16, 16, 1},      {24, 16, 2},      {32, 32, 1},      {48, 32, 2},
+    {64, 64, 1},      {128, 64, 2},     {256, 128, 2},    {512, 256, 2},    {560, 256, 4},    {640, 256, 5},
+    {1024, 512, 2},   {1152, 512, 4},   {1280, 512, 5},   {1408, 512, 6},   {2048, 512, 8},   {3072, 1024, 4},
+    {5112, 1024, 6},  {7160, 1024, 7},  {8192, 1024, 8}};
 constexpr PlanEntry kPlanF32Unaligned[] = {
-    {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {32, 32, 1},      {40, 32, 2},      {64, 64, 1},
-    {128, 64, 2},    {256, 64, 4},     {320, 128, 4},    {512, 256, 2},    {640, 256, 4},    {1024, 512, 2},
-    {1280, 256, 5},  {2048, 512, 4},   {2560, 512, 5},   {4096, 1024, 4},  {5120, 1024, 5},  {6144, 1024, 6},
-    {7168, 1024, 7}, {8192, 1024, 8}};
+    {4, 4, 1},        {8, 4, 2, true},  {10, 4, 4, true}, {16, 8, 2, true}, {32, 8, 4, true}, {36, 16, 4, true},
+    {40, 32, 2},      {56, 32, 4},      {64, 64, 1},      {68, 32, 4, true}, {128, 64, 2},    {216, 64, 4, true},
+    {288, 64, 8},     {352, 64, 8, true}, {504, 256, 2},  {960, 256, 4},    {1152, 256, 5},   {1920, 256, 8},
+    {2304, 512, 6},   {4088, 1024, 4},  {5112, 1024, 5},  {6136, 1024, 6},  {7160, 1024, 7},  {8192, 1024, 8}};
 constexpr PlanEntry kPlanBF16[] = {
-    {4, 4, 1},       {8, 8, 1},        {10, 8, 2},       {16, 16, 1},      {32, 16, 2},      {64, 32, 2},
-    {128, 64, 2},    {192, 64, 4},     {256, 128, 2},    {384, 64, 8},     {512, 256, 2},    {1024, 256, 4},
-    {1280, 256, 5},  {2048, 256, 8},   {2560, 512, 5},   {3072, 512, 6},   {4096, 1024, 4},  {5120, 1024, 5},  {6144, 1024, 6},
-    {7168, 1024, 7}, {8192, 1024, 8}};
+    {4, 4, 1},        {8, 8, 1},        {16, 16, 1},      {24, 16, 2},      {32, 32, 1},      {64, 32, 2},
+    {128, 64, 2},     {224, 64, 4},     {256, 128, 2},    {352, 64, 8},     {512, 256, 2},    {832, 256, 4},
+    {1024, 512, 2},   {1280, 256, 5},   {1408, 512, 4},   {2552, 512, 5},   {3072, 512, 6},   {4096, 512, 8},
+    {5120, 1024, 5},  {6144, 1024, 6},  {7168, 1024, 7},  {8192, 1024, 8}};
 constexpr PlanEntry kPlanBF16Unaligned[] = {
-    {4, 4, 1},       {8, 8, 1},        {16, 16, 1},      {32, 32, 1},      {48, 32, 2},      {64, 64, 1},
-    {80, 32, 4},     {128, 64, 2},     {256, 64, 4},     {320, 128, 4},    {512, 256, 2},    {640, 256, 4},
-    {1024, 512, 2},  {1280, 256, 5},   {2048, 256, 8},   {2560, 512, 5},   {3072, 512, 6},   {4096, 512, 8},
-    {5120, 1024, 5},
-    {6144, 1024, 6}, {7168, 1024, 7}, {8192, 1024, 8}};
+    {4, 4, 1},        {8, 4, 2},        {11, 4, 4},       {16, 8, 2},       {22, 8, 4},       {32, 16, 2},
+    {48, 16, 4},      {64, 32, 2},      {104, 32, 4},     {128, 64, 2},     {256, 64, 4},     {320, 128, 4},
+    {512, 64, 8},     {640, 128, 8},    {1016, 256, 4},   {1272, 256, 5},   {2040, 256, 8},   {2552, 512, 5},
+    {3064, 512, 6},   {4096, 512, 8},   {5112, 1024, 5},  {6136, 1024, 6},  {7160, 1024, 7},  {8192, 1024, 8}};
 
 const ResidentShape* find_shape(int lpr, int vpl, int dtype) {
     const int bf = dtype == OS_BF16 ? 1 : 0;
@@ -241,8 +247,8 @@ uint32_t resident_grid(int lpr, int vpl, int64_t cols, int dtype, bool al) {
     return one_row && static_cast<int64_t>(lpr) * vpl * 16 >= lead + cols * es + 15 ? kGrid128 : kGrid16;
 }
 
-// Every plan entry names a built shape (for bf16: one built for bf16) that
-// holds its slots, and the entries grow.
+// Every plan entry names a built shape (for bf16: one built for bf16; read
+// through LDS: one with that form) that holds its slots, and the entries grow.
 template <size_t N>
 constexpr bool plan_ok(const PlanEntry (&t)[N], bool bf16) {
     for (size_t i = 0; i < N; ++i) {
@@ -251,13 +257,21 @@ constexpr bool plan_ok(const PlanEntry (&t)[N], bool bf16) {
         bool built = false;
         for (int k = 0; k < kNumResident; ++k)
             built = built || (kResident[k].lpr == t[i].lpr && kResident[k].vpl == t[i].vpl &&
-                              kResident[k].fn[bf16 ? 1 : 0][0] != nullptr);
+                              kResident[k].fn[bf16 ? 1 : 0][0] != nullptr &&
+                              (!t[i].staged || kResident[k].staged[bf16 ? 1 : 0] != nullptr));
         if (!built) return false;
     }
     return true;
 }
 static_assert(plan_ok(kPlanF32, false) && plan_ok(kPlanF32Unaligned, false), "fp32 plan names an unbuilt shape");
 static_assert(plan_ok(kPlanBF16, true) && plan_ok(kPlanBF16Unaligned, true), "bf16 plan names an unbuilt shape");
+template <size_t N>
+constexpr bool never_staged(const PlanEntry (&t)[N]) {
+    for (size_t i = 0; i < N; ++i)
+        if (t[i].staged) return false;
+    return true;
+}
+static_assert(never_staged(kPlanF32) && never_staged(kPlanBF16), "aligned rows take direct loads");
 template <size_t N>
 constexpr int last_slots(const PlanEntry (&t)[N]) {
     return t[N - 1].max_slots;
@@ -271,8 +285,8 @@ static_assert(last_slots(kPlanF32) == 8192 && last_slots(kPlanF32Unaligned) == 8
                   last_slots(kPlanBF16) == 8192 && last_slots(kPlanBF16Unaligned) == 8192,
               "plans end at 8192 slots; longer rows take the hybrid or streaming kernels");
 
-void auto_plan(int64_t cols, int dtype, bool al, int* lpr, int* vpl) {
-    const int64_t need = slots_needed(cols, dtype, al);
+// The plan entry for rows spanning `slots` 16-byte slots (nullptr past 8192).
+const PlanEntry* plan_entry(int64_t slots, int dtype, bool al) {
     const PlanEntry* t;
     int n;
     if (dtype == OS_BF16) {
@@ -282,15 +296,17 @@ void auto_plan(int64_t cols, int dtype, bool al, int* lpr, int* vpl) {
         t = al ? kPlanF32 : kPlanF32Unaligned;
         n = al ? sizeof(kPlanF32) / sizeof(PlanEntry) : sizeof(kPlanF32Unaligned) / sizeof(PlanEntry);
     }
-    for (int i = 0; i < n; ++i) {
-        if (need <= t[i].max_slots) {
-            *lpr = t[i].lpr;
-            *vpl = t[i].vpl;
-            return;
-        }
-    }
-    *lpr = 0;
-    *vpl = 0;
+    for (int i = 0; i < n; ++i)
+        if (slots <= t[i].max_slots) return &t[i];
+    return nullptr;
+}
+
+// The plan's shape for rows of `cols` elements, holding every block they span.
+void auto_plan(int64_t cols, int dtype, bool al, int* lpr, int* vpl, bool* staged) {
+    const PlanEntry* e = plan_entry(slots_needed(cols, dtype, al), dtype, al);
+    *lpr = e != nullptr ? e->lpr : 0;
+    *vpl = e != nullptr ? e->vpl : 0;
+    *staged = e != nullptr && e->staged;
 }
 
 // Streaming kernels: 4 vectors per lane per step; waves per row sized to the
@@ -373,23 +389,25 @@ int grid_for(int64_t groups, int block, int requested) {
 constexpr int64_t kHybridMaxCols = 4 * 65536;
 
 // The register-resident shape os_softmax_forward takes for these rows
-// (lpr = 0: longer rows, hybrid or streaming).  Rows that are not 16-byte
-// aligned span one more 16-byte block than their length needs; where that
-// block alone pushes them into a larger shape (lengths just under a power of
-// two: 127 bf16 rows span 17 blocks where 16 would hold 128 entries) and the
-// aligned plan's shape is a multi-row one, they are read through LDS instead
-// (*staged), on the aligned plan's shape.  Measured on MI355X: 127 bf16 rows
-// 1.6x faster, 63 fp32 rows 1.5x; on equal shapes the LDS round trip was up
-// to 13% slower, so those keep direct loads.
+// (lpr = 0: longer rows, hybrid or streaming), and whether it reads them
+// through LDS (*staged).  Rows that are not 16-byte aligned may span one more
+// 16-byte block than their length needs (127 bf16 elements: 16 blocks of
+// their own, 17 spanned).  Read through LDS, such a row needs only the slots
+// of its length, so where the unaligned plan's entry for that length is a
+// smaller multi-row shape (at most 128 slots), the row takes it, staged.
+// Measured on MI355X on rows one element short of a whole number of blocks
+// (4-128 blocks): 1.1-1.2x faster than the shape holding the spanned blocks
+// (127 bf16 columns 185 us against 213 us, 15 fp32 columns 173 us against
+// 190 us, per ~0.5 GiB); larger staged shapes measured slower than the
+// direct shape (bf16 64 x 8 through LDS: 1.7x slower on 4095 columns).
 void plan_for(int64_t cols, int dtype, bool al, int* lpr, int* vpl, bool* staged) {
-    auto_plan(cols, dtype, al, lpr, vpl);
-    *staged = false;
+    auto_plan(cols, dtype, al, lpr, vpl, staged);
     if (al || *lpr == 0) return;
-    int la = 0, va = 0;
-    auto_plan(cols, dtype, true, &la, &va);
-    if (la != 0 && la <= 64 && static_cast<int64_t>(la) * va < static_cast<int64_t>(*lpr) * *vpl) {
-        *lpr = la;
-        *vpl = va;
+    const PlanEntry* s = plan_entry(slots_needed(cols, dtype, true), dtype, false);
+    const int64_t cap = static_cast<int64_t>(s->lpr) * s->vpl;
+    if (s->lpr <= 64 && cap <= 128 && cap < static_cast<int64_t>(*lpr) * *vpl) {
+        *lpr = s->lpr;
+        *vpl = s->vpl;
         *staged = true;
     }
 }
@@ -512,8 +530,11 @@ int baseline_forward(const char* fn, const void* in, void* out, int64_t rows, in
     const bool al = vector_ok(in, out, cols, dtype);
     const int bf = dtype == OS_BF16 ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // the safe kernels load directly: every unaligned plan shape, read
+    // through LDS by the forward or not, holds the blocks its rows span
     int lpr = 0, vpl = 0;
-    auto_plan(cols, dtype, al, &lpr, &vpl);
+    bool staged = false;
+    auto_plan(cols, dtype, al, &lpr, &vpl, &staged);
     (void)hipGetLastError();
     if (lpr != 0) {
         // rows that fit the register-resident geometry: same lanes and

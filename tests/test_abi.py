@@ -299,12 +299,25 @@ def test_forward_plan(ons):
             lanes, vecs = ons.os_forward_plan(cols, dt)
             extra = 0 if cols % vec == 0 else vec - 1
             assert lanes == 0 or lanes * vecs * vec >= cols + extra or (lanes <= 64 and lanes * vecs * vec >= cols)
-    assert ons.os_forward_plan(127) == (32, 1)   # 33 blocks, but read through LDS: 32 slots of its own
-    assert ons.os_forward_plan(129) == (32, 2)
+    assert ons.os_forward_plan(127) == (8, 4)    # 33 blocks, but read through LDS: 32 slots of its own
+    assert ons.os_forward_plan(129) == (16, 4)    # 33 blocks, through LDS
     assert ons.os_forward_plan(124) == (32, 1)
-    assert ons.os_forward_plan(127, torch.bfloat16) == (16, 1)
+    assert ons.os_forward_plan(127, torch.bfloat16) == (8, 2)    # 16 slots of its own, 17 spanned
+    assert ons.os_forward_plan(15) == (4, 1)     # 4 slots of its own, 5 spanned
+    assert ons.os_forward_plan(4095, torch.bfloat16) == (128, 8)   # 513 spanned: no large shape through LDS
     assert ons.os_forward_plan(1001, torch.bfloat16) == (64, 2)   # the same shape either way: direct loads
-    assert ons.os_forward_plan(1023) == (128, 4)   # the aligned shape takes one row per workgroup
+    assert ons.os_forward_plan(1023) == (64, 8)    # 257 blocks; the aligned plan's 128 x 2 is one-row
+    assert ons.os_forward_plan(17) == (4, 2)       # short unaligned fp32 rows: small shapes, read through LDS
+    assert ons.os_forward_plan(33) == (4, 4)
+    assert ons.os_forward_plan(61) == (8, 2)
+    assert ons.os_forward_plan(65) == (8, 4)
+    assert ons.os_forward_plan(65, torch.bfloat16) == (4, 4)   # 9 blocks, direct loads
+    # one-row shapes keep 8 blocks spare for unaligned rows: 16381 fp32
+    # columns span 4096 blocks, exactly what 1024 x 4 holds
+    assert ons.os_forward_plan(16349) == (1024, 4)   # 4088 blocks
+    assert ons.os_forward_plan(16381) == (1024, 5)
+    assert ons.os_forward_plan(16384) == (1024, 6)  # aligned fp32 rows past 4088 slots too
+    assert ons.os_forward_plan(16384, torch.bfloat16) == (512, 5)
     assert ons.os_forward_plan(32000) == (1024, 8)
     assert ons.os_forward_plan(32768) == (1024, 8)
     assert ons.os_forward_plan(32769) == (0, 0)    # the hybrid: registers and LDS

@@ -153,6 +153,27 @@ def test_auto_dispatch_edge_columns(ons, orc, bf16):
         assert_parity(run_forward(ons, x, safe=True), ref, bf16, f"safe cols={cols}")
 
 
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_auto_plan_dense_lengths(ons, orc, bf16):
+    """Every row length up to 600 slots (2400 fp32, 4800 bf16 entries; every
+    third length past the first 200), so every entry of the automatic plan,
+    direct or read through LDS, and every switch between them runs, on
+    aligned and element-aligned bases."""
+    vec = 8 if bf16 else 4
+    lengths = list(range(1, 200)) + list(range(200, 600 * vec + 1, 3))
+    for cols in lengths:
+        rows = 5
+        x32 = workloads.normal(rows, cols, seed=cols * 3 + bf16, scale=3.0)
+        x = bf16_bits(x32) if bf16 else x32
+        ref = orc.softmax(x)
+        for si in ((0, 1) if cols % vec else (0,)):
+            say(f"dense lengths bf16={bf16} rows={rows} cols={cols} in+{si}")
+            xin = device_at(x, si)
+            y = ons.os_softmax_forward(xin)
+            torch.cuda.synchronize()
+            assert_parity(to_host(y), ref, bf16, f"auto cols={cols} in+{si}")
+
+
 @pytest.mark.parametrize("cols,rows", [(32000, 1024), (8000, 2048)], ids=["1024x8", "512x8"])
 def test_dense_small_batches(ons, orc, cols, rows):
     """fp32 rows on 8-vector shapes: batches of up to two rounds of
@@ -280,8 +301,8 @@ def test_misaligned_base_and_in_place(ons, orc):
     assert_fp32_parity(to_host(xd), ref, "in-place safe")
 
 
-# 31, 63, 127, 255, 511 and 1023 (bf16) take multi-row shapes that read the rows
-# through LDS; 1001 (bf16) and 129 keep direct loads on the same shape
+# 5, 31, 63, 127, 129, 255, 511 and 1023 (bf16) take multi-row shapes that read
+# the rows through LDS; 1001 (bf16) and 1023 (fp32) keep direct loads
 UNALIGNED_COLS = [1, 3, 5, 31, 63, 127, 129, 255, 511, 1001, 1023, 2047, 4099, 32001, 50257, 65535, 65537, 100003,
                   262147]
 
