@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "os_abi.hip")]
-DEPENDS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("os_device.hpp", "os_kernels.hpp")] + [
+DEPENDS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("os_device.hpp", "os_kernels.hpp", "os_attention.hpp")] + [
     os.path.join(ROOT, "include", "online_softmax.h")]
 LIB = os.path.join(HERE, "libonline_softmax.so")
 ARCH = "gfx950"

@@ -14,9 +14,10 @@
 // query blocks of "6.2 FlashAttention V2 chi tiết", section 2.2); each wave
 // owns 32 query rows (its section 4.2: no exchange between waves), walks the
 // key tiles of 64 keys in order, and keeps its rows' (m, l) and o~ in
-// registers.  The workgroup stages each tile of K (row-major) and V
-// (transposed) in LDS, double-buffered: the next tile's loads are in flight
-// while the current one is used.
+// registers.  The workgroup loads each tile of K and V straight from global
+// memory into LDS (buffer loads that write LDS, no register round trip),
+// both row-major, over three stages: tile t + 2's loads are in flight while
+// tile t is used.
 //
 // The products are computed transposed, S^T = K Q^T and O^T = V^T P^T, with
 // v_mfma_f32_32x32x16_bf16 (A: lane l holds row l % 32 and 8 consecutive k
@@ -26,9 +27,17 @@
 // statistics need one exchange between the two lane halves, and the
 // accumulator registers of S^T are already the B operand of the second
 // product: registers 8p .. 8p+7 of a 32-key block hold keys
-// 16p + 4 (l / 32) + {0,1,2,3, 8,9,10,11}, and V^T is stored in LDS with the
-// keys of each 16-key group in that order, so the matching A operand is one
-// 16-byte read.
+// 16p + 4 (l / 32) + {0,1,2,3, 8,9,10,11}.  The matching A operand, V^T for
+// those keys, comes from row-major V through gfx950's transposing LDS read
+// (ds_read_b64_tr_b16), two reads of 4 keys each.
+//
+// The running maximum moves only when a tile's maximum exceeds it by more
+// than 8 in log2 units: the weights e^{s - m} then stay below 2^8, and a wave
+// whose rows all keep their maximum skips the rescaling of o~ and l.  In exact
+// arithmetic the result does not depend on which m is used, since O = o~ / l
+// and L = m + ln l are invariant under a common shift of the logits (the
+// max-subtraction argument of "CUDA算子优化(3)：Softmax"); a larger m only
+// keeps the exponentials from overflowing.
 #pragma once
 
 #include "os_device.hpp"
@@ -47,8 +56,6 @@ constexpr int kAttnBc = 64;                // keys per tile
 // would cap a lane at 128 VGPRs and spill)
 constexpr int kAttnWaves = 8;              // waves per workgroup
 constexpr int kAttnBr = 32 * kAttnWaves;   // query rows per workgroup
-constexpr int kAttnKStride = kAttnD + 8;   // LDS row stride of a K tile (elements; +16 B against bank conflicts)
-constexpr int kAttnVStride = kAttnBc + 8;  // LDS row stride of a V^T tile
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -56,23 +63,53 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 r) { return __builtin_bit_cast(bf16x8, r); }
 
-// Position of key kk (0..63) of a tile in its V^T row: within each group of
-// 16 keys, the groups of 4 go in the order 0, 2, 1, 3 (keys 0-3, 8-11, 4-7,
-// 12-15), so lane half h finds its 8 keys at positions 8h .. 8h + 7.
-__device__ __forceinline__ int vt_pos(int kk) {
-    const int g = (kk >> 2) & 3;
-    return (kk & ~15) | (((g & 1) << 3) | ((g & 2) << 1)) | (kk & 3);
+// One 16-byte buffer load per lane straight into LDS: lane l's 16 bytes land
+// at lds + 16 l (lds: the wave's base, the same for every lane).
+__device__ __forceinline__ void load_lds16(const Buf& b, uint16_t* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Meet the workgroup's other waves once this wave's loads into LDS, all but
+// the newest `pending` of them, have landed.  No release fence: a fence here
+// would also wait for the newest loads.  The empty asm keeps the compiler from
+// moving LDS accesses across the barrier.
+template <int PENDING>
+__device__ __forceinline__ void lds_loads_barrier() {
+    static_assert(PENDING >= 0 && PENDING < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | PENDING);  // vmcnt(PENDING); expcnt, lgkmcnt unconstrained
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Four bf16 of one column of a 4 x 16 block, transposed across a 16-lane
+// group: lane 4e + q names row e, elements 4q .. 4q + 3 of the block; lane j
+// receives element j of rows 0 .. 3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)p);
+    return __builtin_bit_cast(u32x2, r);
 }
 
 template <bool CAUSAL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAttnWaves * 64), amdgpu_waves_per_eu(2)))
     k_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                uint16_t* __restrict__ o, float* __restrict__ lse, int64_t heads, int nq, int nk, float scale) {
-    constexpr int NT = kAttnWaves * 64;        // threads
-    constexpr int KV = kAttnBc * kAttnD / 8 / NT;  // K vectors per thread per tile
-    constexpr int VK = kAttnBc * kAttnD / 8 / NT;  // V keys per thread per tile (one 8-dim chunk each)
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kAttnBc * kAttnKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kAttnD * kAttnVStride];
+    constexpr int NT = kAttnWaves * 64;             // threads
+    constexpr int CH = kAttnBc * kAttnD / 8 / NT;   // 16-byte chunks of K (and of V) per thread per tile
+    constexpr int TILE = kAttnBc * kAttnD;          // elements of one K or V tile
+    // Three stages of K and V (16 KB each), as separate arrays so that the
+    // compiler tells them apart when it waits for the loads into one of them.
+    // K rows keep their 16 chunks of 16 bytes at positions chunk ^ (row % 16),
+    // V rows at chunk ^ 4 (row % 4): both reads below then spread a
+    // wavefront's quarter over all LDS banks.
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sK2[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sV2[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -82,16 +119,27 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
     const float c = scale * kLog2e;
     const int nqb = (nq + kAttnBr - 1) / kAttnBr;
     const int64_t units = heads * nqb;
+    static_assert(CH == 2, "staging shape");
 
-    static_assert(KV * NT * 8 == kAttnBc * kAttnD && (VK == 1 || VK == 2 || VK == 4), "staging shape");
+    // this thread's staging chunks: position tid + NT r of a tile, row
+    // (tid + NT r) / 16; the global chunk it loads is the one that position holds
+    uint32_t koff[CH], voff[CH];  // byte offsets within a tile
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+        const int idx = tid + NT * r;
+        const int row = idx >> 4;
+        koff[r] = static_cast<uint32_t>(row * kAttnD + (((idx & 15) ^ (row & 15)) * 8)) * 2u;
+        voff[r] = static_cast<uint32_t>(row * kAttnD + (((idx & 15) ^ ((row & 3) << 2)) * 8)) * 2u;
+    }
+    // the transposed V reads: this lane's row e and dims 4q .. 4q + 3 of its
+    // group's 4 x 16 block
+    const int tr_e = (lane >> 2) & 3, tr_q = lane & 3, tr_g = lane >> 4;
+
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         // Workgroups go to the 8 XCDs in turn (unit % 8), and each XCD has its
         // own L2.  When the heads split evenly, all query blocks of a head run
         // on one XCD, so its K and V tiles are fetched into one L2, and every
         // XCD gets the same mix of long and short (causal) query blocks.
-        // Measured on the 256-head 2048 x 128 workload: 963 -> 855 us, and
-        // causal 865 -> 592 us (with heads in plain order one XCD drew the
-        // longest causal blocks of every head).
         int64_t head = unit / nqb;
         int qbi = static_cast<int>(unit - head * nqb);
         if (heads % 8 == 0) {
@@ -115,53 +163,16 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
         for (int ks = 0; ks < kAttnD / 16; ++ks)
             qb8[ks] = as_bf16x8(bq.load16<true>((static_cast<uint32_t>(qrow) * kAttnD + ks * 16 + h * 8) * 2u));
 
-        // tile staging: thread tid moves K vectors tid + NT r, and V keys
-        // VK (tid % (64 / VK)) .. + VK - 1, dims 8 (tid / (64 / VK)), through one of two
-        // register sets: tile j's loads go to set j % 2 two tiles before its
-        // LDS store, so their latency hides behind two tiles of products
-        struct Stage {
-            u32x4 k[KV], v[VK];
-        };
-        Stage st0, st1;
-        // Consecutive lanes take consecutive keys of one dim chunk, so a V^T
-        // store instruction fills one LDS row across the banks (with the
-        // chunk in the low lane bits, the 16 chunks' rows, 1152 bytes apart,
-        // fell on the same banks)
-        constexpr int VGROUPS = kAttnBc / VK;  // key groups per tile
-        const int vkey0 = (tid % VGROUPS) * VK, vchunk = tid / VGROUPS;
-        auto load_tile = [&](int t, Stage& sg) {
-            const int key0 = t * kAttnBc;
+        // tile t's K and V into one stage: CH loads of each per thread, one
+        // wavefront's load filling 1 KB of the stage.  Keys past nk read
+        // nothing (the buffer range check); causal tiles past the diagonal
+        // are real keys, unused.
+        auto load_tile = [&](int t, uint16_t* sk, uint16_t* sv) {
+            const uint32_t tile_off = static_cast<uint32_t>(t) * (kAttnBc * kAttnD * 2);
 #pragma unroll
-            for (int r = 0; r < KV; ++r) {
-                const int idx = tid + NT * r;
-                sg.k[r] = bk.load16<true>((static_cast<uint32_t>(key0 + (idx >> 4)) * kAttnD + (idx & 15) * 8) * 2u);
-            }
+            for (int r = 0; r < CH; ++r) load_lds16(bk, sk + (w * 64 + NT * r) * 8, koff[r], tile_off);
 #pragma unroll
-            for (int r = 0; r < VK; ++r)
-                sg.v[r] = bv.load16<true>((static_cast<uint32_t>(key0 + vkey0 + r) * kAttnD + vchunk * 8) * 2u);
-        };
-        auto store_tile = [&](const Stage& sg, int buf) {
-#pragma unroll
-            for (int r = 0; r < KV; ++r) {
-                const int idx = tid + NT * r;
-                *reinterpret_cast<u32x4*>(&sK[buf][(idx >> 4) * kAttnKStride + (idx & 15) * 8]) = sg.k[r];
-            }
-            // transpose VK keys x 8 dims: dim dd of the keys becomes VK consecutive V^T entries
-            const int pos = vt_pos(vkey0);
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                const int word = dd >> 1, hi = dd & 1;
-                uint32_t e[VK];
-#pragma unroll
-                for (int r = 0; r < VK; ++r) e[r] = hi ? (sg.v[r][word] >> 16) : (sg.v[r][word] & 0xFFFFu);
-                if constexpr (VK == 4)
-                    *reinterpret_cast<u32x2*>(&sV[buf][(vchunk * 8 + dd) * kAttnVStride + pos]) =
-                        u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-                else if constexpr (VK == 2)
-                    *reinterpret_cast<uint32_t*>(&sV[buf][(vchunk * 8 + dd) * kAttnVStride + pos]) = e[0] | (e[1] << 16);
-                else
-                    sV[buf][(vchunk * 8 + dd) * kAttnVStride + pos] = static_cast<uint16_t>(e[0]);
-            }
+            for (int r = 0; r < CH; ++r) load_lds16(bv, sv + (w * 64 + NT * r) * 8, voff[r], tile_off);
         };
 
         f32x16 oacc[kAttnD / 32];
@@ -172,24 +183,16 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
         float m = -INFINITY;  // running maximum of this row's raw logits q.k
         float l = 0.0f;       // this lane's share of sum e^{(s - m) scale} (its half of the keys)
 
-        load_tile(0, st0);
-        store_tile(st0, 0);
-        __syncthreads();
-        // Q must be in registers before the loop: otherwise the compiler's
-        // wait for Q's loads inside the first product also waits for the
-        // next tiles' loads, every tile (measured 1018 -> 963 us)
-        __builtin_amdgcn_s_waitcnt(0);
-        load_tile(1, st1);
-        // One tile: issue tile t + 2's loads into `cur` (free: it held tile t,
-        // stored before this tile began), the products on LDS buffer t % 2,
-        // then tile t + 1 from `nxt` into the other buffer.  The loads are
-        // issued even past the last tile (keys past nk read nothing: the
-        // buffer range check; causal tiles past the diagonal are real keys,
-        // unused): a conditional load would make the compiler wait for it
-        // together with `nxt`'s loads before the store.
-        auto tile = [&](const int t, Stage& cur, const Stage& nxt) {
-            const int buf = t & 1;
-            load_tile(t + 2, cur);
+        load_tile(0, sK0, sV0);
+        load_tile(1, sK1, sV1);
+        // Q and tile 0 here (tile 1's 2 CH loads may still be in flight), for every wave
+        lds_loads_barrier<2 * CH>();
+        // One tile: issue tile t + 2's loads into stage (t + 2) % 3 (last read
+        // by tile t - 1, which every wave left at the barrier ending it), the
+        // products on stage t % 3, then wait for tile t + 1's loads and meet
+        // the other waves.
+        auto tile = [&](const int t, const uint16_t* sk, const uint16_t* sv, uint16_t* nk_, uint16_t* nv_) {
+            load_tile(t + 2, nk_, nv_);
 
             // causal: a tile whose first key lies past this wave's last row adds nothing to it
             const bool wave_live = !CAUSAL || (t * kAttnBc <= q0 + w * 32 + 31);
@@ -202,8 +205,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
                 for (int i = 0; i < 16; ++i) s[mb][i] = 0.0f;
 #pragma unroll
                 for (int ks = 0; ks < kAttnD / 16; ++ks) {
-                    const bf16x8 a = as_bf16x8(
-                        *reinterpret_cast<const u32x4*>(&sK[buf][(mb * 32 + col) * kAttnKStride + ks * 16 + h * 8]));
+                    const int row = mb * 32 + col;
+                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                        &sk[row * kAttnD + (((2 * ks + h) ^ (col & 15)) * 8)]));
                     s[mb] = mfma32(a, qb8[ks], s[mb]);
                 }
             }
@@ -232,10 +236,21 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
                 const f32x2 x = swap_rows32(mt);
                 mt = fmaxf(x[0], x[1]);
             }
-            const float m_new = fmaxf(m, mt);  // finite from the first tile on (key 0 is visible to every row)
-            const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);  // 0 on the first tile
-            const float mc = m_new * c;
-            m = m_new;
+            // keep the running maximum unless the tile's exceeds it by more than
+            // 8 in log2 units (weights then stay below 2^8); skip the rescaling
+            // of o~ when no row of the wave moves its maximum
+            const bool grow = (mt - m) * c > 8.0f;  // true on the first tile (m = -inf)
+            float alpha = 1.0f;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float m_new = grow ? mt : m;
+                alpha = __builtin_amdgcn_exp2f((m - m_new) * c);  // 0 on the first tile, 1 where kept
+                m = m_new;
+#pragma unroll
+                for (int db = 0; db < kAttnD / 32; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            }
+            const float mc = m * c;
             // P = e^{(s - m) scale} as the B operand of O^T = V^T P^T, and this lane's row sum
             float rs = 0.0f;
             bf16x8 pb[4];
@@ -254,28 +269,33 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
                                       pack_bf16x2(e[6], e[7])});
                 }
             l = fmaf(l, alpha, rs);
+            // O^T += V^T P^T: 4 dim blocks x 4 k-steps of 16 keys.  The A
+            // operand of step kk = 2 mb + p holds, for this lane's dim, keys
+            // 32 mb + 16 p + 4 h + {0..3} and the same + 8 (the order of P^T's
+            // registers): two transposed reads of 4 keys each.
 #pragma unroll
-            for (int db = 0; db < kAttnD / 32; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-            // O^T += V^T P^T: 4 dim blocks x 4 k-steps of 16 keys
-#pragma unroll
-            for (int db = 0; db < kAttnD / 32; ++db)
+            for (int db = 0; db < kAttnD / 32; ++db) {
+                const int dd = db * 32 + 16 * (tr_g & 1) + 4 * tr_q;  // first of this lane's 4 dims
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        &sV[buf][(db * 32 + col) * kAttnVStride + (kk >> 1) * 32 + (kk & 1) * 16 + h * 8]));
+                    const int row = 16 * kk + 4 * h + tr_e;  // 32 mb + 16 p = 16 kk
+                    const int pos = ((dd >> 3) ^ (tr_e << 2)) * 8 + (dd & 7);
+                    const u32x2 lo = lds_read_tr16(&sv[row * kAttnD + pos]);
+                    const u32x2 hi = lds_read_tr16(&sv[(row + 8) * kAttnD + pos]);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                     oacc[db] = mfma32(a, pb[kk], oacc[db]);
                 }
+            }
             }  // wave_live
             if (t + 1 < ntiles) {
-                store_tile(nxt, buf ^ 1);
-                __syncthreads();
+                // tile t + 1's loads (tile t + 2's may still be in flight)
+                lds_loads_barrier<2 * CH>();
             }
         };
-        for (int t = 0; t < ntiles; t += 2) {
-            tile(t, st0, st1);
-            if (t + 1 < ntiles) tile(t + 1, st1, st0);
+        for (int t = 0; t < ntiles; t += 3) {
+            tile(t, sK0, sV0, sK2, sV2);
+            if (t + 1 < ntiles) tile(t + 1, sK1, sV1, sK0, sV0);
+            if (t + 2 < ntiles) tile(t + 2, sK2, sV2, sK1, sV1);
         }
         // the row's sum over both halves; O = o~ / l
         {
@@ -296,7 +316,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
             }
         if ((lse != nullptr) & (h == 0) & (qrow < nq))
             lse[head * nq + qrow] = fmaf(m, scale, __builtin_amdgcn_logf(l) * kLn2);
-        __syncthreads();  // the next unit's first tile overwrites buffer 0
+        // the loads issued past the last tile land before the next unit reuses the stages
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 }
 

@@ -116,6 +116,24 @@ def test_attention_special_inputs(ons, oracle_lib):
     check(ons, oracle_lib, q, kl, v, False, "late winning key")
 
 
+def test_attention_rising_maximum(ons, oracle_lib):
+    """Rows whose maximum rises by more than 8 in log2 units every two or
+    three key tiles, interleaved with rows whose maximum is their first key:
+    in one wavefront some rows move their running maximum (and rescale) while
+    the others keep theirs."""
+    heads, n, d = 2, 700, 128
+    rng = np.random.default_rng(4300)
+    qf = rng.standard_normal((heads, n, d)) * 0.01
+    qf[:, 0::2, 0] = 1.0
+    qf[:, 1::2, 0] = -1.0
+    kf = rng.standard_normal((heads, n, d)) * 0.01
+    kf[:, :, 0] = np.arange(n) * 0.04  # logits of the even rows grow by 2.56 a tile, ~3.7 in log2 units
+    vf = rng.standard_normal((heads, n, d))
+    q, k, v = (workloads.f32_to_bf16_bits(x.astype(np.float32)) for x in (qf, kf, vf))
+    check(ons, oracle_lib, q, k, v, False, "rising maximum", scale=1.0)
+    check(ons, oracle_lib, q, k, v, True, "rising maximum, causal", scale=1.0)
+
+
 def test_attention_in_place_and_deterministic(ons):
     q, k, v = workloads.attention_qkv(2, 300, 300, 128, seed=5000)
     qd, kd, vd = dev(q), dev(k), dev(v)
