@@ -10,13 +10,13 @@
 // Layout: bf16 Q [heads, nq, 128], K and V [heads, nk, 128], O like Q; the
 // per-row logsumexp L = m + ln l in fp32 [heads, nq].
 //
-// One workgroup = 8 waves = 256 query rows of one head (the outer loop over
+// One workgroup = 4 waves = 128 query rows of one head (the outer loop over
 // query blocks of "6.2 FlashAttention V2 chi tiết", section 2.2); each wave
 // owns 32 query rows (its section 4.2: no exchange between waves), walks the
 // key tiles of 64 keys in order, and keeps its rows' (m, l) and o~ in
 // registers.  The workgroup loads each tile of K and V straight from global
 // memory into LDS (buffer loads that write LDS, no register round trip),
-// both row-major, over three stages: tile t + 2's loads are in flight while
+// both row-major, double-buffered: tile t + 1's loads are in flight while
 // tile t is used.
 //
 // The products are computed transposed, S^T = K Q^T and O^T = V^T P^T, with
@@ -50,11 +50,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnD = 128;                // head dimension
 constexpr int kAttnBc = 64;                // keys per tile
-// 8 waves = 256 query rows per workgroup, one workgroup per CU at 2 waves per
-// SIMD: each staged K/V tile feeds twice the products of a 4-wave workgroup
-// (measured 870 -> 719 us on the 256-head 2048 x 128 workload; 16 waves
-// would cap a lane at 128 VGPRs and spill)
-constexpr int kAttnWaves = 8;              // waves per workgroup
+// 4 waves = 128 query rows per workgroup, two workgroups per CU (64 KB of
+// LDS each) at 2 waves per SIMD.  Measured on the 256-head 2048 x 128
+// workload against one 8-wave workgroup per CU with three LDS stages: 547 ->
+// 547 us, causal 374 -> 345 us (the causal diagonal wastes less in 128-row
+// blocks); 16 waves would cap a lane at 128 VGPRs and spill.
+constexpr int kAttnWaves = 4;              // waves per workgroup
 constexpr int kAttnBr = 32 * kAttnWaves;   // query rows per workgroup
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -99,17 +100,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
     constexpr int NT = kAttnWaves * 64;             // threads
     constexpr int CH = kAttnBc * kAttnD / 8 / NT;   // 16-byte chunks of K (and of V) per thread per tile
     constexpr int TILE = kAttnBc * kAttnD;          // elements of one K or V tile
-    // Three stages of K and V (16 KB each), as separate arrays so that the
+    // Two stages of K and V (16 KB each), as separate arrays so that the
     // compiler tells them apart when it waits for the loads into one of them.
     // K rows keep their 16 chunks of 16 bytes at positions chunk ^ (row % 16),
     // V rows at chunk ^ 4 (row % 4): both reads below then spread a
     // wavefront's quarter over all LDS banks.
     __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t sK2[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t sV2[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -119,7 +118,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
     const float c = scale * kLog2e;
     const int nqb = (nq + kAttnBr - 1) / kAttnBr;
     const int64_t units = heads * nqb;
-    static_assert(CH == 2, "staging shape");
+    static_assert(CH * NT * 8 == TILE, "staging shape");
 
     // this thread's staging chunks: position tid + NT r of a tile, row
     // (tid + NT r) / 16; the global chunk it loads is the one that position holds
@@ -184,15 +183,14 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
         float l = 0.0f;       // this lane's share of sum e^{(s - m) scale} (its half of the keys)
 
         load_tile(0, sK0, sV0);
-        load_tile(1, sK1, sV1);
-        // Q and tile 0 here (tile 1's 2 CH loads may still be in flight), for every wave
-        lds_loads_barrier<2 * CH>();
-        // One tile: issue tile t + 2's loads into stage (t + 2) % 3 (last read
+        // Q and tile 0 here, for every wave
+        lds_loads_barrier<0>();
+        // One tile: issue tile t + 1's loads into stage (t + 1) % 2 (last read
         // by tile t - 1, which every wave left at the barrier ending it), the
-        // products on stage t % 3, then wait for tile t + 1's loads and meet
+        // products on stage t % 2, then wait for tile t + 1's loads and meet
         // the other waves.
         auto tile = [&](const int t, const uint16_t* sk, const uint16_t* sv, uint16_t* nk_, uint16_t* nv_) {
-            load_tile(t + 2, nk_, nv_);
+            load_tile(t + 1, nk_, nv_);
 
             // causal: a tile whose first key lies past this wave's last row adds nothing to it
             const bool wave_live = !CAUSAL || (t * kAttnBc <= q0 + w * 32 + 31);
@@ -288,14 +286,13 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
             }
             }  // wave_live
             if (t + 1 < ntiles) {
-                // tile t + 1's loads (tile t + 2's may still be in flight)
-                lds_loads_barrier<2 * CH>();
+                // tile t + 1's loads
+                lds_loads_barrier<0>();
             }
         };
-        for (int t = 0; t < ntiles; t += 3) {
-            tile(t, sK0, sV0, sK2, sV2);
+        for (int t = 0; t < ntiles; t += 2) {
+            tile(t, sK0, sV0, sK1, sV1);
             if (t + 1 < ntiles) tile(t + 1, sK1, sV1, sK0, sV0);
-            if (t + 2 < ntiles) tile(t + 2, sK2, sV2, sK1, sV1);
         }
         // the row's sum over both halves; O = o~ / l
         {

@@ -68,9 +68,10 @@ def check(ons, orc, q, k, v, causal: bool, what: str, scale=None, threads: int =
     return float(np.abs(O - Or).max()), float(np.abs(L - Lr).max())
 
 
-# query and key lengths around the tile sizes (256 query rows per workgroup,
+# query and key lengths around the tile sizes (128 query rows per workgroup,
 # 32 per wave, 64 keys per tile): one row, ragged tails, exact multiples
-SHAPES = [(1, 1), (1, 64), (31, 63), (128, 64), (129, 65), (200, 300), (64, 1), (256, 128), (257, 130), (513, 70)]
+SHAPES = [(1, 1), (1, 64), (31, 63), (127, 64), (128, 64), (129, 65), (200, 300), (64, 1), (256, 128), (257, 130),
+          (513, 70)]
 
 
 @pytest.mark.parametrize("nq,nk", SHAPES, ids=[f"{a}x{b}" for a, b in SHAPES])
@@ -79,7 +80,7 @@ def test_attention_small(ons, oracle_lib, nq, nk):
     check(ons, oracle_lib, q, k, v, False, f"{nq}x{nk}")
 
 
-@pytest.mark.parametrize("n", [1, 2, 31, 33, 63, 64, 65, 128, 129, 255, 256, 257, 300, 600])
+@pytest.mark.parametrize("n", [1, 2, 31, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 383, 385, 600])
 def test_attention_causal(ons, oracle_lib, n):
     q, k, v = workloads.attention_qkv(3, n, n, 128, seed=3000 + n)
     check(ons, oracle_lib, q, k, v, True, f"causal n={n}")
