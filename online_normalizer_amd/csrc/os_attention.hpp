@@ -249,41 +249,38 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
                     for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
             }
             const float mc = m * c;
-            // P = e^{(s - m) scale} as the B operand of O^T = V^T P^T, and this lane's row sum
-            float rs = 0.0f;
-            bf16x8 pb[4];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    float e[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        e[u] = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * p + u], c, -mc));
-                        rs += e[u];
-                    }
-                    pb[mb * 2 + p] = __builtin_bit_cast(
-                        bf16x8, u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                                      pack_bf16x2(e[6], e[7])});
-                }
-            l = fmaf(l, alpha, rs);
-            // O^T += V^T P^T: 4 dim blocks x 4 k-steps of 16 keys.  The A
+            // P = e^{(s - m) scale} as the B operand of O^T = V^T P^T, and this
+            // lane's row sum, one k-step of 16 keys at a time, each followed
+            // by its products: O^T += V^T P^T over the 4 dim blocks.  The A
             // operand of step kk = 2 mb + p holds, for this lane's dim, keys
             // 32 mb + 16 p + 4 h + {0..3} and the same + 8 (the order of P^T's
-            // registers): two transposed reads of 4 keys each.
+            // registers): two transposed reads of 4 keys each.  Each dim
+            // block still adds its k-steps in order 0..3.
+            float rs = 0.0f;
 #pragma unroll
-            for (int db = 0; db < kAttnD / 32; ++db) {
-                const int dd = db * 32 + 16 * (tr_g & 1) + 4 * tr_q;  // first of this lane's 4 dims
+            for (int kk = 0; kk < 4; ++kk) {
+                const int mb = kk >> 1, p = kk & 1;
+                float e[8];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int row = 16 * kk + 4 * h + tr_e;  // 32 mb + 16 p = 16 kk
+                for (int u = 0; u < 8; ++u) {
+                    e[u] = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * p + u], c, -mc));
+                    rs += e[u];
+                }
+                const bf16x8 pbk = __builtin_bit_cast(
+                    bf16x8, u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                                  pack_bf16x2(e[6], e[7])});
+                const int row = 16 * kk + 4 * h + tr_e;  // 32 mb + 16 p = 16 kk
+#pragma unroll
+                for (int db = 0; db < kAttnD / 32; ++db) {
+                    const int dd = db * 32 + 16 * (tr_g & 1) + 4 * tr_q;  // first of this lane's 4 dims
                     const int pos = ((dd >> 3) ^ (tr_e << 2)) * 8 + (dd & 7);
                     const u32x2 lo = lds_read_tr16(&sv[row * kAttnD + pos]);
                     const u32x2 hi = lds_read_tr16(&sv[(row + 8) * kAttnD + pos]);
                     const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    oacc[db] = mfma32(a, pb[kk], oacc[db]);
+                    oacc[db] = mfma32(a, pbk, oacc[db]);
                 }
             }
+            l = fmaf(l, alpha, rs);
             }  // wave_live
             if (t + 1 < ntiles) {
                 // tile t + 1's loads
