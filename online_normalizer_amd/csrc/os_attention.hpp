@@ -65,9 +65,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 r) { return __builtin_bit_cast(bf16x8, r); }
 
 // One 16-byte buffer load per lane straight into LDS: lane l's 16 bytes land
-// at lds + 16 l (lds: the wave's base, the same for every lane).
-__device__ __forceinline__ void load_lds16(const Buf& b, uint16_t* lds, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+// at lds + 16 l (lds: the wave's base, the same for every lane).  The whole
+// byte offset goes in the per-lane offset, which the buffer's range check
+// covers (the scalar offset is left 0: on this family it is not range-checked),
+// so a load past the buffer's end reads nothing.
+__device__ __forceinline__ void load_lds16(const Buf& b, uint16_t* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 
 // Meet the workgroup's other waves once this wave's loads into LDS, all but
@@ -169,9 +172,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kAttnWaves * 64, kAtt
         auto load_tile = [&](int t, uint16_t* sk, uint16_t* sv) {
             const uint32_t tile_off = static_cast<uint32_t>(t) * (kAttnBc * kAttnD * 2);
 #pragma unroll
-            for (int r = 0; r < CH; ++r) load_lds16(bk, sk + (w * 64 + NT * r) * 8, koff[r], tile_off);
+            for (int r = 0; r < CH; ++r) load_lds16(bk, sk + (w * 64 + NT * r) * 8, tile_off + koff[r]);
 #pragma unroll
-            for (int r = 0; r < CH; ++r) load_lds16(bv, sv + (w * 64 + NT * r) * 8, voff[r], tile_off);
+            for (int r = 0; r < CH; ++r) load_lds16(bv, sv + (w * 64 + NT * r) * 8, tile_off + voff[r]);
         };
 
         f32x16 oacc[kAttnD / 32];
