@@ -737,6 +737,35 @@ def check_lse(ons, orc, x: np.ndarray, what: str, write_y: bool = True, rows=Non
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_stats_and_lse_dense_lengths(ons, orc, bf16):
+    """The row statistics and the logsumexp (with and without y) take the
+    forward's automatic plan: every row length up to 64 slots and every
+    seventh up to 600, aligned and from an element-aligned base, against the
+    oracle (m exact, d within 1e-5 relative, L within lse_tol, y bitwise the
+    forward's)."""
+    vec = 8 if bf16 else 4
+    lengths = list(range(1, 64 * vec + 1)) + list(range(64 * vec + 1, 600 * vec + 1, 7))
+    for cols in lengths:
+        rows = 5
+        x32 = workloads.normal(rows, cols, seed=cols * 5 + 11 + bf16, scale=3.0)
+        x = bf16_bits(x32) if bf16 else x32
+        m_ref, d_ref = orc.stats(x)
+        L_ref = orc.logsumexp(x, threads=8)
+        for si in ((0, 1) if cols % vec else (0,)):
+            say(f"stats/lse dense lengths bf16={bf16} rows={rows} cols={cols} in+{si}")
+            xin = device_at(x, si)
+            m, d = ons.os_softmax_stats(xin)
+            y, L = ons.os_softmax_forward_lse(xin)
+            y_plain = ons.os_softmax_forward(xin)
+            torch.cuda.synchronize()
+            what = f"bf16={bf16} cols={cols} in+{si}"
+            assert np.array_equal(to_host(m).astype(np.float64), m_ref), what
+            assert np.max(np.abs(to_host(d) - d_ref) / d_ref) <= 1e-5, what
+            assert np.all(np.abs(to_host(L).astype(np.float64) - L_ref) <= lse_tol(L_ref)), what
+            assert torch.equal(bits(y), bits(y_plain)), what
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_lse_every_plan_bucket(ons, orc, bf16):
     for cols in [1, 3, 8, 33, 128, 129, 1000, 2048, 4097, 8193, 32000, 65536, 65537, 200001]:
         rows = 13 if cols < 20000 else 4
